@@ -1,0 +1,307 @@
+"""Pins of the CPU oracle to facts other than itself.
+
+Each ``pin_*`` function raises AssertionError when the oracle disagrees with a
+closed form, a library routine, a brute-force enumeration or an invariant that
+the pages and the mathematics fix. ``test_oracle_pins.py`` runs them all;
+``test_oracle_mutants.py`` plants mistakes in the oracle and checks that some
+pin fails for each.
+"""
+from __future__ import annotations
+
+import itertools
+import math
+
+import numpy as np
+import scipy.special
+
+import synth
+import oracle
+from oracle import REPEAT, CAUSAL
+
+
+def _bits(x):
+    return synth.f32_to_bf16(np.asarray(x, dtype=np.float32))
+
+
+def _tiny(seed, Hq, Hkv, D, n_ctx, n_q, mask, chunk, qstd=0.5):
+    r = synth.Recipe(Hq=Hq, Hkv=Hkv, D=D, n_ctx=n_ctx, n_q=n_q, mask=mask, chunk=chunk,
+                     scale=1.0, q_prescale=qstd)
+    return synth.draw(r, seed)
+
+
+# ---------------------------------------------------------------- LSE pins
+
+def pin_softmax_rows_sum_to_one():
+    """Every row of the softmax built from the oracle's LSE sums to 1."""
+    for mask, chunk in [(REPEAT, 5), (REPEAT, 0), (CAUSAL, 0)]:
+        n_ctx = 13 if mask == REPEAT else 11
+        d = _tiny(7, 6, 2, 64, n_ctx, 11, mask, chunk, qstd=1.0)
+        L = oracle.lse(d["Q"], d["Kctx"], d.get("Kself"), 1.0, mask, chunk)
+        c = chunk if chunk else 11
+        for g in range(6):
+            for j0 in range(0, 11, c):
+                j1 = min(j0 + c, 11)
+                a = oracle.attention_weights(d["Q"], d["Kctx"], d.get("Kself"), 1.0, mask, chunk,
+                                             g, j0, j1, L[g, j0:j1])
+                assert np.allclose(a.sum(axis=1), 1.0, rtol=0, atol=1e-12), (mask, g, j0)
+
+
+def pin_lse_zero_queries():
+    """Q = 0: every visible logit is 0, so LSE_j = ln |V(j)| with
+    |V(j)| = n_ctx + (j mod C) + 1 (repeat) or j + 1 (causal)."""
+    Hq, Hkv, D, n_ctx, n_q, C = 4, 2, 64, 9, 10, 4
+    Q = np.zeros((Hq, n_q, D), dtype=np.uint16)
+    d = _tiny(3, Hq, Hkv, D, n_ctx, n_q, REPEAT, C)
+    L = oracle.lse(Q, d["Kctx"], d["Kself"], 0.125, REPEAT, C)
+    want = np.log(n_ctx + (np.arange(n_q) % C) + 1.0)
+    assert np.allclose(L, want[None, :], rtol=0, atol=1e-13)
+    dc = _tiny(3, Hq, Hkv, D, n_q, n_q, CAUSAL, 0)
+    Lc = oracle.lse(Q, dc["Kctx"], None, 0.125, CAUSAL, 0)
+    assert np.allclose(Lc, np.log(np.arange(n_q) + 1.0)[None, :], rtol=0, atol=1e-13)
+
+
+def _brute_visible(Qf, Kc, Ks, g, h, j, scale, mask, chunk, n_q):
+    """Visible logits of (g, j), enumerated key by key with exact sums."""
+    out = []
+    if mask == REPEAT:
+        c = chunk if chunk else n_q
+        c0 = (j // c) * c
+        keys = [Kc[h, i] for i in range(Kc.shape[1])] + [Ks[h, p] for p in range(c0, j + 1)]
+    else:
+        keys = [Kc[h, i] for i in range(j + 1)]
+    for k in keys:
+        out.append(scale * math.fsum(float(a) * float(b) for a, b in zip(Qf[g, j], k)))
+    return out
+
+
+def pin_lse_brute_force_logsumexp():
+    """LSE against scipy's logsumexp over brute-force enumerated logits."""
+    for mask, chunk, n_ctx, n_q in [(REPEAT, 3, 5, 7), (CAUSAL, 0, 6, 6)]:
+        d = _tiny(11, 4, 2, 64, n_ctx, n_q, mask, chunk, qstd=1.0)
+        Qf = synth.bf16_to_f32(d["Q"]).astype(np.float64)
+        Kc = synth.bf16_to_f32(d["Kctx"]).astype(np.float64)
+        Ks = synth.bf16_to_f32(d["Kself"]).astype(np.float64) if "Kself" in d else None
+        L = oracle.lse(d["Q"], d["Kctx"], d.get("Kself"), 0.5, mask, chunk)
+        for g, j in itertools.product(range(4), range(n_q)):
+            h = g // 2
+            want = scipy.special.logsumexp(_brute_visible(Qf, Kc, Ks, g, h, j, 0.5, mask, chunk, n_q))
+            assert abs(L[g, j] - want) < 1e-12, (mask, g, j)
+
+
+# ---------------------------------------------------------------- max-mode pins
+
+def pin_max_zero_queries():
+    """Q = 0: a_ji = 1/|V(j)|, so the unweighted score is 1/(n_ctx + 1) (the
+    first query of a chunk sees the fewest keys) and the weighted score is
+    vnorm_i * max_j 1 / ((n_ctx + (j mod C) + 1) * hnorm_j)."""
+    Hq, Hkv, D, n_ctx, n_q, C = 6, 2, 64, 8, 9, 4
+    d = _tiny(5, Hq, Hkv, D, n_ctx, n_q, REPEAT, C)
+    Q = np.zeros((Hq, n_q, D), dtype=np.uint16)
+    L = oracle.lse(Q, d["Kctx"], d["Kself"], 0.125, REPEAT, C)
+    s = oracle.max_scores(Q, d["Kctx"], L, 0.125, Hkv)
+    assert np.allclose(s, 1.0 / (n_ctx + 1), rtol=1e-13, atol=0)
+    vn = np.linspace(0.5, 3.0, Hkv * n_ctx).reshape(Hkv, n_ctx)
+    hn = np.linspace(2.0, 0.25, n_q)
+    sw = oracle.max_scores(Q, d["Kctx"], L, 0.125, Hkv, vnorm=vn, hnorm=hn)
+    nv = n_ctx + (np.arange(n_q) % C) + 1.0
+    want = vn * np.max(1.0 / (nv * hn))
+    assert np.allclose(sw, want, rtol=1e-13, atol=0)
+
+
+def pin_max_orthogonal_keys():
+    """Orthogonal keys k_i = e_i (D = 64, 16 context keys, zero self keys) and
+    queries 64 * e_j on query head 1 only (other heads zero), scale 1. Head 1
+    belongs to KV head 0 when G = 2, so on KV head 0 key i is hit once, by
+    j = i: s_i = e^64 / (e^64 + 16 + i); KV head 1 only sees zero queries:
+    s_i = 1/17."""
+    D, T = 64, 16
+    Hq, Hkv = 4, 2
+    K = np.zeros((Hkv, T, D), dtype=np.float32)
+    for h in range(Hkv):
+        K[h, np.arange(T), np.arange(T)] = 1.0
+    Q = np.zeros((Hq, T, D), dtype=np.float32)
+    Q[1, np.arange(T), np.arange(T)] = 64.0
+    Qb, Kb = _bits(Q), _bits(K)
+    Ks = np.zeros((Hkv, T, D), dtype=np.uint16)
+    L = oracle.lse(Qb, Kb, Ks, 1.0, REPEAT, T)
+    s = oracle.max_scores(Qb, Kb, L, 1.0, Hkv)
+    i = np.arange(T)
+    want0 = 1.0 / (1.0 + (16.0 + i) * math.exp(-64.0))
+    assert np.allclose(s[0], want0, rtol=1e-15, atol=0)
+    assert np.all(s[0] >= 1 - 32 * math.exp(-64.0))
+    assert np.allclose(s[1], 1.0 / 17.0, rtol=1e-13, atol=0)
+
+
+def pin_max_brute_force():
+    """Scores against brute force: scipy softmax over each (g, j)'s visible
+    logits, then a plain max over queries and the group's heads."""
+    Hq, Hkv, D, n_ctx, n_q, C = 4, 2, 64, 6, 7, 3
+    d = _tiny(13, Hq, Hkv, D, n_ctx, n_q, REPEAT, C, qstd=1.5)
+    vn = np.linspace(1.0, 2.0, Hkv * n_ctx).reshape(Hkv, n_ctx)
+    hn = np.linspace(1.5, 0.5, n_q)
+    Qf = synth.bf16_to_f32(d["Q"]).astype(np.float64)
+    Kc = synth.bf16_to_f32(d["Kctx"]).astype(np.float64)
+    Ks = synth.bf16_to_f32(d["Kself"]).astype(np.float64)
+    L = oracle.lse(d["Q"], d["Kctx"], d["Kself"], 0.25, REPEAT, C)
+    s = oracle.max_scores(d["Q"], d["Kctx"], L, 0.25, Hkv, vnorm=vn, hnorm=hn)
+    for h in range(Hkv):
+        for i in range(n_ctx):
+            best = 0.0
+            for g in range(h * 2, h * 2 + 2):
+                for j in range(n_q):
+                    a = scipy.special.softmax(_brute_visible(Qf, Kc, Ks, g, h, j, 0.25, REPEAT, C, n_q))
+                    best = max(best, a[i] * vn[h, i] / hn[j])
+            assert abs(s[h, i] - best) <= 1e-12 * best, (h, i)
+
+
+def pin_max_weight_scaling():
+    """Eq. 3's weights act linearly: doubling vnorm doubles the score, and a
+    constant hnorm c divides it by c."""
+    d = _tiny(17, 4, 2, 64, 10, 8, REPEAT, 4, qstd=1.0)
+    L = oracle.lse(d["Q"], d["Kctx"], d["Kself"], 0.5, REPEAT, 4)
+    s = oracle.max_scores(d["Q"], d["Kctx"], L, 0.5, 2)
+    s2 = oracle.max_scores(d["Q"], d["Kctx"], L, 0.5, 2, vnorm=np.full((2, 10), 2.0),
+                           hnorm=np.full(8, 4.0))
+    assert np.allclose(s2, s * 0.5, rtol=1e-14, atol=0)
+
+
+# ---------------------------------------------------------------- sum-mode pins
+
+def _causal_lse(d, scale):
+    return oracle.lse(d["Q"], d["Kctx"], None, scale, CAUSAL, 0)
+
+
+def pin_sum_zero_queries():
+    """Q = 0: a_ji = 1/(j+1) under the causal mask, so
+    t_i = G * sum_{j=i+w}^{T-1} 1/(j+1) (a harmonic tail)."""
+    Hq, Hkv, D, T = 6, 2, 64, 12
+    d = _tiny(19, Hq, Hkv, D, T, T, CAUSAL, 0)
+    Q = np.zeros((Hq, T, D), dtype=np.uint16)
+    L = oracle.lse(Q, d["Kctx"], None, 0.125, CAUSAL, 0)
+    for w in (0, 1, 3, 11, 12, 40):
+        t = oracle.future_mass(Q, d["Kctx"], L, 0.125, w, Hkv)
+        want = np.array([3 * sum(1.0 / (j + 1) for j in range(i + w, T)) for i in range(T)])
+        assert np.allclose(t, want[None, :], rtol=1e-13, atol=1e-15), w
+
+
+def pin_sum_mass_conservation():
+    """w = 0: every query row's softmax sums to 1 and every visible key is
+    counted, so the targets of a KV head add up to G * T."""
+    Hq, Hkv, D, T = 8, 2, 64, 23
+    d = _tiny(23, Hq, Hkv, D, T, T, CAUSAL, 0, qstd=2.0)
+    L = _causal_lse(d, 0.5)
+    t = oracle.future_mass(d["Q"], d["Kctx"], L, 0.5, 0, Hkv)
+    assert np.allclose(t.sum(axis=1), 4 * T, rtol=1e-13, atol=0)
+    t_big = oracle.future_mass(d["Q"], d["Kctx"], L, 0.5, T, Hkv)
+    assert np.all(t_big == 0.0)
+
+
+def pin_sum_brute_force():
+    """Future mass against brute force with scipy softmax rows."""
+    Hq, Hkv, D, T, w = 4, 2, 64, 9, 2
+    d = _tiny(29, Hq, Hkv, D, T, T, CAUSAL, 0, qstd=1.5)
+    Qf = synth.bf16_to_f32(d["Q"]).astype(np.float64)
+    Kc = synth.bf16_to_f32(d["Kctx"]).astype(np.float64)
+    vn = np.linspace(0.5, 1.5, Hkv * T).reshape(Hkv, T)
+    hn = np.linspace(1.0, 3.0, T)
+    L = _causal_lse(d, 0.25)
+    t = oracle.future_mass(d["Q"], d["Kctx"], L, 0.25, w, Hkv, vnorm=vn, hnorm=hn)
+    for h in range(Hkv):
+        for i in range(T):
+            acc = []
+            for g in range(h * 2, h * 2 + 2):
+                for j in range(i + w, T):
+                    a = scipy.special.softmax(_brute_visible(Qf, Kc, None, g, h, j, 0.25, CAUSAL, 0, T))
+                    acc.append(a[i] * vn[h, i] / hn[j])
+            want = math.fsum(acc)
+            assert abs(t[h, i] - want) <= 1e-12 * max(want, 1e-300), (h, i)
+
+
+# ---------------------------------------------------------------- selection pins
+
+def _sel_scores():
+    s = synth.evict_scores(31, 3, 200, tie_frac=0.2, zero_frac=0.05)
+    s[1, 5] = np.float32(-0.0)
+    s[1, 6] = np.float32(0.0)
+    s[2, 7] = np.nan
+    s[2, 8] = np.inf
+    s[2, 9] = -np.inf
+    s[0, 3] = np.nan
+    return s
+
+
+def pin_select_topk_library_order():
+    """Top-k equals the first k of Python's sort on (NaN last, -score,
+    position) over the non-window keys, plus the window."""
+    s = _sel_scores()
+    for k, w in [(0, 0), (17, 10), (50, 0), (190, 10), (500, 30), (5, 200), (5, 250)]:
+        kept = oracle.select(s, w, k=k)
+        for h in range(s.shape[0]):
+            n = s.shape[1]
+            ww = min(w, n)
+            cand = s[h, : n - ww].astype(np.float64).tolist()
+            order = sorted(range(len(cand)),
+                           key=lambda i: (math.isnan(cand[i]), 0.0 if math.isnan(cand[i]) else -cand[i], i))
+            order = np.asarray(order, dtype=np.int64)
+            want = np.union1d(order[: min(k, n - ww)], np.arange(n - ww, n))
+            assert np.array_equal(kept[h], want), (k, w, h)
+
+
+def pin_select_invariants():
+    """Exactly k' + |W| kept; W kept; ascending; top-k sets nest in k;
+    tau = 0 keeps every non-negative score; tau = inf keeps only the window."""
+    s = _sel_scores()
+    n, w = s.shape[1], 16
+    prev = None
+    for k in range(0, n - w + 3, 7):
+        kept = oracle.select(s, w, k=k)
+        for h in range(s.shape[0]):
+            assert kept[h].size == min(k, n - w) + w
+            assert np.all(np.diff(kept[h]) > 0)
+            assert set(range(n - w, n)) <= set(kept[h].tolist())
+            if prev is not None:
+                assert set(prev[h].tolist()) <= set(kept[h].tolist())
+        prev = kept
+    kept0 = oracle.select(s, w, tau=0.0)
+    for h in range(s.shape[0]):
+        want = np.union1d(np.nonzero(s[h, : n - w] >= 0)[0], np.arange(n - w, n))
+        assert np.array_equal(kept0[h], want)
+    kinf = oracle.select(s, w, tau=np.inf)
+    for h in range(s.shape[0]):
+        want = np.union1d(np.nonzero(s[h, : n - w] == np.inf)[0], np.arange(n - w, n))
+        assert np.array_equal(kinf[h], want)
+
+
+def pin_select_ties_lower_index_first():
+    """Equal scores at the cut are taken lowest position first; -0 == +0."""
+    s = np.array([[1.0, 2.0, 2.0, 2.0, 0.5, 2.0, 3.0, 0.0]], dtype=np.float32)
+    assert oracle.select(s, 1, k=3)[0].tolist() == [1, 2, 6, 7]
+    z = np.array([[-0.0, 0.0, -0.0, 1.0]], dtype=np.float32)
+    assert oracle.select(z, 0, k=2)[0].tolist() == [0, 3]
+    assert oracle.select(z, 0, tau=0.0)[0].tolist() == [0, 1, 2, 3]
+
+
+def pin_select_threshold_is_ge():
+    """Keep iff score >= tau (Algorithm 1's comparison), window always kept."""
+    s = np.array([[0.1, 0.2, 0.3, 0.2, 0.05, 0.0]], dtype=np.float32)
+    assert oracle.select(s, 2, tau=np.float32(0.2))[0].tolist() == [1, 2, 3, 4, 5]
+    assert oracle.select(s, 0, tau=np.float32(0.2))[0].tolist() == [1, 2, 3]
+
+
+# ---------------------------------------------------------------- compaction pins
+
+def pin_compact_rows_bitwise():
+    """Compacted rows are the kept rows, bit for bit, head after head."""
+    K = synth.normal_bf16(41, 1, (3, 50, 64))
+    V = synth.normal_bf16(41, 2, (3, 50, 64))
+    kept = [np.array([0, 7, 49]), np.array([], dtype=np.int64), np.arange(10, 50, 3)]
+    Ko, Vo, off = oracle.compact(K, V, kept)
+    assert off.tolist() == [0, 3, 3, 3 + len(range(10, 50, 3))]
+    r = 0
+    for h, idx in enumerate(kept):
+        for i in idx:
+            assert np.array_equal(Ko[r], K[h, i]) and np.array_equal(Vo[r], V[h, i])
+            r += 1
+
+
+ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

@@ -1,0 +1,69 @@
+"""Plant plausible mistakes in the oracle (on the CPU) and check that at least
+one pin catches each. A mutant is the oracle's source with one edit, loaded
+as a separate module and swapped in for the ``oracle`` package's functions."""
+import inspect
+import types
+
+import pytest
+
+import oracle
+import oracle.reference as ref
+import pins
+
+MUTANTS = {
+    "gqa-mapping-modulo": ("return g // G", "return g % G"),
+    "self-diagonal-excluded": ("self_pos[None, :] <= rows[:, None]", "self_pos[None, :] < rows[:, None]"),
+    "self-keys-dropped": ("return np.concatenate([l_ctx, l_self], axis=1)", "return l_ctx"),
+    "causal-diagonal-excluded": ("np.where(keys[None, :] <= rows[:, None], l, -np.inf)",
+                                 "np.where(keys[None, :] < rows[:, None], l, -np.inf)"),
+    "ctx-logit-unscaled": ("l_ctx = scale * (q_rows @ Kctx_h.T)", "l_ctx = (q_rows @ Kctx_h.T)"),
+    "lse-max-term-dropped": ("M[:, 0] + np.log(", "np.log("),
+    "window-edge-exclusive": ("keys[None, :] + window <= rows[:, None]", "keys[None, :] + window < rows[:, None]"),
+    "max-hnorm-dropped": ("w = a * vn[h][None, :] / hn[j0:j1, None]\n            s[h]",
+                          "w = a * vn[h][None, :]\n            s[h]"),
+    "max-vnorm-dropped": ("w = a * vn[h][None, :] / hn[j0:j1, None]\n            s[h]",
+                          "w = a / hn[j0:j1, None]\n            s[h]"),
+    "max-lse-sign": ("a = np.exp(scale * (Qf[g, j0:j1] @ Kc[h].T) - lse_in[g, j0:j1, None])",
+                     "a = np.exp(scale * (Qf[g, j0:j1] @ Kc[h].T) + lse_in[g, j0:j1, None])"),
+    "max-overwrites": ("s[h] = np.maximum(s[h], w.max(axis=0))", "s[h] = w.max(axis=0)"),
+    "max-key-axis": ("s[h] = np.maximum(s[h], w.max(axis=0))", "s[h] = np.maximum(s[h], w.max(axis=1).max())"),
+    "sum-group-overwrites": ("t[h] += w.sum(axis=0)", "t[h] = w.sum(axis=0)"),
+    "sum-hnorm-multiplies": ("a * vn[h][None, :] / hn[j0:j1, None], 0.0)", "a * vn[h][None, :] * hn[j0:j1, None], 0.0)"),
+    "window-not-kept": ("keep[n - w:] = True", "pass"),
+    "threshold-strict": ("keep[cand] |= s[cand] >= float(np.float32(tau))", "keep[cand] |= s[cand] > float(np.float32(tau))"),
+    "ties-higher-index-first": ("order = np.lexsort((cand, neg, is_nan))", "order = np.lexsort((-cand, neg, is_nan))"),
+    "topk-ascending": ("neg = np.where(is_nan, 0.0, -s[cand])", "neg = np.where(is_nan, 0.0, s[cand])"),
+    "compact-reversed": ("K_out[offsets[h]:offsets[h + 1]] = K[h, idx]", "K_out[offsets[h]:offsets[h + 1]] = K[h, idx[::-1]]"),
+    "compact-offsets-shifted": ("offsets = np.concatenate([[0], np.cumsum(counts)])",
+                                "offsets = np.concatenate([np.cumsum(counts), [0]])"),
+}
+
+EXPORTED = ["lse", "attention_weights", "max_scores", "future_mass", "select", "compact",
+            "visible_logits", "kv_head_of", "outside_window"]
+
+
+def _mutant_module(old, new):
+    src = inspect.getsource(ref)
+    assert src.count(old) == 1, f"mutation anchor not unique: {old!r}"
+    mod = types.ModuleType("oracle_mutant")
+    exec(compile(src.replace(old, new), "oracle_mutant", "exec"), mod.__dict__)
+    return mod
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_some_pin_catches_mutant(name, monkeypatch):
+    mod = _mutant_module(*MUTANTS[name])
+    for attr in EXPORTED:
+        monkeypatch.setattr(oracle, attr, getattr(mod, attr))
+    caught = []
+    for pin in pins.ALL_PINS:
+        try:
+            pin()
+        except Exception as e:  # an assertion or an error raised by the mutant
+            caught.append((pin.__name__, type(e).__name__))
+    assert caught, f"no pin caught mutant {name}"
+
+
+def test_unmutated_oracle_passes_all_pins():
+    for pin in pins.ALL_PINS:
+        pin()
