@@ -1,0 +1,181 @@
+/*
+ * kvscore.h — C ABI of the KV-cache importance scoring and eviction library
+ * (libkvscore.so, gfx950 / MI355X).
+ *
+ * What it computes, for one transformer layer, without ever storing an
+ * attention map:
+ *
+ *   kvscore_lse        the log-sum-exp normaliser of every query row, the
+ *                      quantity an attention kernel returns with its output
+ *                      and that the KVpop review's transposed-attention pass
+ *                      reuses ("[논문리뷰] KVpop ...", §1 Key Terms).
+ *   kvscore_max        KVzip's score, the largest attention weight a context
+ *                      key receives from any repeat query and any query head
+ *                      of its GQA group ("KVzap: Fast, Adaptive, and Faithful
+ *                      KV Cache Pruning", §3.1 Eq. 1), optionally weighted by
+ *                      ||W_O v_i|| / ||h_j|| (same page, §3.2 Eq. 3, KVzip+).
+ *   kvscore_futuremass KVpop's future-attention target: the attention mass a
+ *                      key receives from queries at least `window` positions
+ *                      later, i.e. after it has left the protected window
+ *                      (KVpop review, §1 Key Terms), summed over the group.
+ *   kv_evict           per KV head, keep the last `window` keys plus either
+ *                      the k best-scoring other keys (KVpop review §3, per-head
+ *                      top-k) or those scoring >= tau (KVzap page, threshold
+ *                      rule and Algorithm 1), then copy the kept K and V rows
+ *                      into one dense cache, head after head.
+ *
+ * Conventions shared by every call
+ *   - Tensors are device pointers owned by the caller. The library allocates
+ *     nothing and keeps no state between calls.
+ *   - bf16 tensors are passed as their 16-bit patterns (kvs_bf16). The head
+ *     dimension is contiguous; head and token strides are in elements.
+ *   - Logit of query j (query head g) and key i: l = scale * q_j . k_i.
+ *     Query head g reads KV head g / (n_qheads / n_kvheads).
+ *   - Every call is asynchronous on `stream` (a hipStream_t; NULL is the
+ *     default stream) and never synchronises. Arguments are checked on the
+ *     host first; on any error nothing is launched and the status is
+ *     returned. kvs_last_error() then holds a one-line reason (per thread).
+ *   - Calls are thread-safe. Concurrent calls that write the same output race.
+ */
+#ifndef KVSCORE_H
+#define KVSCORE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- status codes ---------------------------------------------------- */
+enum {
+  KVS_OK = 0,
+  KVS_EINVAL = 1,        /* bad argument: null pointer, negative size, shape mismatch */
+  KVS_EUNSUPPORTED = 2,  /* head_dim not 64/128, misaligned pointer or stride */
+  KVS_ECAPACITY = 3,     /* output capacity smaller than the worst-case kept rows */
+  KVS_EWORKSPACE = 4,    /* workspace missing or smaller than kv_evict_workspace_bytes */
+  KVS_EHIP = 5,          /* HIP runtime or launch error (text in kvs_last_error) */
+  KVS_ENODEV = 6         /* no usable gfx950 device is current */
+};
+
+/* ---- masks ----------------------------------------------------------- */
+/* KVS_MASK_REPEAT: the teacher-forced repeat of the context (KVzap page §3.1
+ * repeat prompt; KVzip review "Methods" and "Methods: technical-details").
+ * Repeat query j belongs to chunk c = j / chunk and sees all n_ctx context
+ * keys plus the self keys c*chunk .. j of its own chunk (diagonal included).
+ * KVS_MASK_CAUSAL: plain causal self-attention over one sequence of n_ctx
+ * tokens: query j sees keys 0 .. j. */
+enum { KVS_MASK_REPEAT = 0, KVS_MASK_CAUSAL = 1 };
+
+typedef uint16_t kvs_bf16; /* bfloat16 bit pattern */
+
+/* Shape of one layer's attention, shared by the three scoring calls.
+ *   Q      [n_qheads, n_q, head_dim]    strides q_head_stride, q_tok_stride
+ *   K      [n_kvheads, n_ctx, head_dim] strides k_head_stride, k_tok_stride
+ *          (context keys; for CAUSAL the sequence's keys, n_q == n_ctx)
+ *   Kself  [n_kvheads, n_q, head_dim]   strides ks_head_stride, ks_tok_stride
+ *          (REPEAT only: the keys of the repeated copy; row j is query j's)
+ * Requirements: n_qheads % n_kvheads == 0; head_dim is 64 or 128; every
+ * pointer and every stride keeps rows 16-byte aligned (strides multiple of 8).
+ * chunk > 0 for REPEAT (the last chunk may be shorter); ignored for CAUSAL. */
+typedef struct kvs_attn_desc {
+  int32_t n_qheads;
+  int32_t n_kvheads;
+  int32_t head_dim;
+  int32_t mask;
+  int64_t n_ctx;
+  int64_t n_q;
+  int64_t chunk;
+  int64_t q_head_stride, q_tok_stride;
+  int64_t k_head_stride, k_tok_stride;
+  int64_t ks_head_stride, ks_tok_stride;
+  float scale;
+  int32_t reserved; /* set to 0 */
+} kvs_attn_desc;
+
+/* LSE pass. lse [n_qheads, n_q] fp32, dense, natural log:
+ *   lse[g][j] = ln sum_{i visible to j} exp(scale * q_j . k_i)
+ * over the keys the mask makes visible (context + own-chunk self keys for
+ * REPEAT, keys 0..j for CAUSAL). Kself is ignored (may be NULL) for CAUSAL.
+ * Every query sees at least one key, so every value is finite. */
+int kvscore_lse(const kvs_attn_desc* d, const kvs_bf16* Q, const kvs_bf16* K,
+                const kvs_bf16* Kself, float* lse, void* stream);
+
+/* KVzip / KVzip+ max score (KVzap page §3.1 Eq. 1 and §3.2 Eq. 3), for the
+ * context keys of a REPEAT layer; every repeat query sees every context key:
+ *   s[h][i] = max_{g in group(h)} max_{j < n_q}
+ *             exp(scale * q_j^g . k_i - lse[g][j]) * vnorm[h][i] / hnorm[j]
+ * lse    [n_qheads, n_q] fp32 (normally kvscore_lse's output)
+ * vnorm  [n_kvheads, n_ctx] fp32 >= 0, or NULL for 1 (||W_O v_i||)
+ * hnorm  [n_q] fp32 > 0, or NULL for 1 (||h_j||, one per query position)
+ * scores [n_kvheads, n_ctx] fp32, dense.
+ * accumulate = 0 overwrites scores (0 when n_q == 0); accumulate = 1 keeps
+ * the larger of the stored and the new value, so calling once per chunk of
+ * queries (Q, lse, hnorm pointing at that chunk) equals one call over all.
+ * The stored values must then be >= 0 (earlier scores). desc->mask must be
+ * KVS_MASK_REPEAT; chunk and Kself play no part here. */
+int kvscore_max(const kvs_attn_desc* d, const kvs_bf16* Q, const kvs_bf16* K,
+                const float* lse, const float* vnorm, const float* hnorm,
+                float* scores, int accumulate, void* stream);
+
+/* KVpop future-attention target on CAUSAL self-attention (KVpop review §1):
+ *   t[h][i] = sum_{g in group(h)} sum_{i + window <= j < n_ctx}
+ *             exp(scale * q_j^g . k_i - lse[g][j]) * vnorm[h][i] / hnorm[j]
+ * lse [n_qheads, n_ctx] (the CAUSAL kvscore_lse output); vnorm/hnorm as for
+ * kvscore_max (NULL for 1); target [n_kvheads, n_ctx] fp32, overwritten.
+ * Keys with i + window >= n_ctx get 0. window >= 0. */
+int kvscore_futuremass(const kvs_attn_desc* d, const kvs_bf16* Q,
+                       const kvs_bf16* K, const float* lse, int64_t window,
+                       const float* vnorm, const float* hnorm, float* target,
+                       void* stream);
+
+/* Eviction of one layer's cache.
+ *   scores [n_kvheads, n_tok] fp32, head stride score_head_stride (elements)
+ *   K, V   [n_kvheads, n_tok, head_dim] bf16, strides kv_head_stride,
+ *          kv_tok_stride (shared by K and V)
+ * Per head h, with w = min(window, n_tok):
+ *   window   positions n_tok - w .. n_tok - 1 are always kept;
+ *   top-k    (k >= 0): plus the min(k, n_tok - w) other positions with the
+ *            highest scores; equal scores are taken lowest position first,
+ *            -0 equals +0 and NaN ranks below every number;
+ *   threshold (k < 0): plus the other positions with score >= tau.
+ * Outputs (device):
+ *   head_offsets [n_kvheads + 1] int64: rows of head h are
+ *                head_offsets[h] .. head_offsets[h+1]-1; [n_kvheads] = total
+ *   kept_idx     [capacity] int32: position of each kept row, ascending
+ *                within a head
+ *   K_out, V_out [capacity, head_dim] bf16, dense: bit copies of the rows.
+ * capacity must cover the worst case: n_kvheads * (min(k, n_tok - w) + w) in
+ * top-k mode, n_kvheads * n_tok in threshold mode (where the count is only
+ * known on the device; read head_offsets after synchronising).
+ * workspace: device memory of at least kv_evict_workspace_bytes(e) bytes,
+ * 256-byte aligned, owned by the caller, contents need not be initialised. */
+typedef struct kvs_evict_desc {
+  int32_t n_kvheads;
+  int32_t head_dim;
+  int64_t n_tok;
+  int64_t k;
+  float tau;
+  int32_t reserved; /* set to 0 */
+  int64_t window;
+  int64_t capacity;
+  int64_t kv_head_stride, kv_tok_stride;
+  int64_t score_head_stride;
+} kvs_evict_desc;
+
+size_t kv_evict_workspace_bytes(const kvs_evict_desc* e);
+
+int kv_evict(const kvs_evict_desc* e, const float* scores, const kvs_bf16* K,
+             const kvs_bf16* V, int32_t* kept_idx, int64_t* head_offsets,
+             kvs_bf16* K_out, kvs_bf16* V_out, void* workspace,
+             size_t workspace_bytes, void* stream);
+
+/* ---- diagnostics ----------------------------------------------------- */
+const char* kvs_strerror(int status);   /* static text for a status code */
+const char* kvs_last_error(void);       /* this thread's last failure reason */
+int kvs_version(void);                  /* major * 10000 + minor * 100 + patch */
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* KVSCORE_H */

@@ -1,0 +1,258 @@
+"""Python binding of libkvscore (KV-cache importance scoring and eviction on
+MI355X / gfx950).
+
+Argument marshalling only: every step runs in the library's HIP kernels.
+Torch supplies device memory and the current stream. The functions mirror
+the C ABI in ``include/kvscore.h``:
+
+* :func:`lse`          -> ``kvscore_lse``
+* :func:`max_scores`   -> ``kvscore_max``
+* :func:`future_mass`  -> ``kvscore_futuremass``
+* :func:`evict`        -> ``kv_evict`` (+ ``kv_evict_workspace_bytes``)
+
+Tensors: bf16 ``[heads, tokens, head_dim]`` with a contiguous last dimension
+(any head/token strides that keep rows 16-byte aligned), fp32 normalisers and
+scores. The library allocates nothing; outputs are allocated here with torch
+when not given.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+from . import accounting  # noqa: F401  (host-side, no GPU needed)
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libkvscore.so")
+
+KVS_OK, KVS_EINVAL, KVS_EUNSUPPORTED, KVS_ECAPACITY, KVS_EWORKSPACE, KVS_EHIP, KVS_ENODEV = range(7)
+MASK_REPEAT, MASK_CAUSAL = 0, 1
+
+EXPORTED_SYMBOLS = (
+    "kvscore_lse", "kvscore_max", "kvscore_futuremass", "kv_evict_workspace_bytes", "kv_evict",
+    "kvs_strerror", "kvs_last_error", "kvs_version",
+)
+
+
+class AttnDesc(ctypes.Structure):
+    _fields_ = [
+        ("n_qheads", ctypes.c_int32), ("n_kvheads", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32), ("mask", ctypes.c_int32),
+        ("n_ctx", ctypes.c_int64), ("n_q", ctypes.c_int64), ("chunk", ctypes.c_int64),
+        ("q_head_stride", ctypes.c_int64), ("q_tok_stride", ctypes.c_int64),
+        ("k_head_stride", ctypes.c_int64), ("k_tok_stride", ctypes.c_int64),
+        ("ks_head_stride", ctypes.c_int64), ("ks_tok_stride", ctypes.c_int64),
+        ("scale", ctypes.c_float), ("reserved", ctypes.c_int32),
+    ]
+
+
+class EvictDesc(ctypes.Structure):
+    _fields_ = [
+        ("n_kvheads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+        ("n_tok", ctypes.c_int64), ("k", ctypes.c_int64),
+        ("tau", ctypes.c_float), ("reserved", ctypes.c_int32),
+        ("window", ctypes.c_int64), ("capacity", ctypes.c_int64),
+        ("kv_head_stride", ctypes.c_int64), ("kv_tok_stride", ctypes.c_int64),
+        ("score_head_stride", ctypes.c_int64),
+    ]
+
+
+class KvsError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"[{status}] {message}")
+        self.status = status
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libkvscore.so (built in-tree by ``build.build()``); raises if absent."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing: build it with `python -m kv_cache_eviction_lse_amd.build` "
+                          "(there is no fallback path)")
+    L = ctypes.CDLL(LIB_PATH)
+    vp, i64, i32, c = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_int
+    pA, pE = ctypes.POINTER(AttnDesc), ctypes.POINTER(EvictDesc)
+    L.kvscore_lse.argtypes = [pA, vp, vp, vp, vp, vp]
+    L.kvscore_max.argtypes = [pA, vp, vp, vp, vp, vp, vp, c, vp]
+    L.kvscore_futuremass.argtypes = [pA, vp, vp, vp, i64, vp, vp, vp, vp]
+    L.kv_evict_workspace_bytes.argtypes = [pE]
+    L.kv_evict_workspace_bytes.restype = ctypes.c_size_t
+    L.kv_evict.argtypes = [pE, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
+    L.kvs_strerror.argtypes = [i32]
+    L.kvs_strerror.restype = ctypes.c_char_p
+    L.kvs_last_error.argtypes = []
+    L.kvs_last_error.restype = ctypes.c_char_p
+    L.kvs_version.restype = c
+    for name in ("kvscore_lse", "kvscore_max", "kvscore_futuremass", "kv_evict"):
+        getattr(L, name).restype = c
+    _lib = L
+    return L
+
+
+def check(status: int) -> None:
+    if status != KVS_OK:
+        L = lib()
+        raise KvsError(status, f"{L.kvs_strerror(status).decode()}: {L.kvs_last_error().decode()}")
+
+
+# ---------------------------------------------------------------- helpers
+
+def _torch():
+    import torch
+
+    return torch
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    torch = _torch()
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _bf16(name, t, ndim=3):
+    torch = _torch()
+    if t.dtype != torch.bfloat16:
+        raise TypeError(f"{name} must be bfloat16, got {t.dtype}")
+    if t.dim() != ndim or t.stride(-1) != 1:
+        raise ValueError(f"{name} must be [heads, tokens, head_dim] with a contiguous last dimension")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    return t
+
+
+def _f32(name, t, shape):
+    torch = _torch()
+    if t is None:
+        return None
+    if t.dtype != torch.float32 or not t.is_contiguous() or tuple(t.shape) != tuple(shape) or not t.is_cuda:
+        raise ValueError(f"{name} must be a contiguous float32 GPU tensor of shape {tuple(shape)}")
+    return t
+
+
+def attn_desc(Q, K, Kself, scale, mask, chunk) -> AttnDesc:
+    Hq, n_q, D = Q.shape
+    Hkv, n_ctx, Dk = K.shape
+    if Dk != D:
+        raise ValueError("Q and K head_dim differ")
+    d = AttnDesc()
+    d.n_qheads, d.n_kvheads, d.head_dim = Hq, Hkv, D
+    d.mask = MASK_REPEAT if mask == "repeat" else MASK_CAUSAL
+    d.n_ctx, d.n_q = n_ctx, n_q
+    d.chunk = chunk if chunk else max(n_q, 1)
+    d.q_head_stride, d.q_tok_stride = Q.stride(0), Q.stride(1)
+    d.k_head_stride, d.k_tok_stride = K.stride(0), K.stride(1)
+    if Kself is not None:
+        d.ks_head_stride, d.ks_tok_stride = Kself.stride(0), Kself.stride(1)
+    d.scale = float(scale)
+    d.reserved = 0
+    return d
+
+
+# ---------------------------------------------------------------- entry points
+
+def lse(Q, K, Kself=None, *, scale: float, mask: str = "repeat", chunk: int = 0, out=None, stream=None):
+    """Per-query log-sum-exp [Hq, n_q] fp32 (``kvscore_lse``)."""
+    torch = _torch()
+    _bf16("Q", Q), _bf16("K", K)
+    if mask == "repeat":
+        _bf16("Kself", Kself)
+    d = attn_desc(Q, K, Kself, scale, mask, chunk)
+    if out is None:
+        out = torch.empty((d.n_qheads, d.n_q), dtype=torch.float32, device=Q.device)
+    _f32("out", out, (d.n_qheads, d.n_q))
+    check(lib().kvscore_lse(ctypes.byref(d), _ptr(Q), _ptr(K), _ptr(Kself), _ptr(out), _stream(stream)))
+    return out
+
+
+def max_scores(Q, K, lse_vals, *, scale: float, vnorm=None, hnorm=None, out=None, accumulate: bool = False,
+               stream=None):
+    """KVzip / KVzip+ max score per context key [Hkv, n_ctx] fp32 (``kvscore_max``)."""
+    torch = _torch()
+    _bf16("Q", Q), _bf16("K", K)
+    d = attn_desc(Q, K, None, scale, "repeat", 0)
+    _f32("lse", lse_vals, (d.n_qheads, d.n_q))
+    _f32("vnorm", vnorm, (d.n_kvheads, d.n_ctx))
+    _f32("hnorm", hnorm, (d.n_q,))
+    if out is None:
+        if accumulate:
+            raise ValueError("accumulate needs an existing out tensor")
+        out = torch.empty((d.n_kvheads, d.n_ctx), dtype=torch.float32, device=Q.device)
+    _f32("out", out, (d.n_kvheads, d.n_ctx))
+    check(lib().kvscore_max(ctypes.byref(d), _ptr(Q), _ptr(K), _ptr(lse_vals), _ptr(vnorm), _ptr(hnorm),
+                            _ptr(out), 1 if accumulate else 0, _stream(stream)))
+    return out
+
+
+def future_mass(Q, K, lse_vals, *, scale: float, window: int, vnorm=None, hnorm=None, out=None, stream=None):
+    """KVpop future-attention target per key [Hkv, T] fp32 (``kvscore_futuremass``)."""
+    torch = _torch()
+    _bf16("Q", Q), _bf16("K", K)
+    d = attn_desc(Q, K, None, scale, "causal", 0)
+    _f32("lse", lse_vals, (d.n_qheads, d.n_q))
+    _f32("vnorm", vnorm, (d.n_kvheads, d.n_ctx))
+    _f32("hnorm", hnorm, (d.n_q,))
+    if out is None:
+        out = torch.empty((d.n_kvheads, d.n_ctx), dtype=torch.float32, device=Q.device)
+    _f32("out", out, (d.n_kvheads, d.n_ctx))
+    check(lib().kvscore_futuremass(ctypes.byref(d), _ptr(Q), _ptr(K), _ptr(lse_vals), int(window), _ptr(vnorm),
+                                   _ptr(hnorm), _ptr(out), _stream(stream)))
+    return out
+
+
+def evict_desc(scores, K, *, window: int, k=None, tau=None, capacity=None) -> EvictDesc:
+    if (k is None) == (tau is None):
+        raise ValueError("give exactly one of k, tau")
+    Hkv, n, D = K.shape
+    e = EvictDesc()
+    e.n_kvheads, e.head_dim, e.n_tok = Hkv, D, n
+    e.k = int(k) if k is not None else -1
+    e.tau = float(tau) if tau is not None else 0.0
+    e.reserved = 0
+    e.window = int(window)
+    w = min(int(window), n)
+    need = Hkv * (w + min(int(k), n - w)) if k is not None else Hkv * n
+    e.capacity = need if capacity is None else int(capacity)
+    e.kv_head_stride, e.kv_tok_stride = K.stride(0), K.stride(1)
+    e.score_head_stride = scores.stride(0)
+    return e
+
+
+def evict_workspace_bytes(desc: EvictDesc) -> int:
+    return int(lib().kv_evict_workspace_bytes(ctypes.byref(desc)))
+
+
+def evict(scores, K, V, *, window: int, k=None, tau=None, capacity=None, workspace=None, outputs=None,
+          stream=None):
+    """Keep the window plus top-k / tau-passing keys per KV head and compact K, V
+    (``kv_evict``). Returns (kept_idx int32 [capacity], head_offsets int64 [Hkv+1],
+    K_out, V_out bf16 [capacity, D]); rows past head_offsets[-1] are unused."""
+    torch = _torch()
+    _bf16("K", K), _bf16("V", V)
+    if K.shape != V.shape or K.stride() != V.stride():
+        raise ValueError("K and V must have the same shape and strides")
+    if scores.dtype != torch.float32 or scores.dim() != 2 or (scores.numel() and scores.stride(1) != 1):
+        raise ValueError("scores must be float32 [Hkv, n] with contiguous rows")
+    e = evict_desc(scores, K, window=window, k=k, tau=tau, capacity=capacity)
+    dev = K.device
+    if outputs is None:
+        kept = torch.empty(max(e.capacity, 1), dtype=torch.int32, device=dev)
+        offs = torch.empty(e.n_kvheads + 1, dtype=torch.int64, device=dev)
+        Ko = torch.empty((max(e.capacity, 1), e.head_dim), dtype=torch.bfloat16, device=dev)
+        Vo = torch.empty((max(e.capacity, 1), e.head_dim), dtype=torch.bfloat16, device=dev)
+    else:
+        kept, offs, Ko, Vo = outputs
+    nbytes = evict_workspace_bytes(e)
+    if workspace is None:
+        workspace = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=dev)
+    check(lib().kv_evict(ctypes.byref(e), _ptr(scores), _ptr(K), _ptr(V), _ptr(kept), _ptr(offs), _ptr(Ko),
+                         _ptr(Vo), _ptr(workspace), workspace.numel(), _stream(stream)))
+    return kept, offs, Ko, Vo

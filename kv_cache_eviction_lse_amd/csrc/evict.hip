@@ -1,0 +1,389 @@
+// Per-KV-head eviction: keep the window of the last w keys plus the top-k or
+// the tau-thresholded other keys, and compact the kept K and V rows.
+//
+// Selection rules: the protected window and the ">= tau" comparison of the
+// thresholding rule and Algorithm 1 of "KVzap: Fast, Adaptive, and Faithful KV
+// Cache Pruning"; per-head top-k as in "[논문리뷰] KVpop ..." §3. Kept rows are
+// written in ascending position, head after head (Algorithm 1's keys[indices],
+// values[indices]).
+//
+// Kernels (one grid of blocks of EPB keys per head, unless noted):
+//   top-k only: evict_zero, then three radix-digit histogram passes over the
+//     order-preserving 32-bit keys of the candidate scores (bits 31..21,
+//     20..10, 9..0). Each pass re-derives, from the previous passes'
+//     histograms, the prefix of the k-th largest key, so no separate "find"
+//     launch is needed. After the last pass the k-th key T is exact; keys > T
+//     are kept, and among keys == T the lowest positions up to the quota.
+//   evict_count: per block, rows kept for sure and rows tied at T.
+//   evict_scan (one block): block offsets and per-head offsets.
+//   evict_write: predicate, ballot/prefix scan, index write and a coalesced
+//     gather of the kept K and V rows (16 lanes x 16 bytes per 256-byte row).
+#include "common.hpp"
+#include "internal.hpp"
+
+namespace kvs {
+namespace {
+
+constexpr int EV_THREADS = 256;
+constexpr int EV_PER_THREAD = 8;
+constexpr int EPB = EV_THREADS * EV_PER_THREAD;  // keys per block
+constexpr int NBINS = 2048;
+
+enum Mode : int { MODE_TOPK = 0, MODE_TAU = 1, MODE_ALL = 2, MODE_WINDOW = 3 };
+
+struct EvictParams {
+  const float* scores;
+  int64_t s_hs;
+  const uint16_t* K;
+  const uint16_t* V;
+  int64_t kv_hs, kv_ts;
+  int32_t* kept_idx;
+  int64_t* head_offsets;
+  uint16_t* K_out;
+  uint16_t* V_out;
+  uint32_t* hist;   // [3][Hkv][NBINS]
+  int32_t* blk;     // [Hkv][nb][4]: kept-for-sure, tied, offset in head, ties before
+  int32_t* state;   // [Hkv][4]: threshold key T (bits), quota
+  int64_t n, n_cand, kprime;
+  int Hkv, D, nb, mode;
+  float tau;
+};
+
+// Order-preserving key: a > b as floats <=> key(a) > key(b); -0 and +0 share
+// a key; NaN maps below every number.
+__device__ __forceinline__ uint32_t order_key(float s) {
+  if (s != s) return 0u;
+  uint32_t b = __float_as_uint(s);
+  if (b == 0x80000000u) b = 0u;
+  return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+}
+
+__device__ __forceinline__ int digit_shift(int pass) { return pass == 0 ? 21 : (pass == 1 ? 10 : 0); }
+__device__ __forceinline__ uint32_t digit_mask(int pass) { return pass == 2 ? 1023u : 2047u; }
+
+// Exclusive prefix sum over the block's threads (tid order); *total gets the sum.
+__device__ int block_exclusive_scan(int v, int* total) {
+  __shared__ int s_wave[EV_THREADS / WAVE];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int x = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(x, o);
+    if (lane >= o) x += y;
+  }
+  if (lane == 63) s_wave[wave] = x;
+  __syncthreads();
+  int before = 0, tot = 0;
+#pragma unroll
+  for (int w = 0; w < EV_THREADS / WAVE; ++w) {
+    const int t = s_wave[w];
+    if (w < wave) before += t;
+    tot += t;
+  }
+  __syncthreads();
+  *total = tot;
+  return before + x - v;
+}
+
+// Walk the finished histogram passes of head h and return the prefix of the
+// k-th largest candidate key, the number of candidates above that prefix's
+// range, and the rank still to find inside it. Block-wide; every thread
+// returns the same values.
+__device__ void radix_state(const EvictParams& p, int h, int passes, uint32_t& prefix, int& above, int& rank) {
+  __shared__ int s_digit, s_cum;
+  prefix = 0;
+  above = 0;
+  rank = (int)p.kprime;
+  for (int pass = 0; pass < passes; ++pass) {
+    const uint32_t* bins = p.hist + ((int64_t)pass * p.Hkv + h) * NBINS;
+    const int nbins = pass == 2 ? 1024 : 2048;
+    const int per = nbins / EV_THREADS;  // 8 or 4 bins per thread
+    const int rt = EV_THREADS - 1 - (int)threadIdx.x;  // reversed: high digits first
+    int mine = 0;
+    for (int k = 0; k < per; ++k) mine += (int)bins[rt * per + k];
+    int tot;
+    const int higher = block_exclusive_scan(mine, &tot);  // keys in higher digit bins
+    if (higher < rank && rank <= higher + mine) {
+      int cum = higher;
+      for (int k = per - 1; k >= 0; --k) {
+        const int c = (int)bins[rt * per + k];
+        if (cum + c >= rank) {
+          s_digit = rt * per + k;
+          s_cum = cum;
+          break;
+        }
+        cum += c;
+      }
+    }
+    __syncthreads();
+    prefix |= (uint32_t)s_digit << digit_shift(pass);
+    above += s_cum;
+    rank -= s_cum;
+    __syncthreads();
+  }
+}
+
+__global__ void evict_zero(uint32_t* p, int64_t n) {
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride) p[i] = 0u;
+}
+
+template <int PASS>
+__global__ __launch_bounds__(EV_THREADS) void evict_hist(EvictParams p) {
+  __shared__ uint32_t s_hist[NBINS];
+  const int h = blockIdx.y, b = blockIdx.x;
+  for (int i = threadIdx.x; i < NBINS; i += EV_THREADS) s_hist[i] = 0u;
+  uint32_t prefix = 0;
+  int above, rank;
+  if (PASS > 0) radix_state(p, h, PASS, prefix, above, rank);
+  __syncthreads();
+  const int hs = PASS > 0 ? digit_shift(PASS - 1) : 32;
+  const int64_t i0 = (int64_t)b * EPB + threadIdx.x * EV_PER_THREAD;
+  const float* sc = p.scores + (int64_t)h * p.s_hs;
+#pragma unroll
+  for (int e = 0; e < EV_PER_THREAD; ++e) {
+    const int64_t i = i0 + e;
+    if (i < p.n_cand) {
+      const uint32_t u = order_key(sc[i]);
+      if (PASS == 0 || (u >> hs) == (prefix >> hs))
+        atomicAdd(&s_hist[(u >> digit_shift(PASS)) & digit_mask(PASS)], 1u);
+    }
+  }
+  __syncthreads();
+  uint32_t* g = p.hist + ((int64_t)PASS * p.Hkv + h) * NBINS;
+  for (int i = threadIdx.x; i < NBINS; i += EV_THREADS)
+    if (s_hist[i]) atomicAdd(&g[i], s_hist[i]);
+}
+
+// keep classes of key i: 2 = kept for sure, 1 = tied at T (top-k), 0 = dropped
+__device__ __forceinline__ int keep_class(const EvictParams& p, int64_t i, float s, uint32_t T) {
+  if (i >= p.n_cand) return 2;  // protected window
+  switch (p.mode) {
+    case MODE_TOPK: {
+      const uint32_t u = order_key(s);
+      return u > T ? 2 : (u == T ? 1 : 0);
+    }
+    case MODE_TAU: return s >= p.tau ? 2 : 0;
+    case MODE_ALL: return 2;
+    default: return 0;
+  }
+}
+
+__global__ __launch_bounds__(EV_THREADS) void evict_count(EvictParams p) {
+  const int h = blockIdx.y, b = blockIdx.x;
+  uint32_t T = 0;
+  int quota = 0;
+  if (p.mode == MODE_TOPK) {
+    uint32_t prefix;
+    int above, rank;
+    radix_state(p, h, 3, prefix, above, rank);
+    T = prefix;
+    quota = (int)p.kprime - above;
+  }
+  if (b == 0 && threadIdx.x == 0) {
+    p.state[h * 4 + 0] = (int32_t)T;
+    p.state[h * 4 + 1] = quota;
+  }
+  const int64_t i0 = (int64_t)b * EPB + threadIdx.x * EV_PER_THREAD;
+  const float* sc = p.scores + (int64_t)h * p.s_hs;
+  int sure = 0, tied = 0;
+#pragma unroll
+  for (int e = 0; e < EV_PER_THREAD; ++e) {
+    const int64_t i = i0 + e;
+    if (i < p.n) {
+      const int c = keep_class(p, i, i < p.n_cand ? sc[i] : 0.f, T);
+      sure += c == 2;
+      tied += c == 1;
+    }
+  }
+  int tot_sure, tot_tied;
+  block_exclusive_scan(sure, &tot_sure);
+  block_exclusive_scan(tied, &tot_tied);
+  if (threadIdx.x == 0) {
+    int32_t* e = p.blk + ((int64_t)h * p.nb + b) * 4;
+    e[0] = tot_sure;
+    e[1] = tot_tied;
+  }
+}
+
+__global__ __launch_bounds__(EV_THREADS) void evict_scan(EvictParams p) {
+  int64_t running = 0;
+  for (int h = 0; h < p.Hkv; ++h) {
+    const int quota = p.mode == MODE_TOPK ? p.state[h * 4 + 1] : 0;
+    if (threadIdx.x == 0) p.head_offsets[h] = running;
+    int sure_base = 0, tied_base = 0;
+    for (int b0 = 0; b0 < p.nb; b0 += EV_THREADS) {
+      const int b = b0 + (int)threadIdx.x;
+      int32_t* e = p.blk + ((int64_t)h * p.nb + (b < p.nb ? b : 0)) * 4;
+      const int sure = b < p.nb ? e[0] : 0;
+      const int tied = b < p.nb ? e[1] : 0;
+      int ts, tt;
+      const int sb = block_exclusive_scan(sure, &ts) + sure_base;
+      const int tb = block_exclusive_scan(tied, &tt) + tied_base;
+      if (b < p.nb) {
+        e[2] = sb + min(tb, quota);
+        e[3] = tb;
+      }
+      sure_base += ts;
+      tied_base += tt;
+    }
+    running += sure_base + min(tied_base, quota);
+  }
+  if (threadIdx.x == 0) p.head_offsets[p.Hkv] = running;
+}
+
+template <int D>
+__global__ __launch_bounds__(EV_THREADS) void evict_write(EvictParams p) {
+  __shared__ int32_t s_list[EPB];
+  const int h = blockIdx.y, b = blockIdx.x;
+  const uint32_t T = (uint32_t)p.state[h * 4 + 0];
+  const int quota = p.state[h * 4 + 1];
+  const int32_t* e = p.blk + ((int64_t)h * p.nb + b) * 4;
+  const int blk_off = e[2];
+  const int ties_before = e[3];
+  const int64_t head_off = p.head_offsets[h];
+
+  const int64_t i0 = (int64_t)b * EPB + threadIdx.x * EV_PER_THREAD;
+  const float* sc = p.scores + (int64_t)h * p.s_hs;
+  int cls[EV_PER_THREAD];
+  int tied = 0;
+#pragma unroll
+  for (int k = 0; k < EV_PER_THREAD; ++k) {
+    const int64_t i = i0 + k;
+    cls[k] = i < p.n ? keep_class(p, i, i < p.n_cand ? sc[i] : 0.f, T) : 0;
+    tied += cls[k] == 1;
+  }
+  int tot;
+  int tie_rank = ties_before + block_exclusive_scan(tied, &tot);
+  int keep = 0;
+#pragma unroll
+  for (int k = 0; k < EV_PER_THREAD; ++k) {
+    if (cls[k] == 1) {
+      cls[k] = tie_rank < quota ? 2 : 0;
+      ++tie_rank;
+    }
+    keep += cls[k] == 2;
+  }
+  int n_keep;
+  int pos = block_exclusive_scan(keep, &n_keep);
+#pragma unroll
+  for (int k = 0; k < EV_PER_THREAD; ++k) {
+    if (cls[k] == 2) {
+      const int64_t i = i0 + k;
+      p.kept_idx[head_off + blk_off + pos] = (int32_t)i;
+      s_list[pos] = (int32_t)i;
+      ++pos;
+    }
+  }
+  __syncthreads();
+
+  // gather: LPR lanes per row, 16 bytes each
+  constexpr int LPR = D / 8;
+  constexpr int RPP = EV_THREADS / LPR;  // rows per pass
+  constexpr int UNROLL = 4;
+  const int part = threadIdx.x % LPR;
+  const int r0 = threadIdx.x / LPR;
+  const uint16_t* Kh = p.K + (int64_t)h * p.kv_hs + part * 8;
+  const uint16_t* Vh = p.V + (int64_t)h * p.kv_hs + part * 8;
+  uint16_t* Ko = p.K_out + (head_off + blk_off) * D + part * 8;
+  uint16_t* Vo = p.V_out + (head_off + blk_off) * D + part * 8;
+  for (int rb = 0; rb < n_keep; rb += RPP * UNROLL) {
+    u32x4 kv[UNROLL], vv[UNROLL];
+#pragma unroll
+    for (int u = 0; u < UNROLL; ++u) {
+      const int r = rb + u * RPP + r0;
+      if (r < n_keep) {
+        const int64_t src = (int64_t)s_list[r] * p.kv_ts;
+        kv[u] = ld16(Kh + src);
+        vv[u] = ld16(Vh + src);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < UNROLL; ++u) {
+      const int r = rb + u * RPP + r0;
+      if (r < n_keep) {
+        st16(Ko + (int64_t)r * D, kv[u]);
+        st16(Vo + (int64_t)r * D, vv[u]);
+      }
+    }
+  }
+}
+
+struct WsLayout {
+  size_t hist, blk, state, total;
+};
+
+WsLayout ws_layout(int Hkv, int nb) {
+  auto al = [](size_t x) { return (x + 255) & ~(size_t)255; };
+  WsLayout L;
+  L.hist = 0;
+  L.blk = al((size_t)3 * Hkv * NBINS * 4);
+  L.state = L.blk + al((size_t)Hkv * (nb > 0 ? nb : 1) * 16);
+  L.total = L.state + al((size_t)Hkv * 16);
+  return L;
+}
+
+}  // namespace
+
+size_t evict_workspace_bytes(const kvs_evict_desc& e) {
+  const int64_t nb = (e.n_tok + EPB - 1) / EPB;
+  return ws_layout(e.n_kvheads, (int)nb).total;
+}
+
+hipError_t launch_evict(const kvs_evict_desc& e, const float* scores, const uint16_t* K, const uint16_t* V,
+                        int32_t* kept_idx, int64_t* head_offsets, uint16_t* K_out, uint16_t* V_out,
+                        void* workspace, hipStream_t s) {
+  EvictParams p{};
+  p.scores = scores;
+  p.s_hs = e.score_head_stride;
+  p.K = K;
+  p.V = V;
+  p.kv_hs = e.kv_head_stride;
+  p.kv_ts = e.kv_tok_stride;
+  p.kept_idx = kept_idx;
+  p.head_offsets = head_offsets;
+  p.K_out = K_out;
+  p.V_out = V_out;
+  p.Hkv = e.n_kvheads;
+  p.D = e.head_dim;
+  p.n = e.n_tok;
+  const int64_t w = e.window < e.n_tok ? e.window : e.n_tok;
+  p.n_cand = e.n_tok - w;
+  p.nb = (int)((e.n_tok + EPB - 1) / EPB);
+  p.tau = e.tau;
+  if (e.k < 0) {
+    p.mode = MODE_TAU;
+  } else {
+    p.kprime = e.k < p.n_cand ? e.k : p.n_cand;
+    p.mode = p.kprime == 0 ? MODE_WINDOW : (p.kprime == p.n_cand ? MODE_ALL : MODE_TOPK);
+  }
+  const WsLayout L = ws_layout(p.Hkv, p.nb);
+  char* ws = static_cast<char*>(workspace);
+  p.hist = reinterpret_cast<uint32_t*>(ws + L.hist);
+  p.blk = reinterpret_cast<int32_t*>(ws + L.blk);
+  p.state = reinterpret_cast<int32_t*>(ws + L.state);
+
+  const dim3 grid(p.nb > 0 ? p.nb : 1, p.Hkv);
+  hipError_t err;
+  if (p.nb > 0) {
+    if (p.mode == MODE_TOPK) {
+      hipLaunchKernelGGL(evict_zero, dim3(64), dim3(256), 0, s, p.hist, (int64_t)3 * p.Hkv * NBINS);
+      hipLaunchKernelGGL(evict_hist<0>, grid, dim3(EV_THREADS), 0, s, p);
+      hipLaunchKernelGGL(evict_hist<1>, grid, dim3(EV_THREADS), 0, s, p);
+      hipLaunchKernelGGL(evict_hist<2>, grid, dim3(EV_THREADS), 0, s, p);
+    }
+    hipLaunchKernelGGL(evict_count, grid, dim3(EV_THREADS), 0, s, p);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+  }
+  hipLaunchKernelGGL(evict_scan, dim3(1), dim3(EV_THREADS), 0, s, p);
+  if ((err = hipGetLastError()) != hipSuccess) return err;
+  if (p.nb > 0) {
+    if (p.D == 128)
+      hipLaunchKernelGGL(evict_write<128>, grid, dim3(EV_THREADS), 0, s, p);
+    else
+      hipLaunchKernelGGL(evict_write<64>, grid, dim3(EV_THREADS), 0, s, p);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace kvs

@@ -1,0 +1,28 @@
+// Host-side launch entry points of the kernels (called by api.cpp after the
+// arguments have been validated). Each returns the hipError_t of its launches.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/kvscore.h"
+
+namespace kvs {
+
+hipError_t launch_lse(const kvs_attn_desc& d, const uint16_t* Q, const uint16_t* K, const uint16_t* Kself,
+                      float* lse, hipStream_t s);
+
+hipError_t launch_score_max(const kvs_attn_desc& d, const uint16_t* Q, const uint16_t* K, const float* lse,
+                            const float* vnorm, const float* hnorm, float* scores, int accumulate,
+                            int num_cus, hipStream_t s);
+
+hipError_t launch_score_sum(const kvs_attn_desc& d, const uint16_t* Q, const uint16_t* K, const float* lse,
+                            int64_t window, const float* vnorm, const float* hnorm, float* target,
+                            hipStream_t s);
+
+size_t evict_workspace_bytes(const kvs_evict_desc& e);
+
+hipError_t launch_evict(const kvs_evict_desc& e, const float* scores, const uint16_t* K, const uint16_t* V,
+                        int32_t* kept_idx, int64_t* head_offsets, uint16_t* K_out, uint16_t* V_out,
+                        void* workspace, hipStream_t s);
+
+}  // namespace kvs

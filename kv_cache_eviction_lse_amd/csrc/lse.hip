@@ -1,0 +1,270 @@
+// LSE pass: lse_j = ln sum_{i visible to j} exp(scale * q_j . k_i) for every
+// query row, the normaliser an attention kernel returns with its output
+// ("[논문리뷰] KVpop ..." §1, transposed-attention pass), here without the PV
+// product.
+//
+// Visibility:
+//   REPEAT - the teacher-forced repeat of the context ("KVzap: Fast, Adaptive,
+//            and Faithful KV Cache Pruning" §3.1; KVzip review, "Methods" and
+//            "Methods: technical-details"): query j of chunk c sees all
+//            context keys and the self keys of chunk c up to position j.
+//   CAUSAL - key i is visible to query j iff i <= j.
+//
+// Layout of the work:
+//   * a workgroup (4 waves) serves 8 query subtiles of one KV head; a subtile
+//     is 32 consecutive positions of one query head, and subtiles are ordered
+//     position-major then head, so the G heads of a GQA group at the same
+//     positions sit in the same workgroup and share every key tile;
+//   * each wave keeps its 2 subtiles in VGPRs as MFMA B operands (queries are
+//     columns); key tiles of 32 rows stream through a double-buffered LDS
+//     stage and are the A operands (keys are rows), so each lane's 16
+//     accumulator registers are 16 keys of one query: the softmax reduction
+//     is in-register, and the two half-waves merge once at the end;
+//   * online softmax in the exp2 domain on raw dot products: running max m,
+//     running sum l of exp2((q.k - m) * scale * log2 e);
+//   * tiles a subtile cannot see are skipped; only tiles cut by the causal
+//     diagonal, a chunk edge or the end of the keys are masked per element.
+#include "common.hpp"
+#include "internal.hpp"
+
+namespace kvs {
+namespace {
+
+struct LseParams {
+  const uint16_t* Q;
+  const uint16_t* K;      // context keys (REPEAT) or the sequence's keys (CAUSAL)
+  const uint16_t* Kself;  // REPEAT self keys
+  float* lse;
+  int64_t q_hs, q_ts, k_hs, k_ts, ks_hs, ks_ts;
+  int64_t n_ctx, n_q, chunk;
+  int Hkv, G;
+  int n_sub;  // subtiles per KV head = ceil(n_q / 32) * G
+  float scale;
+};
+
+template <int D>
+struct KTile {
+  static constexpr int STEPS = D / 16;
+  static constexpr int LDS_STRIDE = D * 2 + 16;
+  static constexpr int CHUNKS = 32 * D / 8;
+  static constexpr int BYTES = 32 * LDS_STRIDE;
+};
+
+constexpr int LSE_WAVES = 4;
+constexpr int LSE_NQ = 2;
+constexpr int SUB_PER_BLOCK = LSE_WAVES * LSE_NQ;
+
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(LSE_WAVES * WAVE) void lse_kernel(LseParams p) {
+  using T = KTile<D>;
+  constexpr int NTHREADS = LSE_WAVES * WAVE;
+  constexpr int CPT = (T::CHUNKS + NTHREADS - 1) / NTHREADS;
+  constexpr int CHUNKS_PER_ROW = D / 8;
+
+  __shared__ __attribute__((aligned(16))) char s_k[2][T::BYTES];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int half = lane >> 5;
+  const int col = lane & 31;
+
+  const int b = blockIdx.x;
+  const int h = b % p.Hkv;
+  const int bx = b / p.Hkv;
+  const int u_lo = bx * SUB_PER_BLOCK;
+  const int u_hi = min(u_lo + SUB_PER_BLOCK, p.n_sub) - 1;
+
+  // positions served by the block
+  const int64_t pos_lo = (int64_t)(u_lo / p.G) * 32;
+  const int64_t pos_end = min((int64_t)(u_hi / p.G) * 32 + 32, p.n_q);
+  const int64_t chunk = CAUSAL ? 1 : p.chunk;
+
+  // key segments: REPEAT -> context keys [0, n_ctx) then self keys
+  // [chunk start of pos_lo, pos_end); CAUSAL -> keys [0, pos_end)
+  const int64_t self_lo = CAUSAL ? 0 : (pos_lo / chunk) * chunk;
+  const int64_t n_ctx_tiles = CAUSAL ? 0 : (p.n_ctx + 31) / 32;
+  const int64_t n_self_tiles = (pos_end - self_lo + 31) / 32;
+  const int64_t n_tiles = n_ctx_tiles + n_self_tiles;
+
+  // ---- this wave's subtiles: resident queries (B operands)
+  int sub_g[LSE_NQ];
+  int64_t sub_pos[LSE_NQ];
+  bool sub_ok[LSE_NQ];
+  bf16x8 qreg[LSE_NQ][T::STEPS];
+#pragma unroll
+  for (int q = 0; q < LSE_NQ; ++q) {
+    const int u = u_lo + wave * LSE_NQ + q;
+    sub_ok[q] = u < p.n_sub;
+    sub_g[q] = h * p.G + (sub_ok[q] ? u % p.G : 0);
+    sub_pos[q] = sub_ok[q] ? (int64_t)(u / p.G) * 32 : 0;
+    const int64_t j = sub_pos[q] + col;
+    const bool ok = sub_ok[q] && j < p.n_q;
+    const uint16_t* qp = p.Q + (int64_t)sub_g[q] * p.q_hs + (ok ? j : 0) * p.q_ts + half * (D / 2);
+#pragma unroll
+    for (int s = 0; s < T::STEPS; ++s) {
+      u32x4 v = ok ? ld16(qp + 8 * s) : u32x4{0, 0, 0, 0};
+      qreg[q][s] = as_bf16x8(v);
+    }
+  }
+
+  // tile tt -> first key position kt (segment-relative for context tiles,
+  // sequence position for self/causal tiles), source rows and key count
+  auto tile_src = [&](int64_t tt, const uint16_t*& base, int64_t& ts, int64_t& k0, int64_t& kend) {
+    if (tt < n_ctx_tiles) {
+      base = p.K + (int64_t)h * p.k_hs;
+      ts = p.k_ts;
+      k0 = tt * 32;
+      kend = p.n_ctx;
+    } else {
+      base = CAUSAL ? p.K + (int64_t)h * p.k_hs : p.Kself + (int64_t)h * p.ks_hs;
+      ts = CAUSAL ? p.k_ts : p.ks_ts;
+      k0 = self_lo + (tt - n_ctx_tiles) * 32;
+      kend = pos_end;
+    }
+  };
+
+  u32x4 pre[CPT];
+  auto load_tile = [&](int64_t tt) {
+    const uint16_t* base;
+    int64_t ts, k0, kend;
+    tile_src(tt, base, ts, k0, kend);
+#pragma unroll
+    for (int c = 0; c < CPT; ++c) {
+      const int idx = tid + c * NTHREADS;
+      pre[c] = u32x4{0, 0, 0, 0};
+      if (idx < T::CHUNKS) {
+        const int rr = idx / CHUNKS_PER_ROW, part = idx % CHUNKS_PER_ROW;
+        const int64_t key = k0 + rr;
+        if (key < kend) pre[c] = ld16(base + key * ts + part * 8);
+      }
+    }
+  };
+  auto store_tile = [&](int buf) {
+#pragma unroll
+    for (int c = 0; c < CPT; ++c) {
+      const int idx = tid + c * NTHREADS;
+      if (idx < T::CHUNKS) {
+        const int rr = idx / CHUNKS_PER_ROW, part = idx % CHUNKS_PER_ROW;
+        *reinterpret_cast<u32x4*>(&s_k[buf][rr * T::LDS_STRIDE + part * 16]) = pre[c];
+      }
+    }
+  };
+
+  const float c2 = p.scale * LOG2E;
+  float m_run[LSE_NQ], l_run[LSE_NQ];
+#pragma unroll
+  for (int q = 0; q < LSE_NQ; ++q) {
+    m_run[q] = -INFINITY;
+    l_run[q] = 0.f;
+  }
+
+  if (n_tiles > 0) {
+    load_tile(0);
+    store_tile(0);
+  }
+  __syncthreads();
+
+  for (int64_t tt = 0; tt < n_tiles; ++tt) {
+    const int cur = (int)(tt & 1);
+    if (tt + 1 < n_tiles) load_tile(tt + 1);
+
+    const uint16_t* base_unused;
+    int64_t ts_unused, k0, kend;
+    tile_src(tt, base_unused, ts_unused, k0, kend);
+    const bool is_ctx = tt < n_ctx_tiles;
+
+    bf16x8 a[T::STEPS];
+    const char* krow = &s_k[cur][col * T::LDS_STRIDE + half * (D / 2) * 2];
+#pragma unroll
+    for (int s = 0; s < T::STEPS; ++s) a[s] = as_bf16x8(*reinterpret_cast<const u32x4*>(krow + 16 * s));
+
+#pragma unroll
+    for (int q = 0; q < LSE_NQ; ++q) {
+      if (!sub_ok[q]) continue;
+      const int64_t pj = sub_pos[q];
+      // visibility of this tile for the subtile's 32 queries [pj, pj + 31]
+      bool full, none;
+      if (is_ctx) {
+        none = false;
+        full = k0 + 31 < kend;
+      } else {
+        const int64_t cs_first = CAUSAL ? 0 : (pj / chunk) * chunk;
+        const int64_t cs_last = CAUSAL ? 0 : ((pj + 31) / chunk) * chunk;
+        none = (k0 > pj + 31) || (k0 + 31 < cs_first);
+        full = (k0 + 31 <= pj) && (k0 >= cs_last) && (k0 + 31 < kend);
+      }
+      if (none) continue;
+
+      f32x16 acc = {};
+#pragma unroll
+      for (int s = 0; s < T::STEPS; ++s) acc = mfma32(a[s], qreg[q][s], acc);
+
+      if (!full) {
+        const int64_t j = pj + col;
+        const int64_t cs = (is_ctx || CAUSAL) ? 0 : (j / chunk) * chunk;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int64_t key = k0 + acc_row(r, half);
+          const bool vis = is_ctx ? (key < kend) : (key <= j && key >= cs);
+          acc[r] = vis ? acc[r] : -INFINITY;
+        }
+      }
+
+      float tm = acc[0];
+#pragma unroll
+      for (int r = 1; r < 16; r += 2) tm = max3(tm, acc[r], (r + 1 < 16) ? acc[r + 1] : acc[r]);
+      const float m_new = fmaxf(m_run[q], tm);
+      const float mcs = (m_new == -INFINITY) ? 0.f : m_new * c2;
+      float sum = 0.f;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) sum += fast_exp2(__builtin_fmaf(acc[r], c2, -mcs));
+      l_run[q] = l_run[q] * fast_exp2(__builtin_fmaf(m_run[q], c2, -mcs)) + sum;
+      m_run[q] = m_new;
+    }
+
+    if (tt + 1 < n_tiles) store_tile(cur ^ 1);
+    __syncthreads();
+  }
+
+  // ---- merge half-waves, write natural-log LSE
+#pragma unroll
+  for (int q = 0; q < LSE_NQ; ++q) {
+    const float m_o = __shfl_xor(m_run[q], 32);
+    const float l_o = __shfl_xor(l_run[q], 32);
+    const float M = fmaxf(m_run[q], m_o);
+    const float Mc = (M == -INFINITY) ? 0.f : M * c2;
+    const float L = l_run[q] * fast_exp2(__builtin_fmaf(m_run[q], c2, -Mc)) +
+                    l_o * fast_exp2(__builtin_fmaf(m_o, c2, -Mc));
+    const int64_t j = sub_pos[q] + col;
+    if (half == 0 && sub_ok[q] && j < p.n_q) p.lse[(int64_t)sub_g[q] * p.n_q + j] = (Mc + __log2f(L)) * LN2;
+  }
+}
+
+template <int D, bool CAUSAL>
+hipError_t run(const LseParams& p, int nblocks, hipStream_t s) {
+  hipLaunchKernelGGL((lse_kernel<D, CAUSAL>), dim3(nblocks), dim3(LSE_WAVES * WAVE), 0, s, p);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_lse(const kvs_attn_desc& d, const uint16_t* Q, const uint16_t* K, const uint16_t* Kself,
+                      float* lse, hipStream_t s) {
+  if (d.n_q == 0) return hipSuccess;
+  LseParams p{};
+  p.Q = Q; p.K = K; p.Kself = Kself; p.lse = lse;
+  p.q_hs = d.q_head_stride; p.q_ts = d.q_tok_stride;
+  p.k_hs = d.k_head_stride; p.k_ts = d.k_tok_stride;
+  p.ks_hs = d.ks_head_stride; p.ks_ts = d.ks_tok_stride;
+  p.n_ctx = d.n_ctx; p.n_q = d.n_q; p.chunk = d.chunk;
+  p.Hkv = d.n_kvheads; p.G = d.n_qheads / d.n_kvheads; p.scale = d.scale;
+  const int64_t n_sub = ((d.n_q + 31) / 32) * p.G;
+  p.n_sub = (int)n_sub;
+  const int64_t nblocks = ((n_sub + SUB_PER_BLOCK - 1) / SUB_PER_BLOCK) * p.Hkv;
+  const bool causal = d.mask == KVS_MASK_CAUSAL;
+  if (d.head_dim == 128) return causal ? run<128, true>(p, (int)nblocks, s) : run<128, false>(p, (int)nblocks, s);
+  return causal ? run<64, true>(p, (int)nblocks, s) : run<64, false>(p, (int)nblocks, s);
+}
+
+}  // namespace kvs

@@ -40,17 +40,21 @@ def bf16_bits_to_f64(bits: np.ndarray) -> np.ndarray:
     return b.view(np.float32).astype(np.float64)
 
 
-def _row_blocks(n_q: int, mask: str, chunk: int):
-    """Query-row blocks [j0, j1); under REPEAT no block crosses a chunk edge."""
+def _row_blocks(n_q: int, mask: str, chunk: int, rows=None):
+    """Blocks of query positions (int arrays); under REPEAT a block stays inside
+    one chunk [c0, c1). ``rows`` restricts the positions visited."""
     c = chunk if (mask == REPEAT and chunk > 0) else max(n_q, 1)
+    rows = np.arange(n_q) if rows is None else np.asarray(rows, dtype=np.int64)
     for c0 in range(0, n_q, c):
         c1 = min(c0 + c, n_q)
-        for j0 in range(c0, c1, _ROWS):
-            yield j0, min(j0 + _ROWS, c1), c0, c1
+        in_chunk = rows[(rows >= c0) & (rows < c1)]
+        for b0 in range(0, in_chunk.size, _ROWS):
+            yield in_chunk[b0:b0 + _ROWS], c0, c1
 
 
-def visible_logits(q_rows, j0, Kctx_h, Kself_h, scale, mask, c0=0, c1=0):
-    """Logits of query rows j0.. against the keys they can see; -inf elsewhere.
+def visible_logits(q_rows, rows, Kctx_h, Kself_h, scale, mask, c0=0, c1=0):
+    """Logits of the queries at positions ``rows`` against the keys they can
+    see; -inf elsewhere.
 
     REPEAT ([KVzap] §3.1 repeat prompt; [KVzip] Methods and technical
     details): columns are the n_ctx context keys followed by the self keys of
@@ -58,7 +62,7 @@ def visible_logits(q_rows, j0, Kctx_h, Kself_h, scale, mask, c0=0, c1=0):
     iff p <= j (teacher-forced, causal inside the repeat).
     CAUSAL: columns are the keys 0..n_ctx-1; key i is visible iff i <= j.
     """
-    rows = np.arange(j0, j0 + q_rows.shape[0])
+    rows = np.asarray(rows, dtype=np.int64)
     if mask == REPEAT:
         l_ctx = scale * (q_rows @ Kctx_h.T)
         self_pos = np.arange(c0, c1)
@@ -91,25 +95,28 @@ def _dims(Q, Kctx):
     return Hq, n_q, D, Hkv, Hq // Hkv
 
 
-def lse(Q, Kctx, Kself, scale, mask=REPEAT, chunk=0):
+def lse(Q, Kctx, Kself, scale, mask=REPEAT, chunk=0, rows=None):
     """Per-query log-sum-exp normaliser, natural log, fp64 [Hq, n_q].
 
     LSE_j = ln sum_{i visible to j} exp(l_ji), the normaliser an attention
     kernel returns alongside its output ([KVpop] §1, transposed-attention
     pass), evaluated as M + ln sum exp(l - M) with M the row maximum.
+    ``rows`` (positions) restricts the output to those queries: [Hq, len(rows)].
     """
     Hq, n_q, D, Hkv, G = _dims(Q, Kctx)
     Qf, Kc = bf16_bits_to_f64(Q), bf16_bits_to_f64(Kctx)
     Ks = bf16_bits_to_f64(Kself) if Kself is not None else None
     scale = float(np.float32(scale))
-    out = np.empty((Hq, n_q))
+    want = np.arange(n_q) if rows is None else np.asarray(rows, dtype=np.int64)
+    col_of = {int(j): c for c, j in enumerate(want)}
+    out = np.empty((Hq, want.size))
     for g in range(Hq):
         h = kv_head_of(g, G)
-        for j0, j1, c0, c1 in _row_blocks(n_q, mask, chunk):
-            L = visible_logits(Qf[g, j0:j1], j0, Kc[h], Ks[h] if Ks is not None else None,
+        for blk, c0, c1 in _row_blocks(n_q, mask, chunk, want):
+            L = visible_logits(Qf[g, blk], blk, Kc[h], Ks[h] if Ks is not None else None,
                                scale, mask, c0, c1)
             M = L.max(axis=1, keepdims=True)
-            out[g, j0:j1] = M[:, 0] + np.log(np.exp(L - M).sum(axis=1))
+            out[g, [col_of[int(j)] for j in blk]] = M[:, 0] + np.log(np.exp(L - M).sum(axis=1))
     return out
 
 
@@ -123,12 +130,12 @@ def attention_weights(Q, Kctx, Kself, scale, mask, chunk, g, j0, j1, lse_rows):
     c0 = (j0 // c) * c
     c1 = min(c0 + c, n_q)
     h = kv_head_of(g, G)
-    L = visible_logits(Qf[g, j0:j1], j0, Kc[h], Ks[h] if Ks is not None else None,
+    L = visible_logits(Qf[g, j0:j1], np.arange(j0, j1), Kc[h], Ks[h] if Ks is not None else None,
                        float(np.float32(scale)), mask, c0, c1)
     return np.exp(L - np.asarray(lse_rows, dtype=np.float64)[:, None])
 
 
-def max_scores(Q, Kctx, lse_in, scale, n_kvheads, vnorm=None, hnorm=None):
+def max_scores(Q, Kctx, lse_in, scale, n_kvheads, vnorm=None, hnorm=None, keys=None):
     """KVzip / KVzip+ score of every context key, fp64 [Hkv, n_ctx].
 
     [KVzap] §3.1 Eq. 1: s_i = max over repeat queries j of a_ji, with every
@@ -137,7 +144,7 @@ def max_scores(Q, Kctx, lse_in, scale, n_kvheads, vnorm=None, hnorm=None):
     (``vnorm[h, i]`` and ``hnorm[j]``; either may be omitted, meaning 1).
     a_ji = exp(l_ji - LSE_j), with LSE_j taken as given (``lse_in`` [Hq, n_q]).
     Context keys are visible to every repeat query. With no queries the
-    score is 0.
+    score is 0. ``keys`` (positions) restricts the output to those keys.
     """
     Hq, n_q, D, Hkv, G = _dims(Q, Kctx)
     assert Hkv == n_kvheads
@@ -147,6 +154,10 @@ def max_scores(Q, Kctx, lse_in, scale, n_kvheads, vnorm=None, hnorm=None):
     n_ctx = Kc.shape[1]
     vn = np.ones((Hkv, n_ctx)) if vnorm is None else np.asarray(vnorm, dtype=np.float64)
     hn = np.ones(n_q) if hnorm is None else np.asarray(hnorm, dtype=np.float64)
+    if keys is not None:
+        keys = np.asarray(keys, dtype=np.int64)
+        Kc, vn = Kc[:, keys], vn[:, keys]
+        n_ctx = keys.size
     s = np.zeros((Hkv, n_ctx))
     for g in range(Hq):
         h = kv_head_of(g, G)
@@ -158,7 +169,7 @@ def max_scores(Q, Kctx, lse_in, scale, n_kvheads, vnorm=None, hnorm=None):
     return s
 
 
-def future_mass(Q, K, lse_in, scale, window, n_kvheads, vnorm=None, hnorm=None):
+def future_mass(Q, K, lse_in, scale, window, n_kvheads, vnorm=None, hnorm=None, keys=None):
     """KVpop future-attention target, fp64 [Hkv, T].
 
     [KVpop] §1: the attention mass token i receives after it has left the
@@ -167,7 +178,8 @@ def future_mass(Q, K, lse_in, scale, window, n_kvheads, vnorm=None, hnorm=None):
     j exactly when j >= i + w, so t_i = sum_{g in group} sum_{i+w <= j < T} a_ji,
     a_ji = exp(l_ji - LSE_j) with LSE_j given (``lse_in`` [Hq, T]). Query heads
     of a group are summed. Optional ``vnorm[h, i]`` / ``hnorm[j]`` weight each
-    term as in [KVzap] §3.2 Eq. 3.
+    term as in [KVzap] §3.2 Eq. 3. ``keys`` (positions) restricts the output
+    to those keys.
     """
     Hq, T, D, Hkv, G = _dims(Q, K)
     assert Hkv == n_kvheads and K.shape[1] == T
@@ -176,8 +188,9 @@ def future_mass(Q, K, lse_in, scale, window, n_kvheads, vnorm=None, hnorm=None):
     scale = float(np.float32(scale))
     vn = np.ones((Hkv, T)) if vnorm is None else np.asarray(vnorm, dtype=np.float64)
     hn = np.ones(T) if hnorm is None else np.asarray(hnorm, dtype=np.float64)
-    keys = np.arange(T)
-    t = np.zeros((Hkv, T))
+    keys = np.arange(T) if keys is None else np.asarray(keys, dtype=np.int64)
+    Kf, vn = Kf[:, keys], vn[:, keys]
+    t = np.zeros((Hkv, keys.size))
     for g in range(Hq):
         h = kv_head_of(g, G)
         for j0 in range(0, T, _ROWS):

@@ -304,4 +304,25 @@ def pin_compact_rows_bitwise():
             r += 1
 
 
+# ---------------------------------------------------------------- sampling
+
+def pin_sampled_rows_and_keys_match_full():
+    """Restricting the oracle to sampled query rows or keys returns exactly the
+    matching entries of the full computation (used for full-size sampling)."""
+    d = _tiny(37, 6, 2, 64, 40, 29, REPEAT, 10, qstd=1.0)
+    L = oracle.lse(d["Q"], d["Kctx"], d["Kself"], 0.5, REPEAT, 10)
+    rows = np.array([0, 3, 9, 10, 19, 28])
+    Ls = oracle.lse(d["Q"], d["Kctx"], d["Kself"], 0.5, REPEAT, 10, rows=rows)
+    assert np.array_equal(Ls, L[:, rows])
+    s = oracle.max_scores(d["Q"], d["Kctx"], L, 0.5, 2)
+    keys = np.array([1, 5, 39])
+    assert np.array_equal(oracle.max_scores(d["Q"], d["Kctx"], L, 0.5, 2, keys=keys), s[:, keys])
+    dc = _tiny(41, 4, 2, 64, 30, 30, CAUSAL, 0, qstd=1.0)
+    Lc = _causal_lse(dc, 0.5)
+    t = oracle.future_mass(dc["Q"], dc["Kctx"], Lc, 0.5, 3, 2)
+    keys = np.array([0, 7, 26, 29])
+    assert np.allclose(oracle.future_mass(dc["Q"], dc["Kctx"], Lc, 0.5, 3, 2, keys=keys), t[:, keys],
+                       rtol=1e-14, atol=0)
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

@@ -1,0 +1,199 @@
+"""The C ABI without a GPU: header, exports, argument checks, status text.
+
+Calls here pass invalid arguments (rejected on the host before any HIP call)
+or run only where no GPU is present (then valid calls return KVS_ENODEV)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import kv_cache_eviction_lse_amd as kvs
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kvscore.h")
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(kvs.LIB_PATH):
+        from kv_cache_eviction_lse_amd import build
+
+        build.build()
+    return kvs.lib()
+
+
+def _no_gpu():
+    try:
+        import torch
+
+        return torch.cuda.device_count() == 0
+    except Exception:
+        return True
+
+
+def _declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(kv[a-z_]+)\s*\(", src)))
+
+
+@pytest.mark.parametrize("std,cc", [("c99", "gcc"), ("c++17", "g++")])
+def test_header_compiles(tmp_path, std, cc):
+    src = tmp_path / ("t.c" if cc == "gcc" else "t.cpp")
+    src.write_text('#include "kvscore.h"\nint main(void){ kvs_attn_desc d; kvs_evict_desc e; (void)d; (void)e;'
+                   ' return (int)sizeof(d) + (int)sizeof(e) > 0 ? 0 : 1; }\n')
+    subprocess.run([cc, f"-std={std}", "-Wall", "-Werror", "-pedantic", "-I", os.path.dirname(HEADER),
+                    "-fsyntax-only", str(src)], check=True)
+
+
+def test_exports_match_header(L):
+    declared = _declared_functions()
+    assert set(declared) == set(kvs.EXPORTED_SYMBOLS), declared
+    out = subprocess.run(["nm", "-D", "--defined-only", kvs.LIB_PATH], capture_output=True, text=True,
+                         check=True).stdout
+    exported = {ln.split()[-1] for ln in out.splitlines() if " T " in ln}
+    assert exported == set(declared), exported ^ set(declared)
+
+
+def test_struct_layouts_match_header(tmp_path):
+    src = tmp_path / "sz.c"
+    src.write_text('#include <stdio.h>\n#include <stddef.h>\n#include "kvscore.h"\nint main(void){'
+                   'printf("%zu %zu %zu %zu\\n", sizeof(kvs_attn_desc), offsetof(kvs_attn_desc, scale),'
+                   ' sizeof(kvs_evict_desc), offsetof(kvs_evict_desc, score_head_stride)); return 0; }\n')
+    exe = tmp_path / "sz"
+    subprocess.run(["gcc", "-std=c99", "-I", os.path.dirname(HEADER), str(src), "-o", str(exe)], check=True)
+    got = list(map(int, subprocess.run([str(exe)], capture_output=True, text=True, check=True).stdout.split()))
+    want = [ctypes.sizeof(kvs.AttnDesc), kvs.AttnDesc.scale.offset, ctypes.sizeof(kvs.EvictDesc),
+            kvs.EvictDesc.score_head_stride.offset]
+    assert got == want
+
+
+def test_strerror_covers_codes(L):
+    texts = [L.kvs_strerror(c).decode() for c in range(7)]
+    assert len(set(texts)) == 7 and "unknown" not in " ".join(texts)
+    assert L.kvs_strerror(99).decode() == "unknown status"
+    assert L.kvs_version() >= 100
+
+
+FAKE = ctypes.c_void_p(0x100000)  # 16-byte aligned, never dereferenced: rejected or no device
+
+
+def _desc(**kw):
+    d = kvs.AttnDesc()
+    d.n_qheads, d.n_kvheads, d.head_dim, d.mask = 4, 2, 128, kvs.MASK_REPEAT
+    d.n_ctx, d.n_q, d.chunk = 64, 32, 32
+    d.q_head_stride, d.q_tok_stride = 32 * 128, 128
+    d.k_head_stride, d.k_tok_stride = 64 * 128, 128
+    d.ks_head_stride, d.ks_tok_stride = 32 * 128, 128
+    d.scale, d.reserved = 0.088, 0
+    for k, v in kw.items():
+        setattr(d, k, v)
+    return d
+
+
+ATTN_BAD = [
+    (dict(n_qheads=5), kvs.KVS_EINVAL),
+    (dict(n_kvheads=0), kvs.KVS_EINVAL),
+    (dict(head_dim=96), kvs.KVS_EUNSUPPORTED),
+    (dict(mask=7), kvs.KVS_EINVAL),
+    (dict(n_q=-1), kvs.KVS_EINVAL),
+    (dict(chunk=0), kvs.KVS_EINVAL),
+    (dict(scale=0.0), kvs.KVS_EINVAL),
+    (dict(scale=float("nan")), kvs.KVS_EINVAL),
+    (dict(q_tok_stride=100), kvs.KVS_EUNSUPPORTED),
+    (dict(k_tok_stride=64), kvs.KVS_EINVAL),
+    (dict(reserved=1), kvs.KVS_EINVAL),
+    (dict(mask=kvs.MASK_CAUSAL), kvs.KVS_EINVAL),  # CAUSAL needs n_q == n_ctx
+    (dict(n_ctx=1 << 31), kvs.KVS_EUNSUPPORTED),
+]
+
+
+@pytest.mark.parametrize("kw,code", ATTN_BAD)
+def test_lse_rejects(L, kw, code):
+    d = _desc(**kw)
+    assert L.kvscore_lse(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, None) == code
+    assert L.kvs_last_error().decode()
+
+
+def test_null_and_misaligned_pointers(L):
+    d = _desc()
+    assert L.kvscore_lse(None, FAKE, FAKE, FAKE, FAKE, None) == kvs.KVS_EINVAL
+    assert L.kvscore_lse(ctypes.byref(d), None, FAKE, FAKE, FAKE, None) == kvs.KVS_EINVAL
+    assert L.kvscore_lse(ctypes.byref(d), FAKE, FAKE, None, FAKE, None) == kvs.KVS_EINVAL  # Kself for REPEAT
+    assert L.kvscore_lse(ctypes.byref(d), FAKE, FAKE, FAKE, None, None) == kvs.KVS_EINVAL
+    assert L.kvscore_lse(ctypes.byref(d), ctypes.c_void_p(0x100008), FAKE, FAKE, FAKE, None) == kvs.KVS_EUNSUPPORTED
+
+
+def test_max_and_futuremass_reject(L):
+    d = _desc()
+    assert L.kvscore_max(ctypes.byref(d), FAKE, FAKE, FAKE, None, None, FAKE, 2, None) == kvs.KVS_EINVAL
+    assert L.kvscore_max(ctypes.byref(d), FAKE, FAKE, None, None, None, FAKE, 0, None) == kvs.KVS_EINVAL
+    dc = _desc(mask=kvs.MASK_CAUSAL, n_q=64, q_head_stride=64 * 128)
+    assert L.kvscore_max(ctypes.byref(dc), FAKE, FAKE, FAKE, None, None, FAKE, 0, None) == kvs.KVS_EINVAL
+    assert L.kvscore_futuremass(ctypes.byref(d), FAKE, FAKE, FAKE, 0, None, None, FAKE, None) == kvs.KVS_EINVAL
+    assert L.kvscore_futuremass(ctypes.byref(dc), FAKE, FAKE, FAKE, -1, None, None, FAKE, None) == kvs.KVS_EINVAL
+
+
+def _edesc(**kw):
+    e = kvs.EvictDesc()
+    e.n_kvheads, e.head_dim, e.n_tok, e.k, e.tau, e.reserved = 2, 128, 1000, 100, 0.0, 0
+    e.window, e.capacity = 32, 2 * 132
+    e.kv_head_stride, e.kv_tok_stride, e.score_head_stride = 1000 * 128, 128, 1000
+    for k, v in kw.items():
+        setattr(e, k, v)
+    return e
+
+
+EVICT_BAD = [
+    (dict(n_kvheads=0), kvs.KVS_EINVAL),
+    (dict(head_dim=80), kvs.KVS_EUNSUPPORTED),
+    (dict(n_tok=-5), kvs.KVS_EINVAL),
+    (dict(window=-1), kvs.KVS_EINVAL),
+    (dict(capacity=2 * 131), kvs.KVS_ECAPACITY),
+    (dict(k=-1, capacity=1999), kvs.KVS_ECAPACITY),  # threshold mode needs Hkv * n
+    (dict(kv_tok_stride=132), kvs.KVS_EUNSUPPORTED),
+    (dict(kv_tok_stride=120), kvs.KVS_EINVAL),
+    (dict(score_head_stride=999), kvs.KVS_EINVAL),
+    (dict(reserved=3), kvs.KVS_EINVAL),
+]
+
+
+@pytest.mark.parametrize("kw,code", EVICT_BAD)
+def test_evict_rejects(L, kw, code):
+    e = _edesc(**kw)
+    ws = L.kv_evict_workspace_bytes(ctypes.byref(_edesc()))
+    assert L.kv_evict(ctypes.byref(e), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, ws, None) == code
+
+
+def test_evict_workspace_checks(L):
+    e = _edesc()
+    ws = L.kv_evict_workspace_bytes(ctypes.byref(e))
+    assert ws > 0 and ws % 256 == 0
+    assert L.kv_evict_workspace_bytes(ctypes.byref(_edesc(n_kvheads=0))) == 0
+    assert L.kv_evict(ctypes.byref(e), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, ws, None) == kvs.KVS_EWORKSPACE
+    assert L.kv_evict(ctypes.byref(e), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, ws - 1, None) == kvs.KVS_EWORKSPACE
+    assert L.kv_evict(ctypes.byref(e), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, ctypes.c_void_p(0x100010), ws,
+                      None) == kvs.KVS_EWORKSPACE
+    assert L.kv_evict(ctypes.byref(e), FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE, FAKE, ws, None) == kvs.KVS_EINVAL
+
+
+@pytest.mark.skipif(not _no_gpu(), reason="valid calls would launch on a GPU host")
+def test_valid_calls_without_gpu_return_enodev(L):
+    d = _desc()
+    assert L.kvscore_lse(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, None) == kvs.KVS_ENODEV
+    assert L.kvscore_max(ctypes.byref(d), FAKE, FAKE, FAKE, None, None, FAKE, 0, None) == kvs.KVS_ENODEV
+    dc = _desc(mask=kvs.MASK_CAUSAL, n_q=64, q_head_stride=64 * 128)
+    assert L.kvscore_futuremass(ctypes.byref(dc), FAKE, FAKE, FAKE, 8, None, None, FAKE, None) == kvs.KVS_ENODEV
+    e = _edesc()
+    ws = L.kv_evict_workspace_bytes(ctypes.byref(e))
+    assert L.kv_evict(ctypes.byref(e), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, ws, None) == kvs.KVS_ENODEV
+    assert "device" in L.kvs_last_error().decode()
+
+
+def test_binding_requires_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(kvs, "LIB_PATH", str(tmp_path / "missing.so"))
+    monkeypatch.setattr(kvs, "_lib", None)
+    with pytest.raises(ImportError):
+        kvs.lib()

@@ -1,0 +1,275 @@
+"""GPU path against the CPU oracle, element by element, on seeded inputs small
+enough for the oracle (several tiles, ragged tails, odd GQA groups, D = 64
+and 128, chunk edges, degenerate cases). Every call goes through the C ABI."""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from synth.workloads import TINY_KVZIP, QWEN25_1P5B_2K
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+if not torch.cuda.is_available():  # pragma: no cover
+    pytest.skip("needs a GPU", allow_module_level=True)
+
+import kv_cache_eviction_lse_amd as kvs  # noqa: E402
+from gpu_util import (check_kept, check_lse, check_rows, check_scores, dev_bf16, dev_f32, host,  # noqa: E402
+                      host_bits, kept_from_gpu, say)
+
+
+def _draw(seed, **kw):
+    return synth.draw(synth.Recipe(**kw), seed)
+
+
+def _gpu_lse(d, mask, chunk):
+    r = d["recipe"]
+    Ks = dev_bf16(d["Kself"]) if mask == "repeat" else None
+    out = kvs.lse(dev_bf16(d["Q"]), dev_bf16(d["Kctx"]), Ks, scale=d["scale"], mask=mask, chunk=chunk)
+    torch.cuda.synchronize()
+    return host(out)
+
+
+LSE_CASES = [
+    # name, recipe kwargs, mask, chunk
+    ("repeat-g2-d64", dict(Hq=4, Hkv=2, D=64, n_ctx=256, n_q=256, scale=1.0, q_prescale=0.125), "repeat", 256),
+    ("repeat-g5-ragged-chunks", dict(Hq=10, Hkv=2, D=128, n_ctx=1000, n_q=700, lowrank_rank=8,
+                                      lowrank_scale=2.0), "repeat", 300),
+    ("repeat-g6-chunk1", dict(Hq=6, Hkv=1, D=128, n_ctx=77, n_q=130), "repeat", 1),
+    ("repeat-no-context", dict(Hq=4, Hkv=1, D=64, n_ctx=0, n_q=200), "repeat", 64),
+    ("repeat-one-query", dict(Hq=8, Hkv=8, D=128, n_ctx=513, n_q=1), "repeat", 1),
+    ("repeat-chunk-gt-nq", dict(Hq=3, Hkv=3, D=128, n_ctx=40, n_q=97), "repeat", 4096),
+    ("causal-g6-ragged", dict(Hq=6, Hkv=1, D=128, n_ctx=777, n_q=777, mask="causal"), "causal", 0),
+    ("causal-g4-sinks-d64", dict(Hq=8, Hkv=2, D=64, n_ctx=1000, n_q=1000, mask="causal", sinks=4), "causal", 0),
+    ("causal-tiny", dict(Hq=2, Hkv=1, D=128, n_ctx=3, n_q=3, mask="causal"), "causal", 0),
+]
+
+
+@pytest.mark.parametrize("name,kw,mask,chunk", LSE_CASES, ids=[c[0] for c in LSE_CASES])
+def test_lse_parity(name, kw, mask, chunk):
+    kw = dict(kw)
+    kw.setdefault("mask", mask)
+    kw["chunk"] = chunk
+    d = _draw(101, **kw)
+    say(f"[lse] {name}")
+    g = _gpu_lse(d, mask, chunk)
+    ref = oracle.lse(d["Q"], d["Kctx"], d.get("Kself"), d["scale"], mask, chunk)
+    check_lse(g, ref, name)
+
+
+MAX_CASES = [
+    ("tiny-kvzip", TINY_KVZIP.recipe, False),
+    ("g5-ragged-weighted", synth.Recipe(Hq=10, Hkv=2, D=128, n_ctx=1000, n_q=700, chunk=300, lowrank_rank=8,
+                                        lowrank_scale=2.0, value_norms=True), True),
+    ("g6-d64-weighted", synth.Recipe(Hq=6, Hkv=1, D=64, n_ctx=1537, n_q=333, chunk=128, value_norms=True,
+                                     d_hidden=384), True),
+    ("mha-single-query", synth.Recipe(Hq=2, Hkv=2, D=128, n_ctx=100, n_q=1, chunk=1), False),
+]
+
+
+@pytest.mark.parametrize("name,recipe,weighted", MAX_CASES, ids=[c[0] for c in MAX_CASES])
+def test_max_score_parity(name, recipe, weighted):
+    d = synth.draw(recipe, 202)
+    say(f"[max] {name}")
+    Q, K, Ks = dev_bf16(d["Q"]), dev_bf16(d["Kctx"]), dev_bf16(d["Kself"])
+    chunk = recipe.self_chunk
+    L = kvs.lse(Q, K, Ks, scale=d["scale"], mask="repeat", chunk=chunk)
+    vn = dev_f32(d["vnorm"]) if weighted else None
+    hn = dev_f32(d["hnorm"]) if weighted else None
+    s = kvs.max_scores(Q, K, L, scale=d["scale"], vnorm=vn, hnorm=hn)
+    torch.cuda.synchronize()
+    ref_L = oracle.lse(d["Q"], d["Kctx"], d["Kself"], d["scale"], "repeat", chunk)
+    check_lse(host(L), ref_L, name)
+    ref = oracle.max_scores(d["Q"], d["Kctx"], ref_L, d["scale"], recipe.Hkv,
+                            vnorm=d.get("vnorm") if weighted else None, hnorm=d.get("hnorm") if weighted else None)
+    check_scores(host(s), ref, name)
+
+
+def test_max_score_given_lse_input():
+    """The score pass alone, on a stand-in normaliser that no attention produced."""
+    r = synth.Recipe(Hq=8, Hkv=2, D=128, n_ctx=700, n_q=900, chunk=900, lowrank_rank=8, lowrank_scale=2.0,
+                     value_norms=True)
+    d = synth.draw(r, 303)
+    lse_in = synth.lse_values(303, r.Hq, r.n_q, 6.0, 9.0)
+    say("[max] given-lse")
+    s = kvs.max_scores(dev_bf16(d["Q"]), dev_bf16(d["Kctx"]), dev_f32(lse_in), scale=d["scale"],
+                       vnorm=dev_f32(d["vnorm"]), hnorm=dev_f32(d["hnorm"]))
+    torch.cuda.synchronize()
+    ref = oracle.max_scores(d["Q"], d["Kctx"], lse_in, d["scale"], r.Hkv, vnorm=d["vnorm"], hnorm=d["hnorm"])
+    check_scores(host(s), ref, "given-lse")
+
+
+def test_max_score_accumulate_over_chunks_equals_one_call():
+    r = synth.Recipe(Hq=8, Hkv=2, D=128, n_ctx=600, n_q=1000, chunk=400, value_norms=True)
+    d = synth.draw(r, 404)
+    Q, K, Ks = dev_bf16(d["Q"]), dev_bf16(d["Kctx"]), dev_bf16(d["Kself"])
+    L = kvs.lse(Q, K, Ks, scale=d["scale"], mask="repeat", chunk=400)
+    vn, hn = dev_f32(d["vnorm"]), dev_f32(d["hnorm"])
+    say("[max] accumulate")
+    one = kvs.max_scores(Q, K, L, scale=d["scale"], vnorm=vn, hnorm=hn)
+    acc = torch.zeros_like(one)
+    for c0 in range(0, 1000, 400):
+        c1 = min(c0 + 400, 1000)
+        kvs.max_scores(Q[:, c0:c1], K, L[:, c0:c1].contiguous(), scale=d["scale"], vnorm=vn,
+                       hnorm=hn[c0:c1].contiguous(), out=acc, accumulate=True)
+    torch.cuda.synchronize()
+    assert torch.equal(one, acc)
+
+
+def test_max_score_no_queries_gives_zero():
+    r = synth.Recipe(Hq=4, Hkv=2, D=128, n_ctx=300, n_q=0, chunk=1)
+    d = synth.draw(r, 505)
+    Q = torch.empty((4, 0, 128), dtype=torch.bfloat16, device="cuda")
+    out = torch.full((2, 300), 7.0, device="cuda")
+    kvs.max_scores(Q, dev_bf16(d["Kctx"]), torch.empty((4, 0), device="cuda"), scale=d["scale"], out=out)
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(out).item() == 0
+
+
+SUM_CASES = [
+    ("g4-w128-sinks", synth.Recipe(Hq=8, Hkv=2, D=128, n_ctx=1500, n_q=1500, mask="causal", sinks=4), 128, False),
+    ("g5-w0-weighted", synth.Recipe(Hq=5, Hkv=1, D=128, n_ctx=1100, n_q=1100, mask="causal", value_norms=True,
+                                    d_hidden=640), 0, True),
+    ("g2-d64-w37", synth.Recipe(Hq=4, Hkv=2, D=64, n_ctx=2100, n_q=2100, mask="causal"), 37, False),
+    ("window-covers-all", synth.Recipe(Hq=4, Hkv=2, D=128, n_ctx=300, n_q=300, mask="causal"), 300, False),
+    ("short", synth.Recipe(Hq=2, Hkv=1, D=128, n_ctx=5, n_q=5, mask="causal"), 1, False),
+]
+
+
+@pytest.mark.parametrize("name,recipe,window,weighted", SUM_CASES, ids=[c[0] for c in SUM_CASES])
+def test_future_mass_parity(name, recipe, window, weighted):
+    d = synth.draw(recipe, 606)
+    say(f"[sum] {name}")
+    Q, K = dev_bf16(d["Q"]), dev_bf16(d["Kctx"])
+    L = kvs.lse(Q, K, None, scale=d["scale"], mask="causal")
+    vn = dev_f32(d["vnorm"]) if weighted else None
+    hn = dev_f32(d["hnorm"]) if weighted else None
+    t = kvs.future_mass(Q, K, L, scale=d["scale"], window=window, vnorm=vn, hnorm=hn)
+    torch.cuda.synchronize()
+    ref_L = oracle.lse(d["Q"], d["Kctx"], None, d["scale"], "causal", 0)
+    check_lse(host(L), ref_L, name)
+    ref = oracle.future_mass(d["Q"], d["Kctx"], ref_L, d["scale"], window, recipe.Hkv,
+                             vnorm=d.get("vnorm") if weighted else None, hnorm=d.get("hnorm") if weighted else None)
+    check_scores(host(t), ref, name)
+    if window >= recipe.n_ctx:
+        assert np.all(host(t) == 0)
+
+
+def test_future_mass_conserves_mass_at_window_zero():
+    r = synth.Recipe(Hq=8, Hkv=2, D=128, n_ctx=3000, n_q=3000, mask="causal", sinks=4)
+    d = synth.draw(r, 707)
+    Q, K = dev_bf16(d["Q"]), dev_bf16(d["Kctx"])
+    L = kvs.lse(Q, K, None, scale=d["scale"], mask="causal")
+    t = kvs.future_mass(Q, K, L, scale=d["scale"], window=0)
+    tot = host(t).astype(np.float64).sum(axis=1)
+    assert np.allclose(tot, 4 * 3000, rtol=1e-4)
+
+
+# ---------------------------------------------------------------- eviction
+
+def _evict_case(seed, Hkv, n, D, **kw):
+    s = synth.evict_scores(seed, Hkv, n, tie_frac=0.1, zero_frac=0.02)
+    K = synth.normal_bf16(seed, 90, (Hkv, n, D))
+    V = synth.normal_bf16(seed, 91, (Hkv, n, D))
+    return s, K, V
+
+
+EVICT_CASES = [
+    # name, Hkv, n, D, window, k, tau
+    ("topk-multiblock", 3, 5000, 128, 128, 1000, None),
+    ("topk-one-block", 2, 700, 64, 32, 64, None),
+    ("topk-k0", 2, 3000, 128, 16, 0, None),
+    ("topk-keep-all", 2, 3000, 128, 16, 5000, None),
+    ("topk-window-covers", 1, 100, 128, 200, 10, None),
+    ("topk-k-equals-cand-minus-1", 2, 2049, 128, 1, 2047, None),
+    ("topk-no-window", 8, 4096, 128, 0, 1024, None),
+    ("tau", 4, 9000, 128, 128, None, float(np.exp(-6.0))),
+    ("tau-zero", 2, 3000, 64, 8, None, 0.0),
+    ("tau-inf", 2, 3000, 128, 8, None, float("inf")),
+    ("empty", 2, 0, 128, 8, 5, None),
+]
+
+
+@pytest.mark.parametrize("name,Hkv,n,D,window,k,tau", EVICT_CASES, ids=[c[0] for c in EVICT_CASES])
+def test_evict_parity(name, Hkv, n, D, window, k, tau):
+    s, K, V = _evict_case(808, Hkv, n, D)
+    if n > 10:
+        s[0, 3] = np.nan
+        s[-1, 5] = -0.0
+        s[-1, 6] = 0.0
+        s[0, 7] = np.inf
+    say(f"[evict] {name}")
+    kept, offs, Ko, Vo = kvs.evict(dev_f32(s), dev_bf16(K), dev_bf16(V), window=window, k=k, tau=tau)
+    torch.cuda.synchronize()
+    offs = host(offs)
+    ref = oracle.select(s, window, k=k, tau=tau)
+    gk = kept_from_gpu(host(kept), offs)
+    for h in range(Hkv):
+        assert np.array_equal(gk[h], ref[h]), f"{name}: head {h} differs"
+    Kr, Vr, offr = oracle.compact(K, V, ref)
+    assert np.array_equal(offs, offr)
+    total = int(offs[-1])
+    assert np.array_equal(host_bits(Ko)[:total], Kr) and np.array_equal(host_bits(Vo)[:total], Vr)
+
+
+def test_evict_strided_inputs():
+    """Scores with a padded head stride; K/V views with padded token rows."""
+    Hkv, n, D = 2, 3000, 128
+    s, K, V = _evict_case(909, Hkv, n, D)
+    s_pad = np.zeros((Hkv, n + 100), dtype=np.float32)
+    s_pad[:, :n] = s
+    Kp = np.zeros((Hkv, n, D + 64), dtype=np.uint16)
+    Vp = np.zeros((Hkv, n, D + 64), dtype=np.uint16)
+    Kp[:, :, :D], Vp[:, :, :D] = K, V
+    sd = dev_f32(s_pad)[:, :n]
+    Kd, Vd = dev_bf16(Kp)[:, :, :D], dev_bf16(Vp)[:, :, :D]
+    kept, offs, Ko, Vo = kvs.evict(sd, Kd, Vd, window=64, k=500)
+    torch.cuda.synchronize()
+    ref = oracle.select(s, 64, k=500)
+    gk = kept_from_gpu(host(kept), host(offs))
+    for h in range(Hkv):
+        assert np.array_equal(gk[h], ref[h])
+    check_rows(K, V, gk, host_bits(Ko), host_bits(Vo), host(offs), "strided")
+
+
+# ---------------------------------------------------------------- end to end
+
+@pytest.mark.parametrize("wl", [TINY_KVZIP, QWEN25_1P5B_2K], ids=lambda w: w.name)
+def test_workload_end_to_end(wl):
+    r = wl.recipe
+    d = synth.draw(r, wl.seed)
+    say(f"[e2e] {wl.name}")
+    Q, K, Ks, V = dev_bf16(d["Q"]), dev_bf16(d["Kctx"]), dev_bf16(d["Kself"]), dev_bf16(d["V"])
+    L = kvs.lse(Q, K, Ks, scale=d["scale"], mask="repeat", chunk=r.self_chunk)
+    vn = dev_f32(d["vnorm"]) if r.value_norms else None
+    hn = dev_f32(d["hnorm"]) if r.value_norms else None
+    s = kvs.max_scores(Q, K, L, scale=d["scale"], vnorm=vn, hnorm=hn)
+    ref_L = oracle.lse(d["Q"], d["Kctx"], d["Kself"], d["scale"], "repeat", r.self_chunk)
+    check_lse(host(L), ref_L, wl.name)
+    ref_s = oracle.max_scores(d["Q"], d["Kctx"], ref_L, d["scale"], r.Hkv, vnorm=d.get("vnorm"),
+                              hnorm=d.get("hnorm"))
+    check_scores(host(s), ref_s, wl.name)
+    for k in wl.ks():
+        kept, offs, Ko, Vo = kvs.evict(s, K, V, window=wl.window, k=k)
+        torch.cuda.synchronize()
+        gk = kept_from_gpu(host(kept), host(offs))
+        ref_k = oracle.select(ref_s, wl.window, k=k)
+        check_kept(gk, ref_k, ref_s, k=k, window=wl.window, what=f"{wl.name} k={k}")
+        check_rows(d["Kctx"], d["V"], gk, host_bits(Ko), host_bits(Vo), host(offs), wl.name)
+
+
+def test_pipeline_is_deterministic():
+    r = QWEN25_1P5B_2K.recipe
+    d = synth.draw(r, 1)
+    Q, K, Ks, V = dev_bf16(d["Q"]), dev_bf16(d["Kctx"]), dev_bf16(d["Kself"]), dev_bf16(d["V"])
+    vn, hn = dev_f32(d["vnorm"]), dev_f32(d["hnorm"])
+    outs = []
+    for _ in range(2):
+        L = kvs.lse(Q, K, Ks, scale=d["scale"], mask="repeat", chunk=r.self_chunk)
+        s = kvs.max_scores(Q, K, L, scale=d["scale"], vnorm=vn, hnorm=hn)
+        kept, offs, Ko, Vo = kvs.evict(s, K, V, window=128, k=1024)
+        outs.append([x.clone() for x in (L, s, kept, offs, Ko, Vo)])
+    torch.cuda.synchronize()
+    for a, b in zip(*outs):
+        assert torch.equal(a, b)
