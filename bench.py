@@ -1,0 +1,226 @@
+#!/usr/bin/env python3
+"""Throughput of the scoring + eviction path on one MI355X.
+
+Workload: one Qwen3-8B-shaped layer with a 32768-token context (Hq=32,
+Hkv=8, D=128, bf16), KVzip+ scoring of the teacher-forced repeat in 16 chunks
+of 2048 queries, then threshold eviction (tau = e^-6, window 128) with K/V
+compaction. Inputs are seeded synthetic tensors, resident in HBM before the
+timed region.
+
+One step = kvscore_lse (all chunks in one call) + kvscore_max + kv_evict.
+value = context keys scored per second over whole steps (Hkv * n_ctx / step).
+
+Also reported: per-kernel times (HIP events on the launch stream), the score
+pass's TFLOP/s against the bf16 MFMA peak (roofline), the LSE pass's
+TFLOP/s, eviction GB/s against HBM peak, and the CPU oracle timed on a
+bounded sample of the same workload.
+
+    python bench.py [--gpus 1] [--steps 10] [--warmup 3] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+METRIC = "keys scored/sec & score-pass TFLOP/s (MFMA util) at 32k ctx; evict GB/s"
+
+
+def _log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def source_hash(path: str) -> str:
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def stored_traffic(kernel_src: str):
+    """HBM bytes per launch of the score pass from the counter runs kept in
+    profiles/, or None when the kernel source changed since they were taken."""
+    p = os.path.join(ROOT, "profiles", "score_max_qwen3-8b-32k_traffic.json")
+    if not os.path.exists(p):
+        return None
+    with open(p) as f:
+        t = json.load(f)
+    if t.get("source_sha256_16") != source_hash(kernel_src):
+        return None
+    return t.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(d, wl, n_heads_sample=1, n_chunks_sample=2):
+    """The oracle as it stands on a bounded sample: LSE + max score for one KV
+    head's query heads over `n_chunks_sample` repeat chunks against the whole
+    context, then selection + compaction of the full layer; scaled to the
+    whole workload."""
+    import oracle
+
+    try:
+        from threadpoolctl import threadpool_info
+
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count() or 1
+    r = wl.recipe
+    G, C = r.group, r.chunk
+    hs = slice(0, n_heads_sample)
+    gs = slice(0, n_heads_sample * G)
+    qs = slice(0, n_chunks_sample * C)
+    t0 = time.perf_counter()
+    L = oracle.lse(d["Q"][gs, qs], d["Kctx"][hs], d["Kself"][hs, qs], d["scale"], "repeat", C)
+    s = oracle.max_scores(d["Q"][gs, qs], d["Kctx"][hs], L, d["scale"], n_heads_sample,
+                          vnorm=d["vnorm"][hs], hnorm=d["hnorm"][qs])
+    t_score = time.perf_counter() - t0
+    frac = (n_heads_sample / r.Hkv) * (n_chunks_sample * C / r.n_q)
+    import synth
+
+    sc = synth.evict_scores(wl.seed, r.Hkv, r.n_ctx)  # full-layer shape; selection cost is data-light
+    t1 = time.perf_counter()
+    kept = oracle.select(sc, wl.window, tau=wl.tau)
+    oracle.compact(d["Kctx"], d["V"], kept)
+    t_evict = time.perf_counter() - t1
+    t_full = t_score / frac + t_evict
+    return {
+        "value": r.Hkv * r.n_ctx / t_full,
+        "unit": "keys/s",
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": (f"{n_heads_sample} KV head ({n_heads_sample * G} query heads) x {n_chunks_sample} of "
+                   f"{r.n_q // C} repeat chunks against the full {r.n_ctx}-key context: LSE + max score "
+                   f"({t_score:.1f} s, scaled x{1 / frac:.0f}); threshold selection + compaction of a whole "
+                   f"layer's seeded scores ({t_evict:.2f} s)"),
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the scoring path shards by KV head "
+              "with no communication, and multi-GPU runs are not part of this build.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import kv_cache_eviction_lse_amd as kvs
+    from kv_cache_eviction_lse_amd import accounting as acc
+    import synth
+    from synth.workloads import QWEN3_8B_32K as wl
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    kvs.lib()  # fail loudly without the HIP library
+
+    r = wl.recipe
+    _log(f"[bench] drawing {wl.name}")
+    t0 = time.perf_counter()
+    d = synth.draw(r, wl.seed)
+    _log(f"[bench] drawn in {time.perf_counter() - t0:.1f} s")
+
+    def dev_bf16(x):
+        return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).view(torch.bfloat16).cuda()
+
+    Q, K, Ks, V = dev_bf16(d["Q"]), dev_bf16(d["Kctx"]), dev_bf16(d["Kself"]), dev_bf16(d["V"])
+    vn = torch.from_numpy(d["vnorm"]).cuda()
+    hn = torch.from_numpy(d["hnorm"]).cuda()
+    scale = d["scale"]
+    L = torch.empty((r.Hq, r.n_q), dtype=torch.float32, device="cuda")
+    S = torch.empty((r.Hkv, r.n_ctx), dtype=torch.float32, device="cuda")
+    e = kvs.evict_desc(S, K, window=wl.window, tau=wl.tau)
+    cap = e.capacity
+    outs = (torch.empty(cap, dtype=torch.int32, device="cuda"),
+            torch.empty(r.Hkv + 1, dtype=torch.int64, device="cuda"),
+            torch.empty((cap, r.D), dtype=torch.bfloat16, device="cuda"),
+            torch.empty((cap, r.D), dtype=torch.bfloat16, device="cuda"))
+    ws = torch.empty(max(kvs.evict_workspace_bytes(e), 256), dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def step(ev=None):
+        if ev:
+            ev[0].record(stream)
+        kvs.lse(Q, K, Ks, scale=scale, mask="repeat", chunk=r.chunk, out=L)
+        if ev:
+            ev[1].record(stream)
+        kvs.max_scores(Q, K, L, scale=scale, vnorm=vn, hnorm=hn, out=S)
+        if ev:
+            ev[2].record(stream)
+        kvs.evict(S, K, V, window=wl.window, tau=wl.tau, workspace=ws, outputs=outs)
+        if ev:
+            ev[3].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_start
+    ms_per_step = wall * 1e3 / args.steps
+    t_lse = float(np.mean([a[0].elapsed_time(a[1]) for a in evs]))
+    t_score = float(np.mean([a[1].elapsed_time(a[2]) for a in evs]))
+    t_evict = float(np.mean([a[2].elapsed_time(a[3]) for a in evs]))
+
+    offs = outs[1].cpu().numpy()
+    kept = np.diff(offs)
+    kept_total = int(offs[-1])
+    score_flops = acc.flops(acc.max_pairs(r.Hq, r.n_ctx, r.n_q), r.D)
+    lse_flops = acc.flops(acc.lse_pairs(r.Hq, r.n_ctx, r.n_q, "repeat", r.chunk), r.D)
+    ev_bytes = acc.evict_bytes(r.Hkv, r.n_ctx, kept_total, r.D)
+    score_tflops = score_flops / (t_score * 1e-3) / 1e12
+    lse_tflops = lse_flops / (t_lse * 1e-3) / 1e12
+    evict_gbs = ev_bytes / (t_evict * 1e-3) / 1e9
+    keys_per_s = r.Hkv * r.n_ctx / (ms_per_step * 1e-3)
+
+    traffic = stored_traffic(os.path.join(ROOT, "kv_cache_eviction_lse_amd", "csrc", "score.hip"))
+    out = {
+        "metric": METRIC,
+        "value": keys_per_s,
+        "unit": "keys/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "Hq": r.Hq, "Hkv": r.Hkv, "head_dim": r.D, "n_ctx": r.n_ctx,
+                   "n_q": r.n_q, "chunk": r.chunk, "tau": wl.tau, "window": wl.window,
+                   "parallelism": "single GPU"},
+        "roofline": {"bound": "mfma", "achieved": score_tflops, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": score_tflops / PEAK_BF16_TFLOPS, "traffic": traffic,
+                     "kernel": "score pass (kvscore_max)"},
+        "kernels_ms": {"lse": t_lse, "score_max": t_score, "evict": t_evict},
+        "lse_pass": {"tflops": lse_tflops, "frac_of_bf16_peak": lse_tflops / PEAK_BF16_TFLOPS},
+        "score_pass": {"tflops": score_tflops, "flops": score_flops},
+        "evict": {"gbs": evict_gbs, "frac_of_hbm_peak": evict_gbs / PEAK_HBM_GBS, "bytes": ev_bytes,
+                  "kept_per_head": kept.tolist(),
+                  "compression_per_head": [round(acc.compression_ratio(int(x), r.n_ctx), 4) for x in kept]},
+    }
+    if not args.no_cpu_baseline:
+        _log("[bench] timing the CPU oracle on a sample")
+        out["cpu_baseline"] = cpu_baseline(d, wl)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

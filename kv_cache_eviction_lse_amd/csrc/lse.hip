@@ -151,11 +151,16 @@ __global__ __launch_bounds__(LSE_WAVES * WAVE) void lse_kernel(LseParams p) {
     }
   };
 
+  // Running state per subtile column: raw max m, the exp2-domain offset
+  // o = fl(m * c2) that every term of l was computed against, and l. Rescaling
+  // uses exp2(o_old - o_new) on the stored offsets, which is exactly 1 while
+  // the max is unchanged (so rounding of m * c2 cannot drift l tile by tile).
   const float c2 = p.scale * LOG2E;
-  float m_run[LSE_NQ], l_run[LSE_NQ];
+  float m_run[LSE_NQ], o_run[LSE_NQ], l_run[LSE_NQ];
 #pragma unroll
   for (int q = 0; q < LSE_NQ; ++q) {
     m_run[q] = -INFINITY;
+    o_run[q] = 0.f;
     l_run[q] = 0.f;
   }
 
@@ -215,12 +220,14 @@ __global__ __launch_bounds__(LSE_WAVES * WAVE) void lse_kernel(LseParams p) {
 #pragma unroll
       for (int r = 1; r < 16; r += 2) tm = max3(tm, acc[r], (r + 1 < 16) ? acc[r + 1] : acc[r]);
       const float m_new = fmaxf(m_run[q], tm);
-      const float mcs = (m_new == -INFINITY) ? 0.f : m_new * c2;
+      const float o_new = (m_new == -INFINITY) ? 0.f : m_new * c2;
       float sum = 0.f;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) sum += fast_exp2(__builtin_fmaf(acc[r], c2, -mcs));
-      l_run[q] = l_run[q] * fast_exp2(__builtin_fmaf(m_run[q], c2, -mcs)) + sum;
+      for (int r = 0; r < 16; ++r) sum += fast_exp2(__builtin_fmaf(acc[r], c2, -o_new));
+      const float alpha = (m_run[q] == -INFINITY) ? 0.f : fast_exp2(o_run[q] - o_new);
+      l_run[q] = l_run[q] * alpha + sum;
       m_run[q] = m_new;
+      o_run[q] = o_new;
     }
 
     if (tt + 1 < n_tiles) store_tile(cur ^ 1);
@@ -230,12 +237,13 @@ __global__ __launch_bounds__(LSE_WAVES * WAVE) void lse_kernel(LseParams p) {
   // ---- merge half-waves, write natural-log LSE
 #pragma unroll
   for (int q = 0; q < LSE_NQ; ++q) {
-    const float m_o = __shfl_xor(m_run[q], 32);
+    const float o_o = __shfl_xor(o_run[q], 32);
     const float l_o = __shfl_xor(l_run[q], 32);
-    const float M = fmaxf(m_run[q], m_o);
-    const float Mc = (M == -INFINITY) ? 0.f : M * c2;
-    const float L = l_run[q] * fast_exp2(__builtin_fmaf(m_run[q], c2, -Mc)) +
-                    l_o * fast_exp2(__builtin_fmaf(m_o, c2, -Mc));
+    const float m_o = __shfl_xor(m_run[q], 32);
+    // the larger offset belongs to the larger max (rounding is monotone)
+    const float Mc = (m_run[q] == -INFINITY) ? o_o : ((m_o == -INFINITY) ? o_run[q] : fmaxf(o_run[q], o_o));
+    const float L = (l_run[q] > 0.f ? l_run[q] * fast_exp2(o_run[q] - Mc) : 0.f) +
+                    (l_o > 0.f ? l_o * fast_exp2(o_o - Mc) : 0.f);
     const int64_t j = sub_pos[q] + col;
     if (half == 0 && sub_ok[q] && j < p.n_q) p.lse[(int64_t)sub_g[q] * p.n_q + j] = (Mc + __log2f(L)) * LN2;
   }

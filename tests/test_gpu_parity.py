@@ -58,6 +58,18 @@ def test_lse_parity(name, kw, mask, chunk):
     check_lse(g, ref, name)
 
 
+def test_lse_long_context_does_not_drift():
+    """~3000 key tiles per query: the running sum must not pick up a per-tile
+    rescaling error (the error stays far below the 1e-3 parity bar)."""
+    r = synth.Recipe(Hq=4, Hkv=1, D=128, n_ctx=100000, n_q=64, chunk=64, lowrank_rank=8, lowrank_scale=2.0)
+    d = synth.draw(r, 111)
+    say("[lse] long-context drift")
+    g = _gpu_lse(d, "repeat", 64)
+    ref = oracle.lse(d["Q"], d["Kctx"], d["Kself"], d["scale"], "repeat", 64)
+    err = check_lse(g, ref, "long-context")
+    assert err <= 1e-4, f"LSE error {err:.2e} grows with context length"
+
+
 MAX_CASES = [
     ("tiny-kvzip", TINY_KVZIP.recipe, False),
     ("g5-ragged-weighted", synth.Recipe(Hq=10, Hkv=2, D=128, n_ctx=1000, n_q=700, chunk=300, lowrank_rank=8,
