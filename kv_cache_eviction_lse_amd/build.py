@@ -24,8 +24,18 @@ COMMON = [
 ]
 
 
+# Per-file flags. The scoring kernels never see NaN in their reductions (the
+# inputs are finite bf16 values and finite normalisers), so NaN-propagating
+# max/min semantics are not needed there: without them the compiler drops the
+# IEEE canonicalising moves before every v_max and can form v_max3_f32.
+FILE_FLAGS = {
+    "lse.hip": ["-fno-honor-nans"],
+    "score.hip": ["-fno-honor-nans"],
+}
+
+
 def _compile(src: str, obj: str, extra: list[str], verbose: bool) -> None:
-    cmd = [HIPCC, *COMMON, *extra, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC, *COMMON, *FILE_FLAGS.get(src, []), *extra, "-c", os.path.join(CSRC, src), "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)

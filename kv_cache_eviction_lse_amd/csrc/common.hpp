@@ -30,6 +30,10 @@ __device__ __forceinline__ void st16(void* p, const u32x4& v) { *reinterpret_cas
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Make a loaded value opaque to the optimiser: it then stays in registers
+// instead of being re-loaded (rematerialised) where it is used in a loop.
+__device__ __forceinline__ void pin(u32x4& v) { asm volatile("" : "+v"(v)); }
+
 __device__ __forceinline__ float max3(float a, float b, float c) { return fmaxf(a, fmaxf(b, c)); }
 
 constexpr float LOG2E = 1.4426950408889634f;

@@ -58,7 +58,8 @@ template <int D, bool CAUSAL>
 __global__ __launch_bounds__(LSE_WAVES * WAVE) void lse_kernel(LseParams p) {
   using T = KTile<D>;
   constexpr int NTHREADS = LSE_WAVES * WAVE;
-  constexpr int CPT = (T::CHUNKS + NTHREADS - 1) / NTHREADS;
+  static_assert(T::CHUNKS % NTHREADS == 0, "tile chunks must split evenly over the threads");
+  constexpr int CPT = T::CHUNKS / NTHREADS;
   constexpr int CHUNKS_PER_ROW = D / 8;
 
   __shared__ __attribute__((aligned(16))) char s_k[2][T::BYTES];
@@ -98,12 +99,13 @@ __global__ __launch_bounds__(LSE_WAVES * WAVE) void lse_kernel(LseParams p) {
     sub_ok[q] = u < p.n_sub;
     sub_g[q] = h * p.G + (sub_ok[q] ? u % p.G : 0);
     sub_pos[q] = sub_ok[q] ? (int64_t)(u / p.G) * 32 : 0;
-    const int64_t j = sub_pos[q] + col;
-    const bool ok = sub_ok[q] && j < p.n_q;
-    const uint16_t* qp = p.Q + (int64_t)sub_g[q] * p.q_hs + (ok ? j : 0) * p.q_ts + half * (D / 2);
+    // queries past the end load the last row; their results are never written
+    const int64_t j = min(sub_pos[q] + col, p.n_q - 1);
+    const uint16_t* qp = p.Q + (int64_t)sub_g[q] * p.q_hs + j * p.q_ts + half * (D / 2);
 #pragma unroll
     for (int s = 0; s < T::STEPS; ++s) {
-      u32x4 v = ok ? ld16(qp + 8 * s) : u32x4{0, 0, 0, 0};
+      u32x4 v = ld16(qp + 8 * s);
+      pin(v);
       qreg[q][s] = as_bf16x8(v);
     }
   }
@@ -124,6 +126,9 @@ __global__ __launch_bounds__(LSE_WAVES * WAVE) void lse_kernel(LseParams p) {
     }
   };
 
+  // Key tiles: rows past the end of a segment load its last key; every such
+  // row is masked (ctx: key >= n_ctx; self/causal: key > j), so its value never
+  // counts. Loads are unconditional so issuing a prefetch never stalls.
   u32x4 pre[CPT];
   auto load_tile = [&](int64_t tt) {
     const uint16_t* base;
@@ -132,22 +137,17 @@ __global__ __launch_bounds__(LSE_WAVES * WAVE) void lse_kernel(LseParams p) {
 #pragma unroll
     for (int c = 0; c < CPT; ++c) {
       const int idx = tid + c * NTHREADS;
-      pre[c] = u32x4{0, 0, 0, 0};
-      if (idx < T::CHUNKS) {
-        const int rr = idx / CHUNKS_PER_ROW, part = idx % CHUNKS_PER_ROW;
-        const int64_t key = k0 + rr;
-        if (key < kend) pre[c] = ld16(base + key * ts + part * 8);
-      }
+      const int rr = idx / CHUNKS_PER_ROW, part = idx % CHUNKS_PER_ROW;
+      const int64_t key = min(k0 + rr, kend - 1);
+      pre[c] = ld16(base + key * ts + part * 8);
     }
   };
   auto store_tile = [&](int buf) {
 #pragma unroll
     for (int c = 0; c < CPT; ++c) {
       const int idx = tid + c * NTHREADS;
-      if (idx < T::CHUNKS) {
-        const int rr = idx / CHUNKS_PER_ROW, part = idx % CHUNKS_PER_ROW;
-        *reinterpret_cast<u32x4*>(&s_k[buf][rr * T::LDS_STRIDE + part * 16]) = pre[c];
-      }
+      const int rr = idx / CHUNKS_PER_ROW, part = idx % CHUNKS_PER_ROW;
+      *reinterpret_cast<u32x4*>(&s_k[buf][rr * T::LDS_STRIDE + part * 16]) = pre[c];
     }
   };
 

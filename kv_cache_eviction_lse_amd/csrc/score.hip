@@ -9,10 +9,10 @@
 //   t_i = vnorm_i * sum_{g} sum_{j >= i + w} exp(scale*q_j^g.k_i - lse_j^g - ln hnorm_j).
 //
 // Layout of the work:
-//   * a workgroup owns BK = NWAVES * NT * 32 consecutive keys of one KV head;
+//   * a workgroup owns BK = NW * NT * 32 consecutive keys of one KV head;
 //     each wave keeps its NT*32 keys in VGPRs as MFMA B operands for the whole
 //     kernel (the key tile never leaves the chip);
-//   * the group's query rows stream past in tiles of 32 through a
+//   * the group's query rows stream past in tiles of TR rows through a
 //     double-buffered LDS stage, shared by all waves of the workgroup;
 //   * S = Q_tile * K^T on v_mfma_f32_32x32x16_bf16 with queries as rows, so a
 //     lane holds one key column and 16 query rows: the reduction over queries
@@ -24,6 +24,8 @@
 //   * the head dimension is read in a permuted order (lane half h takes
 //     elements [h*D/2, h*D/2 + D/2) in steps of 8) on both operands; a dot
 //     product does not depend on the order of its terms.
+#include <cmath>
+
 #include "common.hpp"
 #include "internal.hpp"
 
@@ -48,25 +50,28 @@ struct ScoreParams {
   float scale;
 };
 
-template <int D>
-struct Tile {
-  static constexpr int STEPS = D / 16;           // k-steps of 16 per MFMA chain
-  static constexpr int ROW_BYTES = D * 2;
-  static constexpr int LDS_STRIDE = ROW_BYTES + 16;  // pad: 16 rows hit distinct banks
-  static constexpr int CHUNKS = 32 * D / 8;      // 16-byte pieces per 32-row tile
-  static constexpr int BYTES = 32 * LDS_STRIDE;
+template <int D, int TR>
+struct QTile {
+  static constexpr int STEPS = D / 16;               // k-steps of 16 per MFMA chain
+  static constexpr int LDS_STRIDE = D * 2 + 16;      // pad: 16 consecutive rows hit distinct banks
+  static constexpr int CHUNKS = TR * D / 8;          // 16-byte pieces per tile
+  static constexpr int CHUNKS_PER_ROW = D / 8;
+  static constexpr int BYTES = TR * LDS_STRIDE;
 };
 
-template <int D, int NWAVES, int NT, bool SUM>
-__global__ __launch_bounds__(NWAVES * WAVE) void score_kernel(ScoreParams p) {
-  using T = Tile<D>;
-  constexpr int NTHREADS = NWAVES * WAVE;
-  constexpr int BK = NWAVES * NT * 32;
-  constexpr int CPT = (T::CHUNKS + NTHREADS - 1) / NTHREADS;  // 16-B chunks per thread per tile
-  constexpr int CHUNKS_PER_ROW = D / 8;
+// NW waves per workgroup, NT key subtiles (of 32) per wave, RT row subtiles
+// (of 32) per streamed query tile.
+template <int D, int NW, int NT, int RT, bool SUM>
+__global__ __launch_bounds__(NW * WAVE) void score_kernel(ScoreParams p) {
+  constexpr int TR = RT * 32;
+  using T = QTile<D, TR>;
+  constexpr int NTHREADS = NW * WAVE;
+  constexpr int BK = NW * NT * 32;
+  static_assert(T::CHUNKS % NTHREADS == 0, "tile chunks must split evenly over the threads");
+  constexpr int CPT = T::CHUNKS / NTHREADS;
 
   __shared__ __attribute__((aligned(16))) char s_q[2][T::BYTES];
-  __shared__ __attribute__((aligned(16))) float s_bias[2][32];
+  __shared__ __attribute__((aligned(16))) float s_bias[2][TR];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -79,6 +84,7 @@ __global__ __launch_bounds__(NWAVES * WAVE) void score_kernel(ScoreParams p) {
   const int rest = b / p.Hkv;
   const float inv_scale = 1.0f / p.scale;
   const float c2 = p.scale * LOG2E;
+  const int n_q = (int)p.n_q;
 
   // work items: max mode -> one key block and one query split;
   // sum mode -> a pair of key blocks (kb, n_kblocks-1-kb), balancing the triangle.
@@ -99,164 +105,168 @@ __global__ __launch_bounds__(NWAVES * WAVE) void score_kernel(ScoreParams p) {
     const int64_t key0 = (int64_t)kb * BK;
     const int64_t wave_key0 = key0 + (int64_t)wave * NT * 32;
 
-    // ---- resident keys: B operands (col = key, k-range per half, permuted D)
+    // ---- resident keys: B operands (col = key, k-range per half, permuted D).
+    // Keys past the end load the last key instead; their results are never written.
     bf16x8 kreg[NT][T::STEPS];
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
-      const int64_t key = wave_key0 + 32 * t + col;
-      const bool ok = key < p.n_keys;
-      const uint16_t* kp = p.K + (int64_t)h * p.k_hs + (ok ? key : 0) * p.k_ts + half * (D / 2);
+      int64_t key = wave_key0 + 32 * t + col;
+      key = key < p.n_keys ? key : p.n_keys - 1;
+      const uint16_t* kp = p.K + (int64_t)h * p.k_hs + key * p.k_ts + half * (D / 2);
 #pragma unroll
       for (int s = 0; s < T::STEPS; ++s) {
-        u32x4 v = ok ? ld16(kp + 8 * s) : u32x4{0, 0, 0, 0};
+        u32x4 v = ld16(kp + 8 * s);
+        pin(v);
         kreg[t][s] = as_bf16x8(v);
       }
     }
 
-    // ---- the row space this item visits, in tiles of 32 rows
-    // max: rows r in [0, G*n_q): g = r / n_q, j = r % n_q; split s takes an even share.
-    // sum: per group head, j-tiles aligned to 32 from the first row any key of the
-    //      block can count (j >= key0 + window) to T.
-    int64_t t_begin, t_end, jt_first = 0, tiles_per_g = 0;
+    // ---- the query tiles this item visits: (group head gl, row tile jt),
+    // head-major. Rows of tile jt are jt*TR .. jt*TR+TR-1 of that head.
+    //   max: every row tile of every group head, split s takes an even share;
+    //   sum: per group head, the row tiles from the first row any key of the
+    //        block can count (j >= key0 + window) to the end.
+    const int n_jt_all = (n_q + TR - 1) / TR;
+    int jt_start = 0, jt_end = n_jt_all;
+    int t_count, gl, jt;
     if (SUM) {
       const int64_t j_lo = key0 + p.window;
-      if (j_lo >= p.n_q) {
-        tiles_per_g = 0;
-      } else {
-        jt_first = j_lo / 32;
-        tiles_per_g = (p.n_q + 31) / 32 - jt_first;
-      }
-      t_begin = 0;
-      t_end = tiles_per_g * p.G;
+      jt_start = j_lo < p.n_q ? (int)(j_lo / TR) : n_jt_all;
+      t_count = (jt_end - jt_start) * p.G;
+      gl = 0;
+      jt = jt_start;
     } else {
-      const int64_t n_tiles = ((int64_t)p.G * p.n_q + 31) / 32;
-      t_begin = n_tiles * split / p.nsplit;
-      t_end = n_tiles * (split + 1) / p.nsplit;
+      const int total = n_jt_all * p.G;
+      const int t0 = (int)((int64_t)total * split / p.nsplit);
+      const int t1 = (int)((int64_t)total * (split + 1) / p.nsplit);
+      t_count = t1 - t0;
+      gl = n_jt_all ? t0 / n_jt_all : 0;
+      jt = n_jt_all ? t0 - gl * n_jt_all : 0;
     }
 
-    // row rr of tile t -> (query head g, query j); valid = j inside the sequence
-    auto row_of = [&](int64_t t, int rr, int& g, int64_t& j) -> bool {
-      if (SUM) {
-        const int64_t gl = t / tiles_per_g;
-        j = (jt_first + t % tiles_per_g) * 32 + rr;
-        g = h * p.G + (int)gl;
-        return j < p.n_q;
-      } else {
-        const int64_t r = t * 32 + rr;
-        const int64_t gl = r / p.n_q;
-        j = r - gl * p.n_q;
-        g = h * p.G + (int)gl;
-        return gl < p.G;
-      }
-    };
-
+    // Prefetch registers: raw Q pieces, and for the first TR threads the raw
+    // lse and hnorm of one row. Loads are unconditional (rows past the end
+    // read the last row) and the bias arithmetic waits until the store, so
+    // issuing a prefetch never stalls the wave. Rows past the end get bias
+    // -inf: they never win a max and add exp2(-inf) = 0 to a sum.
     u32x4 pre[CPT];
-    float pre_bias = 0.f;
-    auto load_tile = [&](int64_t t) {
+    float pre_lse = 0.f, pre_hn = 1.f;
+    bool pre_ok = false;
+    auto load_tile = [&](int tgl, int tjt) {
+      const int g = h * p.G + tgl;
+      const uint16_t* qbase = p.Q + (int64_t)g * p.q_hs;
 #pragma unroll
       for (int c = 0; c < CPT; ++c) {
         const int idx = tid + c * NTHREADS;
-        pre[c] = u32x4{0, 0, 0, 0};
-        if (idx < T::CHUNKS) {
-          const int rr = idx / CHUNKS_PER_ROW, part = idx % CHUNKS_PER_ROW;
-          int g;
-          int64_t j;
-          if (row_of(t, rr, g, j))
-            pre[c] = ld16(p.Q + (int64_t)g * p.q_hs + j * p.q_ts + part * 8);
-        }
+        const int rr = idx / T::CHUNKS_PER_ROW, part = idx % T::CHUNKS_PER_ROW;
+        const int j = min(tjt * TR + rr, n_q - 1);
+        pre[c] = ld16(qbase + (int64_t)j * p.q_ts + part * 8);
       }
-      if (tid < 32) {
-        int g;
-        int64_t j;
-        if (row_of(t, tid, g, j)) {
-          const float hn = p.hnorm ? p.hnorm[j] : 1.0f;
-          pre_bias = -(p.lse[(int64_t)g * p.n_q + j] + __logf(hn)) * inv_scale;
-        } else {
-          pre_bias = -INFINITY;
-        }
+      if (tid < TR) {
+        const int j = tjt * TR + tid;
+        pre_ok = j < n_q;
+        const int jc = min(j, n_q - 1);
+        pre_lse = p.lse[(int64_t)g * p.n_q + jc];
+        pre_hn = p.hnorm ? p.hnorm[jc] : 1.0f;
       }
     };
     auto store_tile = [&](int buf) {
 #pragma unroll
       for (int c = 0; c < CPT; ++c) {
         const int idx = tid + c * NTHREADS;
-        if (idx < T::CHUNKS) {
-          const int rr = idx / CHUNKS_PER_ROW, part = idx % CHUNKS_PER_ROW;
-          *reinterpret_cast<u32x4*>(&s_q[buf][rr * T::LDS_STRIDE + part * 16]) = pre[c];
-        }
+        const int rr = idx / T::CHUNKS_PER_ROW, part = idx % T::CHUNKS_PER_ROW;
+        *reinterpret_cast<u32x4*>(&s_q[buf][rr * T::LDS_STRIDE + part * 16]) = pre[c];
       }
-      if (tid < 32) s_bias[buf][tid] = pre_bias;
+      if (tid < TR) s_bias[buf][tid] = pre_ok ? -(pre_lse + __logf(pre_hn)) * inv_scale : -INFINITY;
+    };
+    auto advance = [&](int& tgl, int& tjt) {
+      if (++tjt == jt_end) {
+        tjt = jt_start;
+        ++tgl;
+      }
     };
 
     float red[NT];  // max: running max of the shifted logit / scale; sum: running sum
 #pragma unroll
     for (int t = 0; t < NT; ++t) red[t] = SUM ? 0.f : -INFINITY;
 
-    if (t_begin < t_end) {
-      load_tile(t_begin);
+    if (t_count > 0) {
+      load_tile(gl, jt);
       store_tile(0);
     }
     __syncthreads();
 
-    for (int64_t t = t_begin; t < t_end; ++t) {
-      const int cur = (int)((t - t_begin) & 1);
-      if (t + 1 < t_end) load_tile(t + 1);
+    for (int t = 0; t < t_count; ++t) {
+      const int cur = t & 1;
+      const int cur_jt = jt;
+      int ngl = gl, njt = jt;
+      advance(ngl, njt);
+      if (t + 1 < t_count) load_tile(ngl, njt);
 
-      // A operands (query rows) and the bias column for this lane's 16 rows
-      bf16x8 a[T::STEPS];
-      const char* qrow = &s_q[cur][col * T::LDS_STRIDE + half * (D / 2) * 2];
 #pragma unroll
-      for (int s = 0; s < T::STEPS; ++s) a[s] = as_bf16x8(*reinterpret_cast<const u32x4*>(qrow + 16 * s));
-      f32x16 bias;
+      for (int rs = 0; rs < RT; ++rs) {
+        // keep each row subtile's operands to itself (bounds register pressure)
+        if (rs) __builtin_amdgcn_sched_barrier(0);
+        // A operands (query rows rs*32 + col) and the bias of this lane's 16 rows
+        bf16x8 a[T::STEPS];
+        const char* qrow = &s_q[cur][(rs * 32 + col) * T::LDS_STRIDE + half * D];
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const float4 v = *reinterpret_cast<const float4*>(&s_bias[cur][8 * q + 4 * half]);
-        bias[4 * q + 0] = v.x;
-        bias[4 * q + 1] = v.y;
-        bias[4 * q + 2] = v.z;
-        bias[4 * q + 3] = v.w;
-      }
+        for (int s = 0; s < T::STEPS; ++s) a[s] = as_bf16x8(*reinterpret_cast<const u32x4*>(qrow + 16 * s));
+        f32x16 bias;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const float4 v = *reinterpret_cast<const float4*>(&s_bias[cur][rs * 32 + 8 * q + 4 * half]);
+          bias[4 * q + 0] = v.x;
+          bias[4 * q + 1] = v.y;
+          bias[4 * q + 2] = v.z;
+          bias[4 * q + 3] = v.w;
+        }
 
-      if (SUM) {
-        // rows j = jt + acc_row(r, half); this wave's keys i = wave_key0 + 32*t + col
-        const int64_t jt = (jt_first + t % tiles_per_g) * 32;
+        if (SUM) {
+          // rows j = jt0 + acc_row(r, half); this wave's keys i = wave_key0 + 32*st + col
+          const int64_t jt0 = (int64_t)cur_jt * TR + 32 * rs;
 #pragma unroll
-        for (int st = 0; st < NT; ++st) {
-          const int64_t ib = wave_key0 + 32 * st;
-          if (jt + 31 < ib + p.window) continue;  // every pair still inside the window
-          f32x16 acc = bias;
+          for (int st = 0; st < NT; ++st) {
+            const int64_t ib = wave_key0 + 32 * st;
+            if (jt0 + 31 < ib + p.window) continue;  // every pair still inside the window
+            f32x16 acc = bias;
 #pragma unroll
-          for (int s = 0; s < T::STEPS; ++s) acc = mfma32(a[s], kreg[st][s], acc);
-          float sum = 0.f;
-          if (jt >= ib + 31 + p.window) {
+            for (int s = 0; s < T::STEPS; ++s) acc = mfma32(a[s], kreg[st][s], acc);
+            float sum = 0.f;
+            if (jt0 >= ib + 31 + p.window) {
 #pragma unroll
-            for (int r = 0; r < 16; ++r) sum += fast_exp2(acc[r] * c2);
-          } else {
-            // diagonal band: keep pairs with j - i >= window
-            const int64_t base = jt - ib - p.window - col + 4 * half;
+              for (int r = 0; r < 16; ++r) sum += fast_exp2(acc[r] * c2);
+            } else {
+              // diagonal band: keep pairs with j - i >= window
+              const int base = (int)(jt0 - ib - p.window) - col + 4 * half;
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-              const float e = fast_exp2(acc[r] * c2);
-              sum += (base + 8 * (r >> 2) + (r & 3) >= 0) ? e : 0.f;
+              for (int r = 0; r < 16; ++r) {
+                const float e = fast_exp2(acc[r] * c2);
+                sum += (base + 8 * (r >> 2) + (r & 3) >= 0) ? e : 0.f;
+              }
             }
+            red[st] += sum;
           }
-          red[st] += sum;
-        }
-      } else {
+        } else {
 #pragma unroll
-        for (int st = 0; st < NT; ++st) {
-          f32x16 acc = bias;
+          for (int st = 0; st < NT; ++st) {
+            // two accumulator chains in flight at a time
+            if (st && (st & 1) == 0) __builtin_amdgcn_sched_barrier(0);
+            f32x16 acc = bias;
 #pragma unroll
-          for (int s = 0; s < T::STEPS; ++s) acc = mfma32(a[s], kreg[st][s], acc);
-          float m = red[st];
+            for (int s = 0; s < T::STEPS; ++s) acc = mfma32(a[s], kreg[st][s], acc);
+            float m = red[st];
 #pragma unroll
-          for (int r = 0; r < 16; r += 2) m = max3(m, acc[r], acc[r + 1]);
-          red[st] = m;
+            for (int r = 0; r < 16; r += 2) m = max3(m, acc[r], acc[r + 1]);
+            red[st] = m;
+          }
         }
       }
 
-      if (t + 1 < t_end) store_tile(cur ^ 1);
+      if (t + 1 < t_count) store_tile(cur ^ 1);
       __syncthreads();
+      gl = ngl;
+      jt = njt;
     }
 
     // ---- combine the two half-waves and write one value per key
@@ -289,13 +299,38 @@ __global__ void fill_zero(float* p, int64_t n) {
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride) p[i] = 0.f;
 }
 
-constexpr int MAX_WAVES = 8, MAX_NT = 2;
-constexpr int SUM_WAVES = 8, SUM_NT = 2;
+// max mode: 8 waves x 2 key subtiles = 512 keys per workgroup, 64-row query tiles
+constexpr int MAX_NW = 8, MAX_NT = 2, MAX_RT = 2;
+// sum mode: 8 waves x 2 key subtiles = 512 keys per workgroup, 64-row query tiles
+constexpr int SUM_NW = 8, SUM_NT = 2, SUM_RT = 2;
 
-template <int D, int NWAVES, int NT, bool SUM>
+template <int D, int NW, int NT, int RT, bool SUM>
 hipError_t run(const ScoreParams& p, int nblocks, hipStream_t s) {
-  hipLaunchKernelGGL((score_kernel<D, NWAVES, NT, SUM>), dim3(nblocks), dim3(NWAVES * WAVE), 0, s, p);
+  hipLaunchKernelGGL((score_kernel<D, NW, NT, RT, SUM>), dim3(nblocks), dim3(NW * WAVE), 0, s, p);
   return hipGetLastError();
+}
+
+// Query-row splits per key block: enough workgroups to fill every CU twice
+// when there are few key blocks; otherwise the split (1..4) whose last round
+// of workgroups is fullest.
+int choose_splits(int64_t base, int64_t n_tiles, int num_cus) {
+  const int64_t max_split = n_tiles / 2 > 1 ? n_tiles / 2 : 1;
+  if (base < num_cus) {
+    int64_t ns = (2 * (int64_t)num_cus + base - 1) / base;
+    return (int)(ns < max_split ? ns : max_split);
+  }
+  int best = 1;
+  double best_eff = 0.0;
+  for (int ns = 1; ns <= 4 && ns <= max_split; ++ns) {
+    const double blocks = (double)base * ns;
+    const double rounds = std::ceil(blocks / num_cus);
+    const double eff = blocks / (rounds * num_cus);
+    if (eff > best_eff + 0.02) {
+      best_eff = eff;
+      best = ns;
+    }
+  }
+  return best;
 }
 
 }  // namespace
@@ -310,16 +345,13 @@ hipError_t launch_score_max(const kvs_attn_desc& d, const uint16_t* Q, const uin
   p.q_hs = d.q_head_stride; p.q_ts = d.q_tok_stride; p.k_hs = d.k_head_stride; p.k_ts = d.k_tok_stride;
   p.n_keys = n_keys; p.n_q = d.n_q; p.window = 0;
   p.Hkv = d.n_kvheads; p.G = d.n_qheads / d.n_kvheads; p.scale = d.scale;
-  constexpr int BK = MAX_WAVES * MAX_NT * 32;
+  constexpr int BK = MAX_NW * MAX_NT * 32;
+  constexpr int TR = MAX_RT * 32;
   p.n_kblocks = (int)((n_keys + BK - 1) / BK);
   const int64_t base = (int64_t)p.n_kblocks * p.Hkv;
-  const int64_t n_tiles = ((int64_t)p.G * d.n_q + 31) / 32;
-  // enough workgroups to cover every CU twice; never split below 4 row tiles
-  int64_t nsplit = (2 * (int64_t)num_cus + base - 1) / base;
-  nsplit = nsplit < 1 ? 1 : nsplit;
-  const int64_t max_split = n_tiles / 4 > 1 ? n_tiles / 4 : 1;
-  nsplit = nsplit > max_split ? max_split : nsplit;
-  p.nsplit = (int)nsplit;
+  const int64_t n_tiles = (int64_t)p.G * ((d.n_q + TR - 1) / TR);
+  const int nsplit = choose_splits(base, n_tiles, num_cus);
+  p.nsplit = nsplit;
   p.use_atomic = (accumulate || nsplit > 1) ? 1 : 0;
   if (!accumulate && nsplit > 1) {
     const int64_t n = (int64_t)p.Hkv * n_keys;
@@ -329,8 +361,8 @@ hipError_t launch_score_max(const kvs_attn_desc& d, const uint16_t* Q, const uin
     if (e != hipSuccess) return e;
   }
   const int nblocks = (int)(base * nsplit);
-  if (d.head_dim == 128) return run<128, MAX_WAVES, MAX_NT, false>(p, nblocks, s);
-  return run<64, MAX_WAVES, MAX_NT, false>(p, nblocks, s);
+  if (d.head_dim == 128) return run<128, MAX_NW, MAX_NT, MAX_RT, false>(p, nblocks, s);
+  return run<64, MAX_NW, MAX_NT, MAX_RT, false>(p, nblocks, s);
 }
 
 hipError_t launch_score_sum(const kvs_attn_desc& d, const uint16_t* Q, const uint16_t* K, const float* lse,
@@ -343,14 +375,14 @@ hipError_t launch_score_sum(const kvs_attn_desc& d, const uint16_t* Q, const uin
   p.q_hs = d.q_head_stride; p.q_ts = d.q_tok_stride; p.k_hs = d.k_head_stride; p.k_ts = d.k_tok_stride;
   p.n_keys = T; p.n_q = T; p.window = window;
   p.Hkv = d.n_kvheads; p.G = d.n_qheads / d.n_kvheads; p.scale = d.scale;
-  constexpr int BK = SUM_WAVES * SUM_NT * 32;
+  constexpr int BK = SUM_NW * SUM_NT * 32;
   p.n_kblocks = (int)((T + BK - 1) / BK);
   p.nsplit = 1;
   p.use_atomic = 0;
   const int npairs = (p.n_kblocks + 1) / 2;
   const int nblocks = npairs * p.Hkv;
-  if (d.head_dim == 128) return run<128, SUM_WAVES, SUM_NT, true>(p, nblocks, s);
-  return run<64, SUM_WAVES, SUM_NT, true>(p, nblocks, s);
+  if (d.head_dim == 128) return run<128, SUM_NW, SUM_NT, SUM_RT, true>(p, nblocks, s);
+  return run<64, SUM_NW, SUM_NT, SUM_RT, true>(p, nblocks, s);
 }
 
 }  // namespace kvs
