@@ -28,9 +28,11 @@ COMMON = [
 # inputs are finite bf16 values and finite normalisers), so NaN-propagating
 # max/min semantics are not needed there: without them the compiler drops the
 # IEEE canonicalising moves before every v_max and can form v_max3_f32.
+# -amdgpu-mfma-vgpr-form keeps MFMA accumulators in VGPRs, where the VALU
+# softmax reads them, instead of AGPRs that need a v_accvgpr_read per value.
 FILE_FLAGS = {
-    "lse.hip": ["-fno-honor-nans"],
-    "score.hip": ["-fno-honor-nans"],
+    "lse.hip": ["-fno-honor-nans", "-mllvm", "-amdgpu-mfma-vgpr-form"],
+    "score.hip": ["-fno-honor-nans", "-mllvm", "-amdgpu-mfma-vgpr-form"],
 }
 
 

@@ -66,7 +66,7 @@ __global__ __launch_bounds__(LSE_WAVES * WAVE) void lse_kernel(LseParams p) {
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: scalar registers
   const int half = lane >> 5;
   const int col = lane & 31;
 
@@ -112,7 +112,7 @@ __global__ __launch_bounds__(LSE_WAVES * WAVE) void lse_kernel(LseParams p) {
 
   // tile tt -> first key position kt (segment-relative for context tiles,
   // sequence position for self/causal tiles), source rows and key count
-  auto tile_src = [&](int64_t tt, const uint16_t*& base, int64_t& ts, int64_t& k0, int64_t& kend) {
+  auto tile_src = [&](int tt, const uint16_t*& base, int64_t& ts, int64_t& k0, int64_t& kend) {
     if (tt < n_ctx_tiles) {
       base = p.K + (int64_t)h * p.k_hs;
       ts = p.k_ts;
@@ -130,7 +130,7 @@ __global__ __launch_bounds__(LSE_WAVES * WAVE) void lse_kernel(LseParams p) {
   // row is masked (ctx: key >= n_ctx; self/causal: key > j), so its value never
   // counts. Loads are unconditional so issuing a prefetch never stalls.
   u32x4 pre[CPT];
-  auto load_tile = [&](int64_t tt) {
+  auto load_tile = [&](int tt) {
     const uint16_t* base;
     int64_t ts, k0, kend;
     tile_src(tt, base, ts, k0, kend);
@@ -157,80 +157,101 @@ __global__ __launch_bounds__(LSE_WAVES * WAVE) void lse_kernel(LseParams p) {
   // the max is unchanged (so rounding of m * c2 cannot drift l tile by tile).
   const float c2 = p.scale * LOG2E;
   float m_run[LSE_NQ], o_run[LSE_NQ], l_run[LSE_NQ];
+  // Per-lane visibility constants (positions fit in 32 bits): this lane's
+  // query position j and the start of its repeat chunk; per subtile the chunk
+  // starts of its first and last query.
+  int lane_j[LSE_NQ], lane_cs[LSE_NQ], sub_pj[LSE_NQ], sub_cs_first[LSE_NQ], sub_cs_last[LSE_NQ];
 #pragma unroll
   for (int q = 0; q < LSE_NQ; ++q) {
     m_run[q] = -INFINITY;
     o_run[q] = 0.f;
     l_run[q] = 0.f;
+    sub_pj[q] = (int)sub_pos[q];
+    lane_j[q] = sub_pj[q] + col;
+    lane_cs[q] = CAUSAL ? 0 : (int)((lane_j[q] / chunk) * chunk);
+    sub_cs_first[q] = CAUSAL ? 0 : (int)((sub_pj[q] / chunk) * chunk);
+    sub_cs_last[q] = CAUSAL ? 0 : (int)(((sub_pj[q] + 31) / chunk) * chunk);
   }
+  const int n_ctx_i = (int)p.n_ctx, pos_end_i = (int)pos_end, self_lo_i = (int)self_lo;
+  const int n_ctx_tiles_i = (int)n_ctx_tiles, n_tiles_i = (int)n_tiles;
 
-  if (n_tiles > 0) {
+  if (n_tiles_i > 0) {
     load_tile(0);
     store_tile(0);
   }
   __syncthreads();
 
-  for (int64_t tt = 0; tt < n_tiles; ++tt) {
-    const int cur = (int)(tt & 1);
-    if (tt + 1 < n_tiles) load_tile(tt + 1);
+  for (int tt = 0; tt < n_tiles_i; ++tt) {
+    const int cur = tt & 1;
+    if (tt + 1 < n_tiles_i) load_tile(tt + 1);
 
-    const uint16_t* base_unused;
-    int64_t ts_unused, k0, kend;
-    tile_src(tt, base_unused, ts_unused, k0, kend);
-    const bool is_ctx = tt < n_ctx_tiles;
+    const bool is_ctx = tt < n_ctx_tiles_i;
+    const int k0 = is_ctx ? tt * 32 : self_lo_i + (tt - n_ctx_tiles_i) * 32;
+    const int kend = is_ctx ? n_ctx_i : pos_end_i;
 
     bf16x8 a[T::STEPS];
     const char* krow = &s_k[cur][col * T::LDS_STRIDE + half * (D / 2) * 2];
 #pragma unroll
     for (int s = 0; s < T::STEPS; ++s) a[s] = as_bf16x8(*reinterpret_cast<const u32x4*>(krow + 16 * s));
 
+    // visibility of this tile for each subtile's 32 queries [pj, pj + 31]
+    bool run_q[LSE_NQ], full_q[LSE_NQ];
 #pragma unroll
     for (int q = 0; q < LSE_NQ; ++q) {
-      if (!sub_ok[q]) continue;
-      const int64_t pj = sub_pos[q];
-      // visibility of this tile for the subtile's 32 queries [pj, pj + 31]
-      bool full, none;
+      const int pj = sub_pj[q];
       if (is_ctx) {
-        none = false;
-        full = k0 + 31 < kend;
+        run_q[q] = sub_ok[q];
+        full_q[q] = k0 + 31 < kend;
       } else {
-        const int64_t cs_first = CAUSAL ? 0 : (pj / chunk) * chunk;
-        const int64_t cs_last = CAUSAL ? 0 : ((pj + 31) / chunk) * chunk;
-        none = (k0 > pj + 31) || (k0 + 31 < cs_first);
-        full = (k0 + 31 <= pj) && (k0 >= cs_last) && (k0 + 31 < kend);
+        run_q[q] = sub_ok[q] && !((k0 > pj + 31) || (k0 + 31 < sub_cs_first[q]));
+        full_q[q] = (k0 + 31 <= pj) && (k0 >= sub_cs_last[q]) && (k0 + 31 < kend);
       }
-      if (none) continue;
+    }
 
-      f32x16 acc = {};
+    // both MFMA chains first, so the second runs while the first is reduced
+    f32x16 acc[LSE_NQ];
 #pragma unroll
-      for (int s = 0; s < T::STEPS; ++s) acc = mfma32(a[s], qreg[q][s], acc);
+    for (int q = 0; q < LSE_NQ; ++q) {
+      if (!run_q[q]) continue;
+      acc[q] = f32x16{};
+#pragma unroll
+      for (int s = 0; s < T::STEPS; ++s) acc[q] = mfma32(a[s], qreg[q][s], acc[q]);
+    }
 
-      if (!full) {
-        const int64_t j = pj + col;
-        const int64_t cs = (is_ctx || CAUSAL) ? 0 : (j / chunk) * chunk;
+#pragma unroll
+    for (int q = 0; q < LSE_NQ; ++q) {
+      if (!run_q[q]) continue;
+      f32x16& x = acc[q];
+      if (!full_q[q]) {
+        const int kb = k0 + 4 * half;
+        const int j = lane_j[q], cs = lane_cs[q];
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int64_t key = k0 + acc_row(r, half);
+          const int key = kb + 8 * (r >> 2) + (r & 3);
           const bool vis = is_ctx ? (key < kend) : (key <= j && key >= cs);
-          acc[r] = vis ? acc[r] : -INFINITY;
+          x[r] = vis ? x[r] : -INFINITY;
         }
       }
-
-      float tm = acc[0];
+      float tm = max3(x[0], x[1], x[2]);
 #pragma unroll
-      for (int r = 1; r < 16; r += 2) tm = max3(tm, acc[r], (r + 1 < 16) ? acc[r + 1] : acc[r]);
+      for (int r = 3; r < 15; r += 2) tm = max3(tm, x[r], x[r + 1]);
+      tm = fmaxf(tm, x[15]);
       const float m_new = fmaxf(m_run[q], tm);
       const float o_new = (m_new == -INFINITY) ? 0.f : m_new * c2;
-      float sum = 0.f;
+      float e[16];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) sum += fast_exp2(__builtin_fmaf(acc[r], c2, -o_new));
+      for (int r = 0; r < 16; ++r) e[r] = fast_exp2(__builtin_fmaf(x[r], c2, -o_new));
+#pragma unroll
+      for (int w = 8; w >= 1; w >>= 1)
+#pragma unroll
+        for (int r = 0; r < w; ++r) e[r] += e[r + w];
       const float alpha = (m_run[q] == -INFINITY) ? 0.f : fast_exp2(o_run[q] - o_new);
-      l_run[q] = l_run[q] * alpha + sum;
+      l_run[q] = l_run[q] * alpha + e[0];
       m_run[q] = m_new;
       o_run[q] = o_new;
     }
 
-    if (tt + 1 < n_tiles) store_tile(cur ^ 1);
+    if (tt + 1 < n_tiles_i) store_tile(cur ^ 1);
     __syncthreads();
   }
 

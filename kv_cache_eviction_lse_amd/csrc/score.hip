@@ -75,7 +75,7 @@ __global__ __launch_bounds__(NW * WAVE) void score_kernel(ScoreParams p) {
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: scalar registers
   const int half = lane >> 5;
   const int col = lane & 31;
 
