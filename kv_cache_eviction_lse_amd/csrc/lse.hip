@@ -20,12 +20,19 @@
 //     stage and are the A operands (keys are rows), so each lane's 16
 //     accumulator registers are 16 keys of one query: the softmax reduction
 //     is in-register, and the two half-waves merge once at the end;
-//   * online softmax in the exp2 domain on raw dot products: running max m,
-//     running sum l of exp2((q.k - m) * scale * log2 e);
+//   * online softmax in the exp2 domain on raw dot products: a running sum l
+//     of exp2(q.k * scale * log2 e - o) against an offset o that follows the
+//     running max lazily (raised only when a tile's sum would grow large);
 //   * tiles a subtile cannot see are skipped; only tiles cut by the causal
 //     diagonal, a chunk edge or the end of the keys are masked per element.
 #include "common.hpp"
 #include "internal.hpp"
+
+// No implicit a*b+c contraction in this file: the running-sum rescale relies
+// on exp2(o_old - o_new) being exactly 1 when the max is unchanged, which
+// needs o = fl(m * c2) rounded once and then used as is. (Explicit fmaf
+// calls still produce FMAs.)
+#pragma clang fp contract(off)
 
 namespace kvs {
 namespace {
@@ -55,7 +62,7 @@ constexpr int LSE_NQ = 2;
 constexpr int SUB_PER_BLOCK = LSE_WAVES * LSE_NQ;
 
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(LSE_WAVES * WAVE) void lse_kernel(LseParams p) {
+__global__ __launch_bounds__(LSE_WAVES * WAVE, 3) void lse_kernel(LseParams p) {
   using T = KTile<D>;
   constexpr int NTHREADS = LSE_WAVES * WAVE;
   static_assert(T::CHUNKS % NTHREADS == 0, "tile chunks must split evenly over the threads");
@@ -151,20 +158,23 @@ __global__ __launch_bounds__(LSE_WAVES * WAVE) void lse_kernel(LseParams p) {
     }
   };
 
-  // Running state per subtile column: raw max m, the exp2-domain offset
-  // o = fl(m * c2) that every term of l was computed against, and l. Rescaling
-  // uses exp2(o_old - o_new) on the stored offsets, which is exactly 1 while
-  // the max is unchanged (so rounding of m * c2 cannot drift l tile by tile).
+  // Running state per subtile column: the exp2-domain offset o that every
+  // term of l was computed against, and l. The offset follows the running max
+  // lazily: a tile is first exponentiated against the current offset, and only
+  // when its partial sum gets large (> 2^20, or +inf on the first visible
+  // tile, whose offset starts at -FLT_MAX) is the offset raised to
+  // fl(tile max * c2), with l rescaled by exp2(o_old - o_new). Offsets are
+  // stored values used as is, so no rounding drift builds up; masked logits
+  // are -inf and contribute exp2(-inf) = 0 (never inf - inf).
   const float c2 = p.scale * LOG2E;
-  float m_run[LSE_NQ], o_run[LSE_NQ], l_run[LSE_NQ];
+  float o_run[LSE_NQ], l_run[LSE_NQ];
   // Per-lane visibility constants (positions fit in 32 bits): this lane's
   // query position j and the start of its repeat chunk; per subtile the chunk
   // starts of its first and last query.
   int lane_j[LSE_NQ], lane_cs[LSE_NQ], sub_pj[LSE_NQ], sub_cs_first[LSE_NQ], sub_cs_last[LSE_NQ];
 #pragma unroll
   for (int q = 0; q < LSE_NQ; ++q) {
-    m_run[q] = -INFINITY;
-    o_run[q] = 0.f;
+    o_run[q] = -3.402823466e38f;
     l_run[q] = 0.f;
     sub_pj[q] = (int)sub_pos[q];
     lane_j[q] = sub_pj[q] + col;
@@ -232,23 +242,33 @@ __global__ __launch_bounds__(LSE_WAVES * WAVE) void lse_kernel(LseParams p) {
           x[r] = vis ? x[r] : -INFINITY;
         }
       }
-      float tm = max3(x[0], x[1], x[2]);
-#pragma unroll
-      for (int r = 3; r < 15; r += 2) tm = max3(tm, x[r], x[r + 1]);
-      tm = fmaxf(tm, x[15]);
-      const float m_new = fmaxf(m_run[q], tm);
-      const float o_new = (m_new == -INFINITY) ? 0.f : m_new * c2;
       float e[16];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) e[r] = fast_exp2(__builtin_fmaf(x[r], c2, -o_new));
+      for (int r = 0; r < 16; ++r) e[r] = fast_exp2(__builtin_fmaf(x[r], c2, -o_run[q]));
 #pragma unroll
       for (int w = 8; w >= 1; w >>= 1)
 #pragma unroll
         for (int r = 0; r < w; ++r) e[r] += e[r + w];
-      const float alpha = (m_run[q] == -INFINITY) ? 0.f : fast_exp2(o_run[q] - o_new);
-      l_run[q] = l_run[q] * alpha + e[0];
-      m_run[q] = m_new;
-      o_run[q] = o_new;
+      float sum = e[0];
+      if (sum > 1048576.0f) {
+        // raise the offset to this tile's max and redo the tile (rare)
+        float tm = max3(x[0], x[1], x[2]);
+#pragma unroll
+        for (int r = 3; r < 15; r += 2) tm = max3(tm, x[r], x[r + 1]);
+        tm = fmaxf(tm, x[15]);
+        const float o_new = fmaxf(o_run[q], tm * c2);
+        float f[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) f[r] = fast_exp2(__builtin_fmaf(x[r], c2, -o_new));
+#pragma unroll
+        for (int w = 8; w >= 1; w >>= 1)
+#pragma unroll
+          for (int r = 0; r < w; ++r) f[r] += f[r + w];
+        l_run[q] *= fast_exp2(o_run[q] - o_new);
+        o_run[q] = o_new;
+        sum = f[0];
+      }
+      l_run[q] += sum;
     }
 
     if (tt + 1 < n_tiles_i) store_tile(cur ^ 1);
@@ -260,9 +280,7 @@ __global__ __launch_bounds__(LSE_WAVES * WAVE) void lse_kernel(LseParams p) {
   for (int q = 0; q < LSE_NQ; ++q) {
     const float o_o = __shfl_xor(o_run[q], 32);
     const float l_o = __shfl_xor(l_run[q], 32);
-    const float m_o = __shfl_xor(m_run[q], 32);
-    // the larger offset belongs to the larger max (rounding is monotone)
-    const float Mc = (m_run[q] == -INFINITY) ? o_o : ((m_o == -INFINITY) ? o_run[q] : fmaxf(o_run[q], o_o));
+    const float Mc = fmaxf(o_run[q], o_o);
     const float L = (l_run[q] > 0.f ? l_run[q] * fast_exp2(o_run[q] - Mc) : 0.f) +
                     (l_o > 0.f ? l_o * fast_exp2(o_o - Mc) : 0.f);
     const int64_t j = sub_pos[q] + col;
