@@ -58,6 +58,7 @@ struct KTile {
 };
 
 constexpr int LSE_WAVES = 4;
+constexpr float LAZY_LIMIT = 1048576.0f;  // 2^20: raise the offset when a tile's sum exceeds this
 constexpr int LSE_NQ = 2;
 constexpr int SUB_PER_BLOCK = LSE_WAVES * LSE_NQ;
 
@@ -184,6 +185,77 @@ __global__ __launch_bounds__(LSE_WAVES * WAVE, 3) void lse_kernel(LseParams p) {
   }
   const int n_ctx_i = (int)p.n_ctx, pos_end_i = (int)pos_end, self_lo_i = (int)self_lo;
   const int n_ctx_tiles_i = (int)n_ctx_tiles, n_tiles_i = (int)n_tiles;
+  const int n_ctx_full_tiles = CAUSAL ? 0 : n_ctx_i / 32;  // context tiles with no key past the end
+  bool all_sub_ok = true;
+#pragma unroll
+  for (int q = 0; q < LSE_NQ; ++q) all_sub_ok = all_sub_ok && sub_ok[q];
+
+  // sum over a tile's 16 logits of exp2(x * c2 - o) (masked logits are -inf)
+  auto exp_sum = [&](const f32x16& x, float o) {
+    float e[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) e[r] = fast_exp2(__builtin_fmaf(x[r], c2, -o));
+#pragma unroll
+    for (int w = 8; w >= 1; w >>= 1)
+#pragma unroll
+      for (int r = 0; r < w; ++r) e[r] += e[r + w];
+    return e[0];
+  };
+  // (rare) raise subtile q's offset to fl(tile max * c2), rescale its sum,
+  // and return the tile's sum against the new offset
+  auto raise_offset = [&](int q, const f32x16& x) {
+    float tm = max3(x[0], x[1], x[2]);
+#pragma unroll
+    for (int r = 3; r < 15; r += 2) tm = max3(tm, x[r], x[r + 1]);
+    tm = fmaxf(tm, x[15]);
+    const float o_new = fmaxf(o_run[q], tm * c2);
+    l_run[q] *= fast_exp2(o_run[q] - o_new);
+    o_run[q] = o_new;
+    return exp_sum(x, o_new);
+  };
+  // Lazy online-softmax update of subtile q with one tile's logits x. See the
+  // running-state comment above.
+  auto softmax_update = [&](int q, f32x16& x) {
+    float sum = exp_sum(x, o_run[q]);
+    if (sum > LAZY_LIMIT) sum = raise_offset(q, x);
+    l_run[q] += sum;
+  };
+
+  // General tile: partial context tiles and self / causal tiles. Subtiles
+  // that see none of the tile skip it; tiles cut by the end of the keys, the
+  // causal diagonal or a chunk edge are masked per element.
+  auto tile_general = [&](int tt, const bf16x8 (&a)[T::STEPS]) {
+    const bool is_ctx = tt < n_ctx_tiles_i;
+    const int k0 = is_ctx ? tt * 32 : self_lo_i + (tt - n_ctx_tiles_i) * 32;
+    const int kend = is_ctx ? n_ctx_i : pos_end_i;
+#pragma unroll
+    for (int q = 0; q < LSE_NQ; ++q) {
+      const int pj = sub_pj[q];
+      bool run, full;
+      if (is_ctx) {
+        run = sub_ok[q];
+        full = k0 + 31 < kend;
+      } else {
+        run = sub_ok[q] && !((k0 > pj + 31) || (k0 + 31 < sub_cs_first[q]));
+        full = (k0 + 31 <= pj) && (k0 >= sub_cs_last[q]) && (k0 + 31 < kend);
+      }
+      if (!run) continue;
+      f32x16 x = mfma32(a[0], qreg[q][0], f32x16{});
+#pragma unroll
+      for (int s = 1; s < T::STEPS; ++s) x = mfma32(a[s], qreg[q][s], x);
+      if (!full) {
+        const int kb = k0 + 4 * half;
+        const int j = lane_j[q], cs = lane_cs[q];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = kb + 8 * (r >> 2) + (r & 3);
+          const bool vis = is_ctx ? (key < kend) : (key <= j && key >= cs);
+          x[r] = vis ? x[r] : -INFINITY;
+        }
+      }
+      softmax_update(q, x);
+    }
+  };
 
   if (n_tiles_i > 0) {
     load_tile(0);
@@ -195,80 +267,30 @@ __global__ __launch_bounds__(LSE_WAVES * WAVE, 3) void lse_kernel(LseParams p) {
     const int cur = tt & 1;
     if (tt + 1 < n_tiles_i) load_tile(tt + 1);
 
-    const bool is_ctx = tt < n_ctx_tiles_i;
-    const int k0 = is_ctx ? tt * 32 : self_lo_i + (tt - n_ctx_tiles_i) * 32;
-    const int kend = is_ctx ? n_ctx_i : pos_end_i;
-
     bf16x8 a[T::STEPS];
     const char* krow = &s_k[cur][col * T::LDS_STRIDE + half * (D / 2) * 2];
 #pragma unroll
     for (int s = 0; s < T::STEPS; ++s) a[s] = as_bf16x8(*reinterpret_cast<const u32x4*>(krow + 16 * s));
 
-    // visibility of this tile for each subtile's 32 queries [pj, pj + 31]
-    bool run_q[LSE_NQ], full_q[LSE_NQ];
+    if (tt < n_ctx_full_tiles && all_sub_ok) {
+      // Fast path (all full context tiles): every key visible to every query
+      // of both subtiles; straight-line code, no masks.
+      // The MFMA block runs at raised wave priority: among the waves of a
+      // SIMD, the one ready to issue matrix work goes first, the others fill
+      // the VALU with their exponentials meanwhile.
+      f32x16 acc[LSE_NQ];
+      __builtin_amdgcn_s_setprio(1);
 #pragma unroll
-    for (int q = 0; q < LSE_NQ; ++q) {
-      const int pj = sub_pj[q];
-      if (is_ctx) {
-        run_q[q] = sub_ok[q];
-        full_q[q] = k0 + 31 < kend;
-      } else {
-        run_q[q] = sub_ok[q] && !((k0 > pj + 31) || (k0 + 31 < sub_cs_first[q]));
-        full_q[q] = (k0 + 31 <= pj) && (k0 >= sub_cs_last[q]) && (k0 + 31 < kend);
+      for (int q = 0; q < LSE_NQ; ++q) {
+        acc[q] = mfma32(a[0], qreg[q][0], f32x16{});
+#pragma unroll
+        for (int s = 1; s < T::STEPS; ++s) acc[q] = mfma32(a[s], qreg[q][s], acc[q]);
       }
-    }
-
-    // both MFMA chains first, so the second runs while the first is reduced
-    f32x16 acc[LSE_NQ];
+      __builtin_amdgcn_s_setprio(0);
 #pragma unroll
-    for (int q = 0; q < LSE_NQ; ++q) {
-      if (!run_q[q]) continue;
-      acc[q] = f32x16{};
-#pragma unroll
-      for (int s = 0; s < T::STEPS; ++s) acc[q] = mfma32(a[s], qreg[q][s], acc[q]);
-    }
-
-#pragma unroll
-    for (int q = 0; q < LSE_NQ; ++q) {
-      if (!run_q[q]) continue;
-      f32x16& x = acc[q];
-      if (!full_q[q]) {
-        const int kb = k0 + 4 * half;
-        const int j = lane_j[q], cs = lane_cs[q];
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = kb + 8 * (r >> 2) + (r & 3);
-          const bool vis = is_ctx ? (key < kend) : (key <= j && key >= cs);
-          x[r] = vis ? x[r] : -INFINITY;
-        }
-      }
-      float e[16];
-#pragma unroll
-      for (int r = 0; r < 16; ++r) e[r] = fast_exp2(__builtin_fmaf(x[r], c2, -o_run[q]));
-#pragma unroll
-      for (int w = 8; w >= 1; w >>= 1)
-#pragma unroll
-        for (int r = 0; r < w; ++r) e[r] += e[r + w];
-      float sum = e[0];
-      if (sum > 1048576.0f) {
-        // raise the offset to this tile's max and redo the tile (rare)
-        float tm = max3(x[0], x[1], x[2]);
-#pragma unroll
-        for (int r = 3; r < 15; r += 2) tm = max3(tm, x[r], x[r + 1]);
-        tm = fmaxf(tm, x[15]);
-        const float o_new = fmaxf(o_run[q], tm * c2);
-        float f[16];
-#pragma unroll
-        for (int r = 0; r < 16; ++r) f[r] = fast_exp2(__builtin_fmaf(x[r], c2, -o_new));
-#pragma unroll
-        for (int w = 8; w >= 1; w >>= 1)
-#pragma unroll
-          for (int r = 0; r < w; ++r) f[r] += f[r + w];
-        l_run[q] *= fast_exp2(o_run[q] - o_new);
-        o_run[q] = o_new;
-        sum = f[0];
-      }
-      l_run[q] += sum;
+      for (int q = 0; q < LSE_NQ; ++q) softmax_update(q, acc[q]);
+    } else {
+      tile_general(tt, a);
     }
 
     if (tt + 1 < n_tiles_i) store_tile(cur ^ 1);
