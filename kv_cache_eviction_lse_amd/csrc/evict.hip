@@ -15,9 +15,11 @@
 //     launch is needed. After the last pass the k-th key T is exact; keys > T
 //     are kept, and among keys == T the lowest positions up to the quota.
 //   evict_count: per block, rows kept for sure and rows tied at T.
-//   evict_scan (one block): block offsets and per-head offsets.
-//   evict_write: predicate, ballot/prefix scan, index write and a coalesced
-//     gather of the kept K and V rows (16 lanes x 16 bytes per 256-byte row).
+//   evict_scan (one block per head): block offsets and the head's total.
+//   evict_write: predicate, tie ranks and prefix scan, kept indices; block
+//     (0, 0) writes the per-head offsets.
+//   evict_gather (a grid over output rows): coalesced copy of the kept K and
+//     V rows, 16-byte pieces, non-temporal loads and stores.
 #include "common.hpp"
 #include "internal.hpp"
 
@@ -206,42 +208,51 @@ __global__ __launch_bounds__(EV_THREADS) void evict_count(EvictParams p) {
   }
 }
 
+// One block per head: scan the head's block counts into block offsets (within
+// the head) and tie ranks, and store the head's total kept rows.
 __global__ __launch_bounds__(EV_THREADS) void evict_scan(EvictParams p) {
-  int64_t running = 0;
-  for (int h = 0; h < p.Hkv; ++h) {
-    const int quota = p.mode == MODE_TOPK ? p.state[h * 4 + 1] : 0;
-    if (threadIdx.x == 0) p.head_offsets[h] = running;
-    int sure_base = 0, tied_base = 0;
-    for (int b0 = 0; b0 < p.nb; b0 += EV_THREADS) {
-      const int b = b0 + (int)threadIdx.x;
-      int32_t* e = p.blk + ((int64_t)h * p.nb + (b < p.nb ? b : 0)) * 4;
-      const int sure = b < p.nb ? e[0] : 0;
-      const int tied = b < p.nb ? e[1] : 0;
-      int ts, tt;
-      const int sb = block_exclusive_scan(sure, &ts) + sure_base;
-      const int tb = block_exclusive_scan(tied, &tt) + tied_base;
-      if (b < p.nb) {
-        e[2] = sb + min(tb, quota);
-        e[3] = tb;
-      }
-      sure_base += ts;
-      tied_base += tt;
+  const int h = blockIdx.x;
+  const int quota = p.mode == MODE_TOPK ? p.state[h * 4 + 1] : 0;
+  int sure_base = 0, tied_base = 0;
+  for (int b0 = 0; b0 < p.nb; b0 += EV_THREADS) {
+    const int b = b0 + (int)threadIdx.x;
+    int32_t* e = p.blk + ((int64_t)h * p.nb + (b < p.nb ? b : 0)) * 4;
+    const int sure = b < p.nb ? e[0] : 0;
+    const int tied = b < p.nb ? e[1] : 0;
+    int ts, tt;
+    const int sb = block_exclusive_scan(sure, &ts) + sure_base;
+    const int tb = block_exclusive_scan(tied, &tt) + tied_base;
+    if (b < p.nb) {
+      e[2] = sb + min(tb, quota);
+      e[3] = tb;
     }
-    running += sure_base + min(tied_base, quota);
+    sure_base += ts;
+    tied_base += tt;
   }
-  if (threadIdx.x == 0) p.head_offsets[p.Hkv] = running;
+  if (threadIdx.x == 0) p.state[h * 4 + 2] = sure_base + min(tied_base, quota);
 }
 
-template <int D>
+// first output row of head h: the totals of the heads before it
+__device__ __forceinline__ int64_t head_start(const EvictParams& p, int h) {
+  int64_t off = 0;
+  for (int k = 0; k < h; ++k) off += p.state[k * 4 + 2];
+  return off;
+}
+
+// Predicate, tie ranks, positions, and the kept indices of one block of keys.
+// Block (0, 0) also writes the per-head offsets.
 __global__ __launch_bounds__(EV_THREADS) void evict_write(EvictParams p) {
-  __shared__ int32_t s_list[EPB];
   const int h = blockIdx.y, b = blockIdx.x;
+  if (b == 0 && h == 0) {
+    for (int k = threadIdx.x; k <= p.Hkv; k += EV_THREADS) p.head_offsets[k] = head_start(p, k);
+  }
+  if (p.nb == 0) return;  // no keys: only the (zero) offsets
   const uint32_t T = (uint32_t)p.state[h * 4 + 0];
   const int quota = p.state[h * 4 + 1];
   const int32_t* e = p.blk + ((int64_t)h * p.nb + b) * 4;
   const int blk_off = e[2];
   const int ties_before = e[3];
-  const int64_t head_off = p.head_offsets[h];
+  const int64_t out0 = head_start(p, h) + blk_off;
 
   const int64_t i0 = (int64_t)b * EPB + threadIdx.x * EV_PER_THREAD;
   const float* sc = p.scores + (int64_t)h * p.s_hs;
@@ -268,43 +279,58 @@ __global__ __launch_bounds__(EV_THREADS) void evict_write(EvictParams p) {
   int pos = block_exclusive_scan(keep, &n_keep);
 #pragma unroll
   for (int k = 0; k < EV_PER_THREAD; ++k) {
-    if (cls[k] == 2) {
-      const int64_t i = i0 + k;
-      p.kept_idx[head_off + blk_off + pos] = (int32_t)i;
-      s_list[pos] = (int32_t)i;
-      ++pos;
-    }
+    if (cls[k] == 2) p.kept_idx[out0 + pos++] = (int32_t)(i0 + k);
   }
-  __syncthreads();
+}
 
-  // gather: LPR lanes per row, 16 bytes each
+// Coalesced copy of the kept K and V rows: GROWS output rows per block, D/8
+// lanes per row with 16 bytes each; all loads of a block's rows are issued
+// before the stores. Rows past the total (known only on the device in
+// threshold mode) are skipped.
+constexpr int GROWS = 64;
+constexpr int MAX_LDS_HEADS = 256;
+
+template <int D>
+__global__ __launch_bounds__(EV_THREADS) void evict_gather(EvictParams p) {
+  __shared__ int64_t s_off[MAX_LDS_HEADS + 1];
+  const int64_t total = p.head_offsets[p.Hkv];
+  const int64_t r0 = (int64_t)blockIdx.x * GROWS;
+  if (r0 >= total) return;
+  const bool lds_heads = p.Hkv <= MAX_LDS_HEADS;
+  if (lds_heads)
+    for (int k = threadIdx.x; k <= p.Hkv; k += EV_THREADS) s_off[k] = p.head_offsets[k];
+  __syncthreads();
+  auto head_of = [&](int64_t r) {  // last h with offset[h] <= r
+    int lo = 0, hi = p.Hkv - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      const int64_t o = lds_heads ? s_off[mid] : p.head_offsets[mid];
+      if (o <= r) lo = mid; else hi = mid - 1;
+    }
+    return lo;
+  };
   constexpr int LPR = D / 8;
   constexpr int RPP = EV_THREADS / LPR;  // rows per pass
-  constexpr int UNROLL = 4;
+  constexpr int PASSES = GROWS / RPP;
   const int part = threadIdx.x % LPR;
-  const int r0 = threadIdx.x / LPR;
-  const uint16_t* Kh = p.K + (int64_t)h * p.kv_hs + part * 8;
-  const uint16_t* Vh = p.V + (int64_t)h * p.kv_hs + part * 8;
-  uint16_t* Ko = p.K_out + (head_off + blk_off) * D + part * 8;
-  uint16_t* Vo = p.V_out + (head_off + blk_off) * D + part * 8;
-  for (int rb = 0; rb < n_keep; rb += RPP * UNROLL) {
-    u32x4 kv[UNROLL], vv[UNROLL];
+  const int rr = threadIdx.x / LPR;
+  u32x4 kv[PASSES], vv[PASSES];
 #pragma unroll
-    for (int u = 0; u < UNROLL; ++u) {
-      const int r = rb + u * RPP + r0;
-      if (r < n_keep) {
-        const int64_t src = (int64_t)s_list[r] * p.kv_ts;
-        kv[u] = ld16(Kh + src);
-        vv[u] = ld16(Vh + src);
-      }
+  for (int i = 0; i < PASSES; ++i) {
+    const int64_t r = r0 + i * RPP + rr;
+    if (r < total) {
+      const int h = head_of(r);
+      const int64_t src = (int64_t)h * p.kv_hs + (int64_t)p.kept_idx[r] * p.kv_ts + part * 8;
+      kv[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p.K + src));
+      vv[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p.V + src));
     }
+  }
 #pragma unroll
-    for (int u = 0; u < UNROLL; ++u) {
-      const int r = rb + u * RPP + r0;
-      if (r < n_keep) {
-        st16(Ko + (int64_t)r * D, kv[u]);
-        st16(Vo + (int64_t)r * D, vv[u]);
-      }
+  for (int i = 0; i < PASSES; ++i) {
+    const int64_t r = r0 + i * RPP + rr;
+    if (r < total) {
+      __builtin_nontemporal_store(kv[i], reinterpret_cast<u32x4*>(p.K_out + r * D + part * 8));
+      __builtin_nontemporal_store(vv[i], reinterpret_cast<u32x4*>(p.V_out + r * D + part * 8));
     }
   }
 }
@@ -365,23 +391,28 @@ hipError_t launch_evict(const kvs_evict_desc& e, const float* scores, const uint
 
   const dim3 grid(p.nb > 0 ? p.nb : 1, p.Hkv);
   hipError_t err;
-  if (p.nb > 0) {
-    if (p.mode == MODE_TOPK) {
-      hipLaunchKernelGGL(evict_zero, dim3(64), dim3(256), 0, s, p.hist, (int64_t)3 * p.Hkv * NBINS);
-      hipLaunchKernelGGL(evict_hist<0>, grid, dim3(EV_THREADS), 0, s, p);
-      hipLaunchKernelGGL(evict_hist<1>, grid, dim3(EV_THREADS), 0, s, p);
-      hipLaunchKernelGGL(evict_hist<2>, grid, dim3(EV_THREADS), 0, s, p);
-    }
-    hipLaunchKernelGGL(evict_count, grid, dim3(EV_THREADS), 0, s, p);
-    if ((err = hipGetLastError()) != hipSuccess) return err;
+  if (p.mode == MODE_TOPK) {
+    hipLaunchKernelGGL(evict_zero, dim3(64), dim3(256), 0, s, p.hist, (int64_t)3 * p.Hkv * NBINS);
+    hipLaunchKernelGGL(evict_hist<0>, grid, dim3(EV_THREADS), 0, s, p);
+    hipLaunchKernelGGL(evict_hist<1>, grid, dim3(EV_THREADS), 0, s, p);
+    hipLaunchKernelGGL(evict_hist<2>, grid, dim3(EV_THREADS), 0, s, p);
   }
-  hipLaunchKernelGGL(evict_scan, dim3(1), dim3(EV_THREADS), 0, s, p);
+  if (p.nb > 0) hipLaunchKernelGGL(evict_count, grid, dim3(EV_THREADS), 0, s, p);
+  hipLaunchKernelGGL(evict_scan, dim3(p.Hkv), dim3(EV_THREADS), 0, s, p);
   if ((err = hipGetLastError()) != hipSuccess) return err;
   if (p.nb > 0) {
+    hipLaunchKernelGGL(evict_write, grid, dim3(EV_THREADS), 0, s, p);
+  } else {
+    // nothing to select: only the offsets (all zero)
+    hipLaunchKernelGGL(evict_write, dim3(1, 1), dim3(EV_THREADS), 0, s, p);
+  }
+  const int64_t cap_rows = e.capacity;
+  if (cap_rows > 0 && p.nb > 0) {
+    const int64_t gblocks = (cap_rows + GROWS - 1) / GROWS;
     if (p.D == 128)
-      hipLaunchKernelGGL(evict_write<128>, grid, dim3(EV_THREADS), 0, s, p);
+      hipLaunchKernelGGL(evict_gather<128>, dim3((unsigned)gblocks), dim3(EV_THREADS), 0, s, p);
     else
-      hipLaunchKernelGGL(evict_write<64>, grid, dim3(EV_THREADS), 0, s, p);
+      hipLaunchKernelGGL(evict_gather<64>, dim3((unsigned)gblocks), dim3(EV_THREADS), 0, s, p);
   }
   return hipGetLastError();
 }
