@@ -287,7 +287,7 @@ __global__ __launch_bounds__(EV_THREADS) void evict_write(EvictParams p) {
 // lanes per row with 16 bytes each; all loads of a block's rows are issued
 // before the stores. Rows past the total (known only on the device in
 // threshold mode) are skipped.
-constexpr int GROWS = 64;
+constexpr int GROWS = 32;
 constexpr int MAX_LDS_HEADS = 256;
 
 template <int D>

@@ -200,6 +200,12 @@ EVICT_CASES = [
     ("tau-zero", 2, 3000, 64, 8, None, 0.0),
     ("tau-inf", 2, 3000, 128, 8, None, float("inf")),
     ("empty", 2, 0, 128, 8, 5, None),
+    # grid path: more heads than the gather's LDS table, or more keys per head
+    # than one workgroup takes
+    ("many-heads-topk", 4097, 100, 64, 10, 30, None),
+    ("many-heads-tau", 300, 700, 64, 16, None, float(np.exp(-6.0))),
+    ("long-heads-topk", 2, 140000, 64, 128, 35000, None),
+    ("long-heads-tau", 2, 140000, 64, 128, None, float(np.exp(-6.0))),
 ]
 
 
