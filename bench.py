@@ -110,6 +110,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy (for scaling HBM byte counters)")
+    ap.add_argument("--workload", default="qwen3-8b-layer-kvzip+-32k",
+                    help="named synthetic layer (synth/workloads.py); the default is the 32k layer the "
+                         "headline metric is quoted on")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the scoring path shards by KV head "
@@ -121,7 +124,10 @@ def main():
     import kv_cache_eviction_lse_amd as kvs
     from kv_cache_eviction_lse_amd import accounting as acc
     import synth
-    from synth.workloads import QWEN3_8B_32K as wl
+    from synth.workloads import BY_NAME
+
+    wl = BY_NAME[args.workload]
+    sum_mode = wl.score_mode == "sum"
 
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
@@ -147,31 +153,41 @@ def main():
     def dev_bf16(x):
         return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).view(torch.bfloat16).cuda()
 
-    Q, K, Ks, V = dev_bf16(d["Q"]), dev_bf16(d["Kctx"]), dev_bf16(d["Kself"]), dev_bf16(d["V"])
-    vn = torch.from_numpy(d["vnorm"]).cuda()
-    hn = torch.from_numpy(d["hnorm"]).cuda()
+    Q, K, V = dev_bf16(d["Q"]), dev_bf16(d["Kctx"]), dev_bf16(d["V"])
+    Ks = dev_bf16(d["Kself"]) if "Kself" in d else None
+    vn = torch.from_numpy(d["vnorm"]).cuda() if "vnorm" in d else None
+    hn = torch.from_numpy(d["hnorm"]).cuda() if "hnorm" in d else None
     scale = d["scale"]
     L = torch.empty((r.Hq, r.n_q), dtype=torch.float32, device="cuda")
     S = torch.empty((r.Hkv, r.n_ctx), dtype=torch.float32, device="cuda")
-    e = kvs.evict_desc(S, K, window=wl.window, tau=wl.tau)
+    sel = dict(tau=wl.tau) if wl.tau >= 0 else dict(k=wl.ks()[0])
+    e = kvs.evict_desc(S, K, window=wl.window, **sel)
     cap = e.capacity
     outs = (torch.empty(cap, dtype=torch.int32, device="cuda"),
             torch.empty(r.Hkv + 1, dtype=torch.int64, device="cuda"),
             torch.empty((cap, r.D), dtype=torch.bfloat16, device="cuda"),
             torch.empty((cap, r.D), dtype=torch.bfloat16, device="cuda"))
     ws = torch.empty(max(kvs.evict_workspace_bytes(e), 256), dtype=torch.uint8, device="cuda")
+    if args.no_cpu_baseline or sum_mode:
+        del d["Q"]  # the host copy is needed only by the CPU baseline
     stream = torch.cuda.current_stream()
 
     def step(ev=None):
         if ev:
             ev[0].record(stream)
-        kvs.lse(Q, K, Ks, scale=scale, mask="repeat", chunk=r.chunk, out=L)
+        if sum_mode:
+            kvs.lse(Q, K, None, scale=scale, mask="causal", out=L)
+        else:
+            kvs.lse(Q, K, Ks, scale=scale, mask="repeat", chunk=r.chunk, out=L)
         if ev:
             ev[1].record(stream)
-        kvs.max_scores(Q, K, L, scale=scale, vnorm=vn, hnorm=hn, out=S)
+        if sum_mode:
+            kvs.future_mass(Q, K, L, scale=scale, window=wl.window, vnorm=vn, hnorm=hn, out=S)
+        else:
+            kvs.max_scores(Q, K, L, scale=scale, vnorm=vn, hnorm=hn, out=S)
         if ev:
             ev[2].record(stream)
-        kvs.evict(S, K, V, window=wl.window, tau=wl.tau, workspace=ws, outputs=outs)
+        kvs.evict(S, K, V, window=wl.window, workspace=ws, outputs=outs, **sel)
         if ev:
             ev[3].record(stream)
 
@@ -193,15 +209,20 @@ def main():
     offs = outs[1].cpu().numpy()
     kept = np.diff(offs)
     kept_total = int(offs[-1])
-    score_flops = acc.flops(acc.max_pairs(r.Hq, r.n_ctx, r.n_q), r.D)
-    lse_flops = acc.flops(acc.lse_pairs(r.Hq, r.n_ctx, r.n_q, "repeat", r.chunk), r.D)
+    if sum_mode:
+        score_flops = acc.flops(acc.sum_pairs(r.Hq, r.n_ctx, wl.window), r.D)
+        lse_flops = acc.flops(acc.lse_pairs(r.Hq, r.n_ctx, r.n_q, "causal"), r.D)
+    else:
+        score_flops = acc.flops(acc.max_pairs(r.Hq, r.n_ctx, r.n_q), r.D)
+        lse_flops = acc.flops(acc.lse_pairs(r.Hq, r.n_ctx, r.n_q, "repeat", r.self_chunk), r.D)
     ev_bytes = acc.evict_bytes(r.Hkv, r.n_ctx, kept_total, r.D)
     score_tflops = score_flops / (t_score * 1e-3) / 1e12
     lse_tflops = lse_flops / (t_lse * 1e-3) / 1e12
     evict_gbs = ev_bytes / (t_evict * 1e-3) / 1e9
     keys_per_s = r.Hkv * r.n_ctx / (ms_per_step * 1e-3)
 
-    traffic = stored_traffic(os.path.join(ROOT, "kv_cache_eviction_lse_amd", "csrc", "score.hip"))
+    traffic = None if sum_mode or wl is not BY_NAME["qwen3-8b-layer-kvzip+-32k"] else \
+        stored_traffic(os.path.join(ROOT, "kv_cache_eviction_lse_amd", "csrc", "score.hip"))
     out = {
         "metric": METRIC,
         "value": keys_per_s,
@@ -216,19 +237,20 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": wl.name, "Hq": r.Hq, "Hkv": r.Hkv, "head_dim": r.D, "n_ctx": r.n_ctx,
-                   "n_q": r.n_q, "chunk": r.chunk, "tau": wl.tau, "window": wl.window,
-                   "parallelism": "single GPU"},
+                   "n_q": r.n_q, "chunk": r.self_chunk, "mask": r.mask,
+                   "selection": ({"tau": wl.tau} if wl.tau >= 0 else {"k": wl.ks()[0]}),
+                   "window": wl.window, "parallelism": "single GPU"},
         "roofline": {"bound": "mfma", "achieved": score_tflops, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": score_tflops / PEAK_BF16_TFLOPS, "traffic": traffic,
-                     "kernel": "score pass (kvscore_max)"},
-        "kernels_ms": {"lse": t_lse, "score_max": t_score, "evict": t_evict},
+                     "kernel": "score pass (" + ("kvscore_futuremass" if sum_mode else "kvscore_max") + ")"},
+        "kernels_ms": {"lse": t_lse, "score": t_score, "evict": t_evict},
         "lse_pass": {"tflops": lse_tflops, "frac_of_bf16_peak": lse_tflops / PEAK_BF16_TFLOPS},
         "score_pass": {"tflops": score_tflops, "flops": score_flops},
         "evict": {"gbs": evict_gbs, "frac_of_hbm_peak": evict_gbs / PEAK_HBM_GBS, "bytes": ev_bytes,
                   "kept_per_head": kept.tolist(),
                   "compression_per_head": [round(acc.compression_ratio(int(x), r.n_ctx), 4) for x in kept]},
     }
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and not sum_mode:
         _log("[bench] timing the CPU oracle on a sample")
         out["cpu_baseline"] = cpu_baseline(d, wl)
     print(json.dumps(out), flush=True)
