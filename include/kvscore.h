@@ -123,7 +123,8 @@ int kvscore_max(const kvs_attn_desc* d, const kvs_bf16* Q, const kvs_bf16* K,
  *             exp(scale * q_j^g . k_i - lse[g][j]) * vnorm[h][i] / hnorm[j]
  * lse [n_qheads, n_ctx] (the CAUSAL kvscore_lse output); vnorm/hnorm as for
  * kvscore_max (NULL for 1); target [n_kvheads, n_ctx] fp32, overwritten.
- * Keys with i + window >= n_ctx get 0. window >= 0. */
+ * Keys with i + window >= n_ctx get 0. window >= 0. The result is
+ * deterministic: the same inputs give the same bits on every call. */
 int kvscore_futuremass(const kvs_attn_desc* d, const kvs_bf16* Q,
                        const kvs_bf16* K, const float* lse, int64_t window,
                        const float* vnorm, const float* hnorm, float* target,

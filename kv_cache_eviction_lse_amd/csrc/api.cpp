@@ -175,7 +175,7 @@ KVS_API int kvscore_futuremass(const kvs_attn_desc* d, const kvs_bf16* Q, const 
   if (d->n_ctx > 0 && (!lse || !target)) return fail(KVS_EINVAL, "lse or target is NULL");
   int cus;
   if ((st = check_device(&cus))) return st;
-  return hip_status(kvs::launch_score_sum(*d, Q, K, lse, window, vnorm, hnorm, target,
+  return hip_status(kvs::launch_score_sum(*d, Q, K, lse, window, vnorm, hnorm, target, cus,
                                           static_cast<hipStream_t>(stream)),
                     "kvscore_futuremass");
 }

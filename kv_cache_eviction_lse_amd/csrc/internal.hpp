@@ -17,7 +17,7 @@ hipError_t launch_score_max(const kvs_attn_desc& d, const uint16_t* Q, const uin
 
 hipError_t launch_score_sum(const kvs_attn_desc& d, const uint16_t* Q, const uint16_t* K, const float* lse,
                             int64_t window, const float* vnorm, const float* hnorm, float* target,
-                            hipStream_t s);
+                            int num_cus, hipStream_t s);
 
 size_t evict_workspace_bytes(const kvs_evict_desc& e);
 

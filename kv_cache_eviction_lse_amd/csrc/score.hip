@@ -45,8 +45,8 @@ struct ScoreParams {
   int64_t window;  // sum mode
   int Hkv, G;
   int n_kblocks;   // key blocks per KV head
-  int nsplit;      // max mode: query-row splits per key block
-  int use_atomic;  // max mode: combine with atomicMax on the score bits
+  int nsplit;      // query-row splits per key block (max) or per key-block pair (sum, at most 2)
+  int use_atomic;  // combine splits: atomicMax on the score bits (max), atomicAdd (sum)
   float scale;
 };
 
@@ -87,13 +87,17 @@ __global__ __launch_bounds__(NW * WAVE) void score_kernel(ScoreParams p) {
   const int n_q = (int)p.n_q;
 
   // work items: max mode -> one key block and one query split;
-  // sum mode -> a pair of key blocks (kb, n_kblocks-1-kb), balancing the triangle.
+  // sum mode -> a pair of key blocks (kb, n_kblocks-1-kb), balancing the
+  // triangle, and one query split of each.
   int kb_list[2];
   int n_items = 1;
   int split = 0;
   if (SUM) {
-    kb_list[0] = rest;
-    kb_list[1] = p.n_kblocks - 1 - rest;
+    const int npairs = (p.n_kblocks + 1) / 2;
+    const int pair = rest % npairs;
+    split = rest / npairs;
+    kb_list[0] = pair;
+    kb_list[1] = p.n_kblocks - 1 - pair;
     n_items = (kb_list[1] != kb_list[0]) ? 2 : 1;
   } else {
     kb_list[0] = rest % p.n_kblocks;
@@ -126,23 +130,21 @@ __global__ __launch_bounds__(NW * WAVE) void score_kernel(ScoreParams p) {
     //   max: every row tile of every group head, split s takes an even share;
     //   sum: per group head, the row tiles from the first row any key of the
     //        block can count (j >= key0 + window) to the end.
+    // Split s of nsplit takes an even share of that list.
     const int n_jt_all = (n_q + TR - 1) / TR;
-    int jt_start = 0, jt_end = n_jt_all;
-    int t_count, gl, jt;
+    int jt_start = 0;
+    const int jt_end = n_jt_all;
     if (SUM) {
       const int64_t j_lo = key0 + p.window;
       jt_start = j_lo < p.n_q ? (int)(j_lo / TR) : n_jt_all;
-      t_count = (jt_end - jt_start) * p.G;
-      gl = 0;
-      jt = jt_start;
-    } else {
-      const int total = n_jt_all * p.G;
-      const int t0 = (int)((int64_t)total * split / p.nsplit);
-      const int t1 = (int)((int64_t)total * (split + 1) / p.nsplit);
-      t_count = t1 - t0;
-      gl = n_jt_all ? t0 / n_jt_all : 0;
-      jt = n_jt_all ? t0 - gl * n_jt_all : 0;
     }
+    const int n_jt = jt_end - jt_start;
+    const int total = n_jt * p.G;
+    const int t0 = (int)((int64_t)total * split / p.nsplit);
+    const int t1 = (int)((int64_t)total * (split + 1) / p.nsplit);
+    const int t_count = t1 - t0;
+    int gl = n_jt ? t0 / n_jt : 0;
+    int jt = jt_start + (n_jt ? t0 - gl * n_jt : 0);
 
     // Prefetch registers: raw Q pieces, and for the first TR threads the raw
     // lse and hnorm of one row. Loads are unconditional (rows past the end
@@ -279,7 +281,11 @@ __global__ __launch_bounds__(NW * WAVE) void score_kernel(ScoreParams p) {
         const float vn = p.vnorm ? p.vnorm[(int64_t)h * p.n_keys + key] : 1.0f;
         float* dst = p.out + (int64_t)h * p.n_keys + key;
         if (SUM) {
-          *dst = v * vn;
+          // two splits at most: (0 + x) + y == (0 + y) + x, so the sum is deterministic
+          if (p.use_atomic)
+            atomicAdd(dst, v * vn);
+          else
+            *dst = v * vn;
         } else {
           float val = __expf(p.scale * v) * vn;
           if (!(val > 0.f)) val = 0.f;  // -0, NaN -> +0 so the bit pattern orders like the value
@@ -367,7 +373,7 @@ hipError_t launch_score_max(const kvs_attn_desc& d, const uint16_t* Q, const uin
 
 hipError_t launch_score_sum(const kvs_attn_desc& d, const uint16_t* Q, const uint16_t* K, const float* lse,
                             int64_t window, const float* vnorm, const float* hnorm, float* target,
-                            hipStream_t s) {
+                            int num_cus, hipStream_t s) {
   const int64_t T = d.n_ctx;
   if (T == 0) return hipSuccess;
   ScoreParams p{};
@@ -377,10 +383,21 @@ hipError_t launch_score_sum(const kvs_attn_desc& d, const uint16_t* Q, const uin
   p.Hkv = d.n_kvheads; p.G = d.n_qheads / d.n_kvheads; p.scale = d.scale;
   constexpr int BK = SUM_NW * SUM_NT * 32;
   p.n_kblocks = (int)((T + BK - 1) / BK);
-  p.nsplit = 1;
-  p.use_atomic = 0;
   const int npairs = (p.n_kblocks + 1) / 2;
-  const int nblocks = npairs * p.Hkv;
+  // Fewer key-block pairs than CUs: split each pair's query rows in two and
+  // add the halves atomically into a zeroed target. Two addends onto zero
+  // round the same in either order, which keeps the result deterministic;
+  // more splits would not.
+  p.nsplit = ((int64_t)npairs * p.Hkv < num_cus && d.n_q >= 2 * SUM_RT * 32) ? 2 : 1;
+  p.use_atomic = p.nsplit > 1;
+  if (p.use_atomic) {
+    const int64_t n = (int64_t)p.Hkv * T;
+    hipLaunchKernelGGL(fill_zero, dim3((unsigned)((n + 255) / 256 < 1024 ? (n + 255) / 256 : 1024)), dim3(256), 0,
+                       s, target, n);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  const int nblocks = npairs * p.Hkv * p.nsplit;
   if (d.head_dim == 128) return run<128, SUM_NW, SUM_NT, SUM_RT, true>(p, nblocks, s);
   return run<64, SUM_NW, SUM_NT, SUM_RT, true>(p, nblocks, s);
 }

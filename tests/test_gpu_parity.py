@@ -178,6 +178,21 @@ def test_future_mass_conserves_mass_at_window_zero():
     assert np.allclose(tot, 4 * 3000, rtol=1e-4)
 
 
+def test_future_mass_is_deterministic():
+    """Few key blocks: the query rows of each block pair are split in two and
+    added atomically; repeated calls must still give identical bits."""
+    r = synth.Recipe(Hq=8, Hkv=2, D=128, n_ctx=4100, n_q=4100, mask="causal", value_norms=True)
+    d = synth.draw(r, 708)
+    Q, K = dev_bf16(d["Q"]), dev_bf16(d["Kctx"])
+    L = kvs.lse(Q, K, None, scale=d["scale"], mask="causal")
+    vn, hn = dev_f32(d["vnorm"]), dev_f32(d["hnorm"])
+    say("[sum] deterministic")
+    outs = [kvs.future_mass(Q, K, L, scale=d["scale"], window=128, vnorm=vn, hnorm=hn) for _ in range(3)]
+    torch.cuda.synchronize()
+    for o in outs[1:]:
+        assert torch.equal(outs[0].view(torch.int32), o.view(torch.int32))
+
+
 # ---------------------------------------------------------------- eviction
 
 def _evict_case(seed, Hkv, n, D, **kw):
