@@ -76,7 +76,8 @@ typedef uint16_t kvs_bf16; /* bfloat16 bit pattern */
  *   Kself  [n_kvheads, n_q, head_dim]   strides ks_head_stride, ks_tok_stride
  *          (REPEAT only: the keys of the repeated copy; row j is query j's)
  * Requirements: n_qheads % n_kvheads == 0; head_dim is 64 or 128; every
- * pointer and every stride keeps rows 16-byte aligned (strides multiple of 8).
+ * pointer and every stride keeps rows 16-byte aligned (strides multiple of 8);
+ * token strides are at least head_dim and at most 2^23 (KVS_EUNSUPPORTED).
  * chunk > 0 for REPEAT (the last chunk may be shorter); ignored for CAUSAL. */
 typedef struct kvs_attn_desc {
   int32_t n_qheads;

@@ -80,6 +80,9 @@ int hip_status(hipError_t e, const char* what) {
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 constexpr int64_t MAX_TOKENS = (int64_t)1 << 30;
+// Tiles are read through buffer resources with 32-bit offsets: 64 rows of
+// 2^23 elements span 2^30 bytes.
+constexpr int64_t MAX_TOK_STRIDE = (int64_t)1 << 23;
 
 // Checks shared by the three scoring calls. `need_self` for REPEAT LSE.
 int check_attn(const kvs_attn_desc* d, const kvs_bf16* Q, const kvs_bf16* K, const kvs_bf16* Kself,
@@ -106,6 +109,8 @@ int check_attn(const kvs_attn_desc* d, const kvs_bf16* Q, const kvs_bf16* K, con
     if (st[i] < 0) return fail(KVS_EINVAL, "negative stride");
     if (st[i] % 8) return fail(KVS_EUNSUPPORTED, "strides must be multiples of 8 elements (16 bytes)");
   }
+  if (d->q_tok_stride > MAX_TOK_STRIDE || d->k_tok_stride > MAX_TOK_STRIDE || d->ks_tok_stride > MAX_TOK_STRIDE)
+    return fail(KVS_EUNSUPPORTED, "token strides above 2^23 elements");
   if (d->n_q > 0 && d->q_tok_stride < d->head_dim)
     return fail(KVS_EINVAL, "q_tok_stride is smaller than head_dim");
   if (d->n_ctx > 0 && d->k_tok_stride < d->head_dim)

@@ -118,37 +118,36 @@ __global__ __launch_bounds__(LSE_WAVES * WAVE, 3) void lse_kernel(LseParams p) {
     }
   }
 
-  // tile tt -> first key position kt (segment-relative for context tiles,
-  // sequence position for self/causal tiles), source rows and key count
-  auto tile_src = [&](int tt, const uint16_t*& base, int64_t& ts, int64_t& k0, int64_t& kend) {
-    if (tt < n_ctx_tiles) {
-      base = p.K + (int64_t)h * p.k_hs;
-      ts = p.k_ts;
-      k0 = tt * 32;
-      kend = p.n_ctx;
-    } else {
-      base = CAUSAL ? p.K + (int64_t)h * p.k_hs : p.Kself + (int64_t)h * p.ks_hs;
-      ts = CAUSAL ? p.k_ts : p.ks_ts;
-      k0 = self_lo + (tt - n_ctx_tiles) * 32;
-      kend = pos_end;
-    }
-  };
-
-  // Key tiles: rows past the end of a segment load its last key; every such
-  // row is masked (ctx: key >= n_ctx; self/causal: key > j), so its value never
-  // counts. Loads are unconditional so issuing a prefetch never stalls.
-  u32x4 pre[CPT];
-  auto load_tile = [&](int tt) {
-    const uint16_t* base;
-    int64_t ts, k0, kend;
-    tile_src(tt, base, ts, k0, kend);
+  // Key tiles come in through buffer loads. A tile's resource starts at its
+  // first row and covers only the rows its segment has, so rows past the end
+  // read as zero; every such row is masked (ctx: key >= n_ctx; self/causal:
+  // key > j), so its value never counts. A thread's byte offsets within a
+  // tile are fixed, so a tile costs no per-thread address arithmetic. Token
+  // strides are at most 2^23 elements, so 32 rows span at most 2^29 bytes.
+  int voff_ctx[CPT], voff_self[CPT];
 #pragma unroll
-    for (int c = 0; c < CPT; ++c) {
-      const int idx = tid + c * NTHREADS;
-      const int rr = idx / CHUNKS_PER_ROW, part = idx % CHUNKS_PER_ROW;
-      const int64_t key = min(k0 + rr, kend - 1);
-      pre[c] = ld16(base + key * ts + part * 8);
-    }
+  for (int c = 0; c < CPT; ++c) {
+    const int idx = tid + c * NTHREADS;
+    const int rr = idx / CHUNKS_PER_ROW, part = idx % CHUNKS_PER_ROW;
+    voff_ctx[c] = (int)(rr * p.k_ts * 2 + part * 16);
+    voff_self[c] = (int)(rr * (CAUSAL ? p.k_ts : p.ks_ts) * 2 + part * 16);
+  }
+  u32x4 pre[CPT];
+  // (32-bit positions and scalar compares: every position is below 2^30)
+  const int n_ctx_tiles_s = (int)n_ctx_tiles, n_ctx_s = (int)p.n_ctx, pos_end_s = (int)pos_end;
+  const int self_lo_s = (int)self_lo, k_ts_s = (int)p.k_ts;
+  const int ks_ts_s = CAUSAL ? k_ts_s : (int)p.ks_ts;
+  const uint16_t* const ctx_base = p.K + (int64_t)h * p.k_hs;
+  const uint16_t* const self_base = CAUSAL ? ctx_base : p.Kself + (int64_t)h * p.ks_hs;
+  auto load_tile = [&](int tt) {
+    const bool ctx = tt < n_ctx_tiles_s;
+    const int k0 = ctx ? tt * 32 : self_lo_s + (tt - n_ctx_tiles_s) * 32;
+    const int kend = ctx ? n_ctx_s : pos_end_s;
+    const int ts = ctx ? k_ts_s : ks_ts_s;
+    const int rows = min(kend - k0, 32);
+    const __amdgpu_buffer_rsrc_t r = tile_rsrc((ctx ? ctx_base : self_base) + (int64_t)k0 * ts, rows * ts * 2);
+#pragma unroll
+    for (int c = 0; c < CPT; ++c) pre[c] = buf_ld16(r, ctx ? voff_ctx[c] : voff_self[c]);
   };
   auto store_tile = [&](int buf) {
 #pragma unroll

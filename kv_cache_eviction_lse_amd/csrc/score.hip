@@ -104,6 +104,15 @@ __global__ __launch_bounds__(NW * WAVE) void score_kernel(ScoreParams p) {
     split = rest / p.n_kblocks;
   }
 
+  // this thread's byte offsets within a query tile (rows of q_ts elements)
+  int voff[CPT];
+#pragma unroll
+  for (int c = 0; c < CPT; ++c) {
+    const int idx = tid + c * NTHREADS;
+    const int rr = idx / T::CHUNKS_PER_ROW, part = idx % T::CHUNKS_PER_ROW;
+    voff[c] = (int)(rr * p.q_ts * 2 + part * 16);
+  }
+
   for (int item = 0; item < n_items; ++item) {
     const int kb = kb_list[item];
     const int64_t key0 = (int64_t)kb * BK;
@@ -147,29 +156,32 @@ __global__ __launch_bounds__(NW * WAVE) void score_kernel(ScoreParams p) {
     int jt = jt_start + (n_jt ? t0 - gl * n_jt : 0);
 
     // Prefetch registers: raw Q pieces, and for the first TR threads the raw
-    // lse and hnorm of one row. Loads are unconditional (rows past the end
-    // read the last row) and the bias arithmetic waits until the store, so
-    // issuing a prefetch never stalls the wave. Rows past the end get bias
+    // lse and hnorm of one row. A tile is read through buffer resources that
+    // start at its first row and cover only the rows that exist, so rows past
+    // the end read as zero and a thread's byte offsets are fixed (token
+    // strides are at most 2^23 elements: a tile spans at most 2^30 bytes).
+    // Loads are unconditional and the bias arithmetic waits until the store,
+    // so issuing a prefetch never stalls the wave. Rows past the end get bias
     // -inf: they never win a max and add exp2(-inf) = 0 to a sum.
     u32x4 pre[CPT];
     float pre_lse = 0.f, pre_hn = 1.f;
     bool pre_ok = false;
     auto load_tile = [&](int tgl, int tjt) {
       const int g = h * p.G + tgl;
-      const uint16_t* qbase = p.Q + (int64_t)g * p.q_hs;
+      const int j0 = tjt * TR;
+      const int rows = min(n_q - j0, TR);
+      const __amdgpu_buffer_rsrc_t rq =
+          tile_rsrc(p.Q + (int64_t)g * p.q_hs + (int64_t)j0 * p.q_ts, rows * (int)p.q_ts * 2);
 #pragma unroll
-      for (int c = 0; c < CPT; ++c) {
-        const int idx = tid + c * NTHREADS;
-        const int rr = idx / T::CHUNKS_PER_ROW, part = idx % T::CHUNKS_PER_ROW;
-        const int j = min(tjt * TR + rr, n_q - 1);
-        pre[c] = ld16(qbase + (int64_t)j * p.q_ts + part * 8);
-      }
+      for (int c = 0; c < CPT; ++c) pre[c] = buf_ld16(rq, voff[c]);
       if (tid < TR) {
-        const int j = tjt * TR + tid;
-        pre_ok = j < n_q;
-        const int jc = min(j, n_q - 1);
-        pre_lse = p.lse[(int64_t)g * p.n_q + jc];
-        pre_hn = p.hnorm ? p.hnorm[jc] : 1.0f;
+        pre_ok = tid < rows;
+        const __amdgpu_buffer_rsrc_t rl = tile_rsrc(p.lse + (int64_t)g * p.n_q + j0, rows * 4);
+        pre_lse = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rl, tid * 4, 0, 0));
+        if (p.hnorm) {
+          const __amdgpu_buffer_rsrc_t rh = tile_rsrc(p.hnorm + j0, rows * 4);
+          pre_hn = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rh, tid * 4, 0, 0));
+        }
       }
     };
     auto store_tile = [&](int buf) {

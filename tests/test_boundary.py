@@ -104,6 +104,7 @@ ATTN_BAD = [
     (dict(scale=float("nan")), kvs.KVS_EINVAL),
     (dict(q_tok_stride=100), kvs.KVS_EUNSUPPORTED),
     (dict(k_tok_stride=64), kvs.KVS_EINVAL),
+    (dict(k_tok_stride=(1 << 23) + 8), kvs.KVS_EUNSUPPORTED),  # tile offsets are 32-bit
     (dict(reserved=1), kvs.KVS_EINVAL),
     (dict(mask=kvs.MASK_CAUSAL), kvs.KVS_EINVAL),  # CAUSAL needs n_q == n_ctx
     (dict(n_ctx=1 << 31), kvs.KVS_EUNSUPPORTED),
