@@ -16,6 +16,7 @@ from .reference import (  # noqa: F401
     kv_head_of,
     outside_window,
     lse,
+    attention,
     attention_weights,
     max_scores,
     future_mass,

@@ -120,6 +120,42 @@ def lse(Q, Kctx, Kself, scale, mask=REPEAT, chunk=0, rows=None):
     return out
 
 
+def attention(Q, Kctx, Kself, Vctx, Vself, scale, mask=REPEAT, chunk=0, rows=None):
+    """Attention output and normaliser, fp64: (O [Hq, m, D], LSE [Hq, m]) for
+    the m query positions in ``rows`` (all when None).
+
+    o_j = sum_i a_ji v_i over the keys visible to j, a_ji = exp(l_ji - LSE_j):
+    the per-head sum that [KVzap] §3.2 Eq. 2 adds to the residual stream
+    (there after W_O), and the output an attention kernel returns together
+    with LSE_j ([KVpop] §1). Values follow the columns of ``visible_logits``:
+    REPEAT sees the context values, then the self values of the query's
+    chunk; CAUSAL sees the values 0..n_ctx-1. Values share the key layout
+    ([Hkv, n, D], bf16 bits).
+    """
+    Hq, n_q, D, Hkv, G = _dims(Q, Kctx)
+    Qf, Kc, Vc = bf16_bits_to_f64(Q), bf16_bits_to_f64(Kctx), bf16_bits_to_f64(Vctx)
+    Ks = bf16_bits_to_f64(Kself) if Kself is not None else None
+    Vs = bf16_bits_to_f64(Vself) if Vself is not None else None
+    scale = float(np.float32(scale))
+    want = np.arange(n_q) if rows is None else np.asarray(rows, dtype=np.int64)
+    col_of = {int(j): c for c, j in enumerate(want)}
+    O = np.empty((Hq, want.size, D))
+    L_out = np.empty((Hq, want.size))
+    for g in range(Hq):
+        h = kv_head_of(g, G)
+        for blk, c0, c1 in _row_blocks(n_q, mask, chunk, want):
+            L = visible_logits(Qf[g, blk], blk, Kc[h], Ks[h] if Ks is not None else None,
+                               scale, mask, c0, c1)
+            vals = np.concatenate([Vc[h], Vs[h][c0:c1]], axis=0) if mask == REPEAT else Vc[h]
+            M = L.max(axis=1, keepdims=True)
+            E = np.exp(L - M)
+            tot = E.sum(axis=1, keepdims=True)
+            cols = [col_of[int(j)] for j in blk]
+            L_out[g, cols] = M[:, 0] + np.log(tot[:, 0])
+            O[g, cols] = (E / tot) @ vals
+    return O, L_out
+
+
 def attention_weights(Q, Kctx, Kself, scale, mask, chunk, g, j0, j1, lse_rows):
     """Softmax rows a_ji = exp(l_ji - LSE_j) for query head g, rows [j0, j1)
     (one chunk at most), over the same columns as ``visible_logits``."""

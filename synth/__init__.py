@@ -9,6 +9,8 @@ to bfloat16, and lays them out the way the library expects:
 * ``Kself``  bf16 bits, uint16 ``[Hkv, n_q, D]`` (the repeated copy's own keys;
   repeat workloads only)
 * ``V``      bf16 bits, uint16 ``[Hkv, n_ctx, D]``
+* ``Vself``  bf16 bits, uint16 ``[Hkv, n_q, D]`` (the repeated copy's own
+  values; repeat workloads with values only)
 * ``vnorm``  fp32 ``[Hkv, n_ctx]``: the norm of a random output-projection
   block applied to each value row (the weight of the value-norm-normalised
   score); an *input* of the scoring call, synthesised here
@@ -31,7 +33,7 @@ _lib = None
 
 # stream ids: each tensor draws from its own counter-based stream
 S_Q, S_QU, S_QB, S_K, S_KSELF, S_V, S_SINK, S_DUP, S_WO, S_HNORM = range(1, 11)
-S_LSE, S_SCORES, S_TIES, S_PERM = range(11, 15)
+S_LSE, S_SCORES, S_TIES, S_PERM, S_VSELF = range(11, 16)
 
 
 def build(verbose: bool = False) -> str:
@@ -228,6 +230,8 @@ def draw(recipe: Recipe, seed: int) -> dict:
 
     if r.mask == "repeat":
         out["Kself"] = normal_bf16(seed, S_KSELF, (r.Hkv, r.n_q, r.D))
+        if r.with_values:
+            out["Vself"] = normal_bf16(seed, S_VSELF, (r.Hkv, r.n_q, r.D))
 
     if r.value_norms:
         dh = r.d_hidden if r.d_hidden else r.Hq * r.D

@@ -88,6 +88,87 @@ def pin_lse_brute_force_logsumexp():
             assert abs(L[g, j] - want) < 1e-12, (mask, g, j)
 
 
+# ---------------------------------------------------------------- attention-output pins
+
+def _brute_visible_values(Vc, Vs, h, j, mask, chunk, n_q):
+    """The value rows query j sees, in the order of ``_brute_visible``'s keys."""
+    if mask == REPEAT:
+        c = chunk if chunk else n_q
+        c0 = (j // c) * c
+        return [Vc[h, i] for i in range(Vc.shape[1])] + [Vs[h, p] for p in range(c0, j + 1)]
+    return [Vc[h, i] for i in range(j + 1)]
+
+
+def _f64(bits):
+    return synth.bf16_to_f32(bits).astype(np.float64)
+
+
+def pin_attn_brute_force():
+    """O_j = sum_i exp(l_ji) v_i / sum_i exp(l_ji) and LSE_j, every visible key
+    enumerated one by one with exact sums."""
+    for mask, chunk, n_ctx, n_q in [(REPEAT, 3, 5, 7), (CAUSAL, 0, 6, 6)]:
+        d = _tiny(13, 4, 2, 64, n_ctx, n_q, mask, chunk, qstd=1.0)
+        Qf, Kc, Vc = _f64(d["Q"]), _f64(d["Kctx"]), _f64(d["V"])
+        Ks = _f64(d["Kself"]) if "Kself" in d else None
+        Vs = _f64(d["Vself"]) if "Vself" in d else None
+        O, L = oracle.attention(d["Q"], d["Kctx"], d.get("Kself"), d["V"], d.get("Vself"), 0.5, mask, chunk)
+        for g, j in itertools.product(range(4), range(n_q)):
+            h = g // 2
+            logits = _brute_visible(Qf, Kc, Ks, g, h, j, 0.5, mask, chunk, n_q)
+            m = max(logits)
+            w = [math.exp(x - m) for x in logits]
+            tot = math.fsum(w)
+            assert abs(L[g, j] - (m + math.log(tot))) < 1e-12, (mask, g, j)
+            vals = _brute_visible_values(Vc, Vs, h, j, mask, chunk, n_q)
+            for dd in range(Qf.shape[2]):
+                want = math.fsum(wi * float(v[dd]) for wi, v in zip(w, vals)) / tot
+                assert abs(O[g, j, dd] - want) < 1e-12, (mask, g, j, dd)
+
+
+def pin_attn_constant_values():
+    """Every value row equal to c: the weights sum to 1, so O_j = c."""
+    for mask, chunk in [(REPEAT, 4), (CAUSAL, 0)]:
+        d = _tiny(17, 6, 3, 64, 9 if mask == REPEAT else 10, 10, mask, chunk, qstd=1.0)
+        c = d["V"][0, 0].copy()
+        V = np.broadcast_to(c, d["V"].shape).copy()
+        Vs = np.broadcast_to(c, d["Vself"].shape).copy() if "Vself" in d else None
+        O, _ = oracle.attention(d["Q"], d["Kctx"], d.get("Kself"), V, Vs, 0.125, mask, chunk)
+        assert np.allclose(O, _f64(c)[None, None, :], rtol=1e-13, atol=1e-13), mask
+
+
+def pin_attn_zero_queries():
+    """Q = 0: all visible logits are equal, so O_j is the plain mean of the
+    value rows j sees (context rows plus its chunk's self rows up to j;
+    causal: rows 0..j)."""
+    Hq, Hkv, D, n_ctx, n_q, C = 4, 2, 64, 7, 9, 4
+    d = _tiny(19, Hq, Hkv, D, n_ctx, n_q, REPEAT, C)
+    Q = np.zeros_like(d["Q"])
+    O, _ = oracle.attention(Q, d["Kctx"], d["Kself"], d["V"], d["Vself"], 0.125, REPEAT, C)
+    Vc, Vs = _f64(d["V"]), _f64(d["Vself"])
+    for g, j in itertools.product(range(Hq), range(n_q)):
+        h, c0 = g // 2, (j // C) * C
+        want = (Vc[h].sum(axis=0) + Vs[h, c0:j + 1].sum(axis=0)) / (n_ctx + j - c0 + 1)
+        assert np.allclose(O[g, j], want, rtol=0, atol=1e-13), (g, j)
+    dc = _tiny(19, Hq, Hkv, D, n_q, n_q, CAUSAL, 0)
+    Oc, _ = oracle.attention(Q, dc["Kctx"], None, dc["V"], None, 0.125, CAUSAL, 0)
+    Vc = _f64(dc["V"])
+    for g, j in itertools.product(range(Hq), range(n_q)):
+        assert np.allclose(Oc[g, j], Vc[g // 2, :j + 1].mean(axis=0), rtol=0, atol=1e-13), (g, j)
+
+
+def pin_attn_linear_in_values():
+    """O is linear in V: O(V1 + V2) = O(V1) + O(V2) (small integers, so the
+    bf16 sums are exact)."""
+    d = _tiny(23, 4, 2, 64, 6, 8, REPEAT, 3, qstd=1.0)
+    rng = np.random.default_rng(5)
+    V1 = rng.integers(-8, 9, size=d["V"].shape).astype(np.float32)
+    V2 = rng.integers(-8, 9, size=d["V"].shape).astype(np.float32)
+    S1 = rng.integers(-8, 9, size=d["Vself"].shape).astype(np.float32)
+    S2 = rng.integers(-8, 9, size=d["Vself"].shape).astype(np.float32)
+    run = lambda V, S: oracle.attention(d["Q"], d["Kctx"], d["Kself"], _bits(V), _bits(S), 0.25, REPEAT, 3)[0]
+    assert np.allclose(run(V1 + V2, S1 + S2), run(V1, S1) + run(V2, S2), rtol=0, atol=1e-11)
+
+
 # ---------------------------------------------------------------- max-mode pins
 
 def pin_max_zero_queries():

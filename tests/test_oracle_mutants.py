@@ -17,7 +17,7 @@ MUTANTS = {
     "causal-diagonal-excluded": ("np.where(keys[None, :] <= rows[:, None], l, -np.inf)",
                                  "np.where(keys[None, :] < rows[:, None], l, -np.inf)"),
     "ctx-logit-unscaled": ("l_ctx = scale * (q_rows @ Kctx_h.T)", "l_ctx = (q_rows @ Kctx_h.T)"),
-    "lse-max-term-dropped": ("M[:, 0] + np.log(", "np.log("),
+    "lse-max-term-dropped": ("for j in blk]] = M[:, 0] + np.log(", "for j in blk]] = np.log("),
     "window-edge-exclusive": ("keys[None, :] + window <= rows[:, None]", "keys[None, :] + window < rows[:, None]"),
     "max-hnorm-dropped": ("w = a * vn[h][None, :] / hn[j0:j1, None]\n            s[h]",
                           "w = a * vn[h][None, :]\n            s[h]"),
@@ -29,6 +29,11 @@ MUTANTS = {
     "max-key-axis": ("s[h] = np.maximum(s[h], w.max(axis=0))", "s[h] = np.maximum(s[h], w.max(axis=1).max())"),
     "sum-group-overwrites": ("t[h] += w.sum(axis=0)", "t[h] = w.sum(axis=0)"),
     "sum-hnorm-multiplies": ("a * vn[h][None, :] / hn[j0:j1, None], 0.0)", "a * vn[h][None, :] * hn[j0:j1, None], 0.0)"),
+    "attn-unnormalised": ("O[g, cols] = (E / tot) @ vals", "O[g, cols] = E @ vals"),
+    "attn-self-values-reversed": ("vals = np.concatenate([Vc[h], Vs[h][c0:c1]], axis=0)",
+                                  "vals = np.concatenate([Vc[h], Vs[h][c0:c1][::-1]], axis=0)"),
+    "attn-causal-value-head": ("if mask == REPEAT else Vc[h]", "if mask == REPEAT else Vc[(h + 1) % Hkv]"),
+    "attn-lse-max-dropped": ("L_out[g, cols] = M[:, 0] + np.log(tot[:, 0])", "L_out[g, cols] = np.log(tot[:, 0])"),
     "window-not-kept": ("keep[n - w:] = True", "pass"),
     "threshold-strict": ("keep[cand] |= s[cand] >= float(np.float32(tau))", "keep[cand] |= s[cand] > float(np.float32(tau))"),
     "ties-higher-index-first": ("order = np.lexsort((cand, neg, is_nan))", "order = np.lexsort((-cand, neg, is_nan))"),
@@ -38,7 +43,7 @@ MUTANTS = {
                                 "offsets = np.concatenate([np.cumsum(counts), [0]])"),
 }
 
-EXPORTED = ["lse", "attention_weights", "max_scores", "future_mass", "select", "compact",
+EXPORTED = ["lse", "attention", "attention_weights", "max_scores", "future_mass", "select", "compact",
             "visible_logits", "kv_head_of", "outside_window"]
 
 
