@@ -102,6 +102,25 @@ typedef struct kvs_attn_desc {
 int kvscore_lse(const kvs_attn_desc* d, const kvs_bf16* Q, const kvs_bf16* K,
                 const kvs_bf16* Kself, float* lse, void* stream);
 
+/* Attention forward with its output (KVzap page §3.2 Eq. 2: the per-head
+ * sum sum_i a_ji v_i that enters the residual update, before W_O; the LSE
+ * it returns alongside is the normaliser the KVpop review §1 reuses):
+ *   O[g][j]   = sum_{i visible to j} exp(scale * q_j . k_i - lse[g][j]) * v_i
+ *   lse[g][j] = exactly what kvscore_lse computes (same visibility rules).
+ * V      [n_kvheads, n_ctx, head_dim] bf16, the values of K (K's strides);
+ * Vself  [n_kvheads, n_q, head_dim] bf16, the values of Kself (Kself's
+ *        strides; REPEAT only, may be NULL for CAUSAL);
+ * O      [n_qheads, n_q, head_dim] bf16 with Q's strides, overwritten
+ *        (fp32 accumulation, rounded once to bf16);
+ * lse    [n_qheads, n_q] fp32, dense, overwritten.
+ * The probabilities enter the value product rounded to bf16 (as in a
+ * bf16 flash-attention kernel); lse is computed in fp32 from the unrounded
+ * exponentials. */
+int kvscore_attention(const kvs_attn_desc* d, const kvs_bf16* Q,
+                      const kvs_bf16* K, const kvs_bf16* Kself,
+                      const kvs_bf16* V, const kvs_bf16* Vself,
+                      kvs_bf16* O, float* lse, void* stream);
+
 /* KVzip / KVzip+ max score (KVzap page §3.1 Eq. 1 and §3.2 Eq. 3), for the
  * context keys of a REPEAT layer; every repeat query sees every context key:
  *   s[h][i] = max_{g in group(h)} max_{j < n_q}

@@ -6,6 +6,7 @@ Torch supplies device memory and the current stream. The functions mirror
 the C ABI in ``include/kvscore.h``:
 
 * :func:`lse`          -> ``kvscore_lse``
+* :func:`attention`    -> ``kvscore_attention``
 * :func:`max_scores`   -> ``kvscore_max``
 * :func:`future_mass`  -> ``kvscore_futuremass``
 * :func:`evict`        -> ``kv_evict`` (+ ``kv_evict_workspace_bytes``)
@@ -29,7 +30,7 @@ KVS_OK, KVS_EINVAL, KVS_EUNSUPPORTED, KVS_ECAPACITY, KVS_EWORKSPACE, KVS_EHIP, K
 MASK_REPEAT, MASK_CAUSAL = 0, 1
 
 EXPORTED_SYMBOLS = (
-    "kvscore_lse", "kvscore_max", "kvscore_futuremass", "kv_evict_workspace_bytes", "kv_evict",
+    "kvscore_lse", "kvscore_attention", "kvscore_max", "kvscore_futuremass", "kv_evict_workspace_bytes", "kv_evict",
     "kvs_strerror", "kvs_last_error", "kvs_version",
 )
 
@@ -78,6 +79,7 @@ def lib() -> ctypes.CDLL:
     vp, i64, i32, c = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_int
     pA, pE = ctypes.POINTER(AttnDesc), ctypes.POINTER(EvictDesc)
     L.kvscore_lse.argtypes = [pA, vp, vp, vp, vp, vp]
+    L.kvscore_attention.argtypes = [pA, vp, vp, vp, vp, vp, vp, vp, vp]
     L.kvscore_max.argtypes = [pA, vp, vp, vp, vp, vp, vp, c, vp]
     L.kvscore_futuremass.argtypes = [pA, vp, vp, vp, i64, vp, vp, vp, vp]
     L.kv_evict_workspace_bytes.argtypes = [pE]
@@ -88,7 +90,7 @@ def lib() -> ctypes.CDLL:
     L.kvs_last_error.argtypes = []
     L.kvs_last_error.restype = ctypes.c_char_p
     L.kvs_version.restype = c
-    for name in ("kvscore_lse", "kvscore_max", "kvscore_futuremass", "kv_evict"):
+    for name in ("kvscore_lse", "kvscore_attention", "kvscore_max", "kvscore_futuremass", "kv_evict"):
         getattr(L, name).restype = c
     _lib = L
     return L
@@ -171,6 +173,32 @@ def lse(Q, K, Kself=None, *, scale: float, mask: str = "repeat", chunk: int = 0,
     _f32("out", out, (d.n_qheads, d.n_q))
     check(lib().kvscore_lse(ctypes.byref(d), _ptr(Q), _ptr(K), _ptr(Kself), _ptr(out), _stream(stream)))
     return out
+
+
+def attention(Q, K, V, Kself=None, Vself=None, *, scale: float, mask: str = "repeat", chunk: int = 0,
+              out=None, lse_out=None, stream=None):
+    """Attention output O (bf16, Q's shape and strides) and LSE [Hq, n_q] fp32
+    (``kvscore_attention``). V has K's shape and strides, Vself Kself's."""
+    torch = _torch()
+    _bf16("Q", Q), _bf16("K", K), _bf16("V", V)
+    if tuple(V.shape) != tuple(K.shape) or V.stride() != K.stride():
+        raise ValueError("V must have K's shape and strides")
+    if mask == "repeat":
+        _bf16("Kself", Kself), _bf16("Vself", Vself)
+        if tuple(Vself.shape) != tuple(Kself.shape) or Vself.stride() != Kself.stride():
+            raise ValueError("Vself must have Kself's shape and strides")
+    d = attn_desc(Q, K, Kself, scale, mask, chunk)
+    if out is None:
+        out = torch.empty_like(Q)
+    _bf16("out", out)
+    if tuple(out.shape) != tuple(Q.shape) or out.stride() != Q.stride():
+        raise ValueError("out must have Q's shape and strides")
+    if lse_out is None:
+        lse_out = torch.empty((d.n_qheads, d.n_q), dtype=torch.float32, device=Q.device)
+    _f32("lse_out", lse_out, (d.n_qheads, d.n_q))
+    check(lib().kvscore_attention(ctypes.byref(d), _ptr(Q), _ptr(K), _ptr(Kself), _ptr(V), _ptr(Vself),
+                                  _ptr(out), _ptr(lse_out), _stream(stream)))
+    return out, lse_out
 
 
 def max_scores(Q, K, lse_vals, *, scale: float, vnorm=None, hnorm=None, out=None, accumulate: bool = False,

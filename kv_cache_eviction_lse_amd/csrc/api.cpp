@@ -155,6 +155,22 @@ KVS_API int kvscore_lse(const kvs_attn_desc* d, const kvs_bf16* Q, const kvs_bf1
   return hip_status(kvs::launch_lse(*d, Q, K, Kself, lse, static_cast<hipStream_t>(stream)), "kvscore_lse");
 }
 
+KVS_API int kvscore_attention(const kvs_attn_desc* d, const kvs_bf16* Q, const kvs_bf16* K, const kvs_bf16* Kself,
+                              const kvs_bf16* V, const kvs_bf16* Vself, kvs_bf16* O, float* lse, void* stream) {
+  const bool repeat = d && d->mask == KVS_MASK_REPEAT;
+  int st = check_attn(d, Q, K, Kself, repeat);
+  if (st) return st;
+  if (d->n_q > 0 && (!lse || !O)) return fail(KVS_EINVAL, "O or lse is NULL");
+  if (d->n_ctx > 0 && !V) return fail(KVS_EINVAL, "V is NULL");
+  if (repeat && d->n_q > 0 && !Vself) return fail(KVS_EINVAL, "Vself is NULL (REPEAT)");
+  if (!aligned16(V) || !aligned16(Vself) || !aligned16(O))
+    return fail(KVS_EUNSUPPORTED, "V, Vself and O must be 16-byte aligned");
+  int cus;
+  if ((st = check_device(&cus))) return st;
+  return hip_status(kvs::launch_attn(*d, Q, K, Kself, V, Vself, O, lse, static_cast<hipStream_t>(stream)),
+                    "kvscore_attention");
+}
+
 KVS_API int kvscore_max(const kvs_attn_desc* d, const kvs_bf16* Q, const kvs_bf16* K, const float* lse,
                         const float* vnorm, const float* hnorm, float* scores, int accumulate, void* stream) {
   int st = check_attn(d, Q, K, nullptr, false);

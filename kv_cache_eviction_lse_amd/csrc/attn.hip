@@ -1,0 +1,335 @@
+// Attention forward that returns the output rows and the normalisers:
+//   O_j = sum_{i visible to j} a_ji v_i,  LSE_j = ln sum_{i visible to j} exp(l_ji),
+//   a_ji = exp(l_ji - LSE_j), l_ji = scale * q_j . k_i.
+// O_j is the per-head sum that enters the residual update (Eq. 2 of
+// "KVzap: Fast, Adaptive, and Faithful KV Cache Pruning", §3.2, before W_O);
+// LSE_j is what the transposed scoring pass reuses ("[논문리뷰] KVpop ..." §1).
+// Visibility is the LSE pass's: REPEAT (context keys, then the self keys of
+// the query's chunk up to its position) or CAUSAL.
+//
+// Layout of the work:
+//   * a workgroup has 8 waves, each owning one query subtile (32 positions of
+//     one query head); subtiles are ordered position-major, so the heads of a
+//     GQA group at the same positions share every key and value tile;
+//   * key tiles of 32 rows go through LDS as the A operand of S = K Q^T (keys
+//     as rows, queries as columns), exactly as in the LSE pass; each lane's
+//     16 accumulators are 16 keys of one query;
+//   * the exponentials P (against a per-query offset) are packed to bf16 and
+//     are, without any data movement, the B operand of O^T += V^T P^T: the
+//     16 keys a lane holds are the 2 x 8 contraction elements it supplies;
+//   * value tiles are stored transposed in LDS (rows = head dimension), so
+//     the A operand V^T is two 8-byte reads per 16 keys;
+//   * O^T accumulates in registers: a lane holds one query and D/2 of its
+//     output elements; it never leaves the chip until the final scaling by
+//     1 / sum P, which is per lane.
+//   * The offset o (exp2 domain) is shared by the two half-waves of a query,
+//     because their P values meet in one MFMA. It moves lazily: a tile is
+//     exponentiated against the stored o, and only when some lane's partial
+//     sum grows large (or overflows, on the first visible tile) does the
+//     whole wave raise o to its new row maxima and rescale l and O.
+#include "common.hpp"
+#include "internal.hpp"
+
+// Offsets are stored values used as is; no implicit contraction, so an
+// unchanged offset rescales by exactly 1.
+#pragma clang fp contract(off)
+
+namespace kvs {
+namespace {
+
+struct AttnParams {
+  const uint16_t* Q;
+  const uint16_t* K;       // context keys (REPEAT) or the sequence's keys (CAUSAL)
+  const uint16_t* Kself;   // REPEAT self keys
+  const uint16_t* V;       // values of K (same strides as K)
+  const uint16_t* Vself;   // values of Kself (same strides as Kself)
+  uint16_t* O;             // [Hq, n_q, D], strides of Q
+  float* lse;              // [Hq, n_q]
+  int64_t q_hs, q_ts, k_hs, k_ts, ks_hs, ks_ts;
+  int64_t n_ctx, n_q, chunk;
+  int Hkv, G;
+  int n_sub;  // subtiles per KV head = ceil(n_q / 32) * G
+  float scale;
+};
+
+constexpr int AT_WAVES = 8;
+constexpr int AT_THREADS = AT_WAVES * WAVE;
+constexpr float AT_LAZY = 1048576.0f;  // 2^20: raise the offset when a lane's tile sum exceeds this
+
+template <int D>
+struct ATile {
+  static constexpr int STEPS = D / 16;         // k-steps of the QK^T chain
+  static constexpr int K_STRIDE = D * 2 + 16;  // padded key rows, bytes
+  static constexpr int K_BYTES = 32 * K_STRIDE;
+  static constexpr int VT_STRIDE = 72;         // transposed value rows: 32 keys * 2 B + 8 B pad
+  static constexpr int V_BYTES = D * VT_STRIDE;
+  static constexpr int STAGE = K_BYTES + V_BYTES;
+  static constexpr int DB = D / 32;            // output row blocks of O^T
+  static constexpr int CHUNKS = 32 * D / 8;    // 16-byte pieces per tile, per tensor
+  static constexpr int CPR = D / 8;            // pieces per row
+  static constexpr int CPT = 2 * CHUNKS / AT_THREADS;  // pieces per thread (K and V together)
+};
+
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ bf16x8 pack_bf16(const f32x16& x, int base) {
+  bf16x8 r;
+#pragma unroll
+  for (int t = 0; t < 8; ++t) r[t] = (__bf16)x[base + t];
+  return r;
+}
+
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(AT_THREADS, 1) void attn_kernel(AttnParams p) {
+  using T = ATile<D>;
+  static_assert((2 * T::CHUNKS) % AT_THREADS == 0 && T::CHUNKS % WAVE == 0,
+                "tile pieces must split evenly over the threads, K and V by whole waves");
+  __shared__ __attribute__((aligned(16))) char s_tile[2][T::STAGE];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int half = lane >> 5;
+  const int col = lane & 31;
+
+  const int b = blockIdx.x;
+  const int h = b % p.Hkv;
+  const int bx = b / p.Hkv;
+  const int u_lo = bx * AT_WAVES;
+  const int u_hi = min(u_lo + AT_WAVES, p.n_sub) - 1;
+
+  const int64_t pos_lo = (int64_t)(u_lo / p.G) * 32;
+  const int64_t pos_end = min((int64_t)(u_hi / p.G) * 32 + 32, p.n_q);
+  const int64_t chunk = CAUSAL ? 1 : p.chunk;
+  const int64_t self_lo = CAUSAL ? 0 : (pos_lo / chunk) * chunk;
+  const int n_ctx_tiles = CAUSAL ? 0 : (int)((p.n_ctx + 31) / 32);
+  const int n_tiles = n_ctx_tiles + (int)((pos_end - self_lo + 31) / 32);
+
+  // ---- this wave's subtile: resident queries (B operands of S = K Q^T)
+  const int u = u_lo + wave;
+  const bool sub_ok = u < p.n_sub;
+  const int g = h * p.G + (sub_ok ? u % p.G : 0);
+  const int pj = sub_ok ? (u / p.G) * 32 : 0;  // first position of the subtile
+  bf16x8 qreg[T::STEPS];
+  {
+    const int64_t j = min((int64_t)pj + col, p.n_q - 1);
+    const uint16_t* qp = p.Q + (int64_t)g * p.q_hs + j * p.q_ts + half * (D / 2);
+#pragma unroll
+    for (int s = 0; s < T::STEPS; ++s) {
+      u32x4 v = ld16(qp + 8 * s);
+      pin(v);
+      qreg[s] = as_bf16x8(v);
+    }
+  }
+
+  // ---- tile loads: K and V rows through buffer resources that cover only
+  // the rows a segment has (rows past the end read as zero and are masked)
+  const int n_ctx_s = (int)p.n_ctx, pos_end_s = (int)pos_end, self_lo_s = (int)self_lo;
+  const int k_ts_s = (int)p.k_ts, ks_ts_s = CAUSAL ? k_ts_s : (int)p.ks_ts;
+  const int64_t kh = (int64_t)h * p.k_hs, ksh = CAUSAL ? kh : (int64_t)h * p.ks_hs;
+  u32x4 pre[T::CPT];
+  auto load_tile = [&](int tt) {
+    const bool ctx = tt < n_ctx_tiles;
+    const int k0 = ctx ? tt * 32 : self_lo_s + (tt - n_ctx_tiles) * 32;
+    const int kend = ctx ? n_ctx_s : pos_end_s;
+    const int ts = ctx ? k_ts_s : ks_ts_s;
+    const int rows = min(kend - k0, 32);
+    const int64_t off = (ctx ? kh : ksh) + (int64_t)k0 * ts;
+    const __amdgpu_buffer_rsrc_t rk = tile_rsrc((ctx || CAUSAL ? p.K : p.Kself) + off, rows * ts * 2);
+    const __amdgpu_buffer_rsrc_t rv = tile_rsrc((ctx || CAUSAL ? p.V : p.Vself) + off, rows * ts * 2);
+#pragma unroll
+    for (int c = 0; c < T::CPT; ++c) {
+      const int idx = tid + c * AT_THREADS;
+      // K or V is decided per wave (CHUNKS is a multiple of the wave size), so
+      // the resource stays wave-uniform
+      const bool is_v = wave * WAVE + c * AT_THREADS >= T::CHUNKS;
+      const int pc = is_v ? idx - T::CHUNKS : idx;
+      const int rr = pc / T::CPR, part = pc % T::CPR;
+      pre[c] = buf_ld16(is_v ? rv : rk, rr * ts * 2 + part * 16);
+    }
+  };
+  // K rows as they are (padded); V transposed: element (key rr, dim 8*part+t)
+  // goes to row 8*part+t, column rr of the value stage.
+  auto store_tile = [&](int buf) {
+    char* st = s_tile[buf];
+#pragma unroll
+    for (int c = 0; c < T::CPT; ++c) {
+      const int idx = tid + c * AT_THREADS;
+      const bool is_v = wave * WAVE + c * AT_THREADS >= T::CHUNKS;
+      const int pc = is_v ? idx - T::CHUNKS : idx;
+      const int rr = pc / T::CPR, part = pc % T::CPR;
+      if (!is_v) {
+        *reinterpret_cast<u32x4*>(st + rr * T::K_STRIDE + part * 16) = pre[c];
+      } else {
+        char* vt = st + T::K_BYTES + (8 * part) * T::VT_STRIDE + rr * 2;
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          const uint32_t w = pre[c][t];
+          *reinterpret_cast<uint16_t*>(vt + (2 * t) * T::VT_STRIDE) = (uint16_t)(w & 0xffffu);
+          *reinterpret_cast<uint16_t*>(vt + (2 * t + 1) * T::VT_STRIDE) = (uint16_t)(w >> 16);
+        }
+      }
+    }
+  };
+
+  // ---- running state: shared offset o (exp2 domain), this lane's partial
+  // sum l over the keys its half holds, and O^T
+  const float c2 = p.scale * LOG2E;
+  float o_run = -3.402823466e38f, l_run = 0.f;
+  f32x16 oacc[T::DB];
+#pragma unroll
+  for (int db = 0; db < T::DB; ++db) oacc[db] = f32x16{};
+  const int lane_j = pj + col;
+  const int lane_cs = CAUSAL ? 0 : (int)((lane_j / chunk) * chunk);
+  const int sub_cs_first = CAUSAL ? 0 : (int)((pj / chunk) * chunk);
+  const int sub_cs_last = CAUSAL ? 0 : (int)(((pj + 31) / chunk) * chunk);
+  const int n_ctx_full_tiles = CAUSAL ? 0 : n_ctx_s / 32;
+
+  auto exp_tile = [&](const f32x16& x, float o, f32x16& e) {
+    float s = 0.f;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      e[r] = fast_exp2(__builtin_fmaf(x[r], c2, -o));
+      s += e[r];
+    }
+    return s;
+  };
+
+  // One tile for this wave's subtile: S, P, lazy offset, O^T += V^T P^T.
+  auto tile = [&](int tt, int buf, bool masked, int k0, int kend, bool is_ctx) {
+    const char* st = s_tile[buf];
+    bf16x8 a[T::STEPS];
+    const char* krow = st + col * T::K_STRIDE + half * D;
+#pragma unroll
+    for (int s = 0; s < T::STEPS; ++s) a[s] = as_bf16x8(*reinterpret_cast<const u32x4*>(krow + 16 * s));
+    f32x16 x = mfma32(a[0], qreg[0], f32x16{});
+#pragma unroll
+    for (int s = 1; s < T::STEPS; ++s) x = mfma32(a[s], qreg[s], x);
+    if (masked) {
+      const int kb = k0 + 4 * half;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int key = kb + 8 * (r >> 2) + (r & 3);
+        const bool vis = is_ctx ? (key < kend) : (key <= lane_j && key >= lane_cs);
+        x[r] = vis ? x[r] : -INFINITY;
+      }
+    }
+    f32x16 e;
+    float sum = exp_tile(x, o_run, e);
+    // wave-uniform: raise the shared offset when any lane's sum is large
+    if (__builtin_amdgcn_ballot_w64(!(sum <= AT_LAZY))) {
+      float tm = x[0];
+#pragma unroll
+      for (int r = 1; r < 16; ++r) tm = fmaxf(tm, x[r]);
+      tm = fmaxf(tm, __shfl_xor(tm, 32));
+      const float o_new = fmaxf(o_run, tm * c2);
+      const float f = fast_exp2(o_run - o_new);
+      l_run *= f;
+#pragma unroll
+      for (int db = 0; db < T::DB; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) oacc[db][r] *= f;
+      o_run = o_new;
+      sum = exp_tile(x, o_run, e);
+    }
+    l_run += sum;
+    const bf16x8 pb0 = pack_bf16(e, 0), pb1 = pack_bf16(e, 8);
+    const char* vrow = st + T::K_BYTES + col * T::VT_STRIDE + half * 8;
+#pragma unroll
+    for (int db = 0; db < T::DB; ++db) {
+      const char* vr = vrow + 32 * db * T::VT_STRIDE;
+      bf16x8 v0, v1;
+      {
+        const bf16x4 lo = *reinterpret_cast<const bf16x4*>(vr);
+        const bf16x4 hi = *reinterpret_cast<const bf16x4*>(vr + 16);
+        v0 = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+      }
+      {
+        const bf16x4 lo = *reinterpret_cast<const bf16x4*>(vr + 32);
+        const bf16x4 hi = *reinterpret_cast<const bf16x4*>(vr + 48);
+        v1 = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+      }
+      oacc[db] = mfma32(v0, pb0, oacc[db]);
+      oacc[db] = mfma32(v1, pb1, oacc[db]);
+    }
+    (void)tt;
+  };
+
+  if (n_tiles > 0) {
+    load_tile(0);
+    store_tile(0);
+  }
+  __syncthreads();
+
+  for (int tt = 0; tt < n_tiles; ++tt) {
+    const int cur = tt & 1;
+    if (tt + 1 < n_tiles) load_tile(tt + 1);
+    if (sub_ok) {
+      const bool is_ctx = tt < n_ctx_tiles;
+      const int k0 = is_ctx ? tt * 32 : self_lo_s + (tt - n_ctx_tiles) * 32;
+      const int kend = is_ctx ? n_ctx_s : pos_end_s;
+      if (tt < n_ctx_full_tiles) {
+        tile(tt, cur, false, k0, kend, true);
+      } else {
+        bool run, full;
+        if (is_ctx) {
+          run = true;
+          full = k0 + 31 < kend;
+        } else {
+          run = !((k0 > pj + 31) || (k0 + 31 < sub_cs_first));
+          full = (k0 + 31 <= pj) && (k0 >= sub_cs_last) && (k0 + 31 < kend);
+        }
+        if (run) tile(tt, cur, !full, k0, kend, is_ctx);
+      }
+    }
+    if (tt + 1 < n_tiles) store_tile(cur ^ 1);
+    __syncthreads();
+  }
+
+  // ---- finish: merge the halves' partial sums, write LSE and O = O^T / l
+  const float l_tot = l_run + __shfl_xor(l_run, 32);
+  const int64_t j = (int64_t)lane_j;
+  if (sub_ok && j < p.n_q) {
+    if (half == 0) p.lse[(int64_t)g * p.n_q + j] = (o_run + __log2f(l_tot)) * LN2;
+    const float inv = 1.0f / l_tot;
+    uint16_t* orow = p.O + (int64_t)g * p.q_hs + j * p.q_ts;
+#pragma unroll
+    for (int db = 0; db < T::DB; ++db) {
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        bf16x4 v;
+#pragma unroll
+        for (int t = 0; t < 4; ++t) v[t] = (__bf16)(oacc[db][4 * q4 + t] * inv);
+        *reinterpret_cast<bf16x4*>(orow + 32 * db + 8 * q4 + 4 * half) = v;
+      }
+    }
+  }
+}
+
+template <int D, bool CAUSAL>
+hipError_t run(const AttnParams& p, int nblocks, hipStream_t s) {
+  hipLaunchKernelGGL((attn_kernel<D, CAUSAL>), dim3(nblocks), dim3(AT_THREADS), 0, s, p);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_attn(const kvs_attn_desc& d, const uint16_t* Q, const uint16_t* K, const uint16_t* Kself,
+                       const uint16_t* V, const uint16_t* Vself, uint16_t* O, float* lse, hipStream_t s) {
+  if (d.n_q == 0) return hipSuccess;
+  AttnParams p{};
+  p.Q = Q; p.K = K; p.Kself = Kself; p.V = V; p.Vself = Vself; p.O = O; p.lse = lse;
+  p.q_hs = d.q_head_stride; p.q_ts = d.q_tok_stride;
+  p.k_hs = d.k_head_stride; p.k_ts = d.k_tok_stride;
+  p.ks_hs = d.ks_head_stride; p.ks_ts = d.ks_tok_stride;
+  p.n_ctx = d.n_ctx; p.n_q = d.n_q; p.chunk = d.chunk;
+  p.Hkv = d.n_kvheads; p.G = d.n_qheads / d.n_kvheads; p.scale = d.scale;
+  const int64_t n_sub = ((d.n_q + 31) / 32) * p.G;
+  p.n_sub = (int)n_sub;
+  const int64_t nblocks = ((n_sub + AT_WAVES - 1) / AT_WAVES) * p.Hkv;
+  const bool causal = d.mask == KVS_MASK_CAUSAL;
+  if (d.head_dim == 128) return causal ? run<128, true>(p, (int)nblocks, s) : run<128, false>(p, (int)nblocks, s);
+  return causal ? run<64, true>(p, (int)nblocks, s) : run<64, false>(p, (int)nblocks, s);
+}
+
+}  // namespace kvs

@@ -5,6 +5,11 @@ Tolerances (fp32 kernels against the fp64 oracle):
   scores: |gpu - ref| / ref <= 5e-3 where ref >= 1e-6, else |gpu - ref| <= 1e-8
   kept sets: identical, except keys whose oracle score is within 5e-3 (relative)
   of the k-th score or of tau; compacted rows are bit copies.
+  attention output O (bf16): |gpu - ref| <= 2^-8 |ref| + 2^-7 sum_i a_ji |v_id|.
+    The probabilities enter the value product rounded to bf16 (relative error
+    <= 2^-8 each, so <= 2^-8 sum a|v| in total), fp32 accumulation adds far
+    less than another 2^-8 sum a|v|, and the final rounding of O to bf16 is
+    <= 2^-8 |O|. sum_i a_ji |v_id| is the oracle's output for |V|.
 """
 from __future__ import annotations
 
@@ -91,3 +96,26 @@ def check_rows(K_bits, V_bits, gpu_kept, K_out, V_out, offs, what=""):
         a, b = offs[h], offs[h + 1]
         assert np.array_equal(K_out[a:b], K_bits[h, idx]), f"{what}: K rows differ on head {h}"
         assert np.array_equal(V_out[a:b], V_bits[h, idx]), f"{what}: V rows differ on head {h}"
+
+
+def bf16_abs(bits: np.ndarray) -> np.ndarray:
+    """|x| of bf16 bit patterns (clears the sign bit; exact)."""
+    return (np.asarray(bits, dtype=np.uint16) & np.uint16(0x7FFF)).astype(np.uint16)
+
+
+def bf16_to_f64(bits: np.ndarray) -> np.ndarray:
+    b = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)
+    return b.view(np.float32).astype(np.float64)
+
+
+def check_attn_out(gpu_bits: np.ndarray, ref: np.ndarray, ref_abs: np.ndarray, what=""):
+    """O parity: gpu_bits bf16 [.., D]; ref = oracle O; ref_abs = oracle O for |V|."""
+    g = bf16_to_f64(gpu_bits)
+    assert np.all(np.isfinite(g)), f"{what}: non-finite O"
+    err = np.abs(g - ref)
+    tol = 2.0 ** -8 * np.abs(ref) + 2.0 ** -7 * ref_abs
+    ratio = err / np.maximum(tol, 1e-30)
+    assert np.all(err <= tol), (f"{what}: O error {err.max():.3e} exceeds its bound "
+                                f"(worst ratio {ratio.max():.2f} at {np.unravel_index(ratio.argmax(), ratio.shape)})")
+    return float(ratio.max())
+

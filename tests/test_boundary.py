@@ -127,6 +127,25 @@ def test_null_and_misaligned_pointers(L):
     assert L.kvscore_lse(ctypes.byref(d), ctypes.c_void_p(0x100008), FAKE, FAKE, FAKE, None) == kvs.KVS_EUNSUPPORTED
 
 
+@pytest.mark.parametrize("kw,code", ATTN_BAD)
+def test_attention_rejects_bad_desc(L, kw, code):
+    d = _desc(**kw)
+    assert L.kvscore_attention(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None) == code
+
+
+def test_attention_rejects_pointers(L):
+    d = _desc()
+    A = L.kvscore_attention
+    assert A(ctypes.byref(d), FAKE, FAKE, FAKE, None, FAKE, FAKE, FAKE, None) == kvs.KVS_EINVAL  # V
+    assert A(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE, None) == kvs.KVS_EINVAL  # Vself (REPEAT)
+    assert A(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, None) == kvs.KVS_EINVAL  # O
+    assert A(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, None) == kvs.KVS_EINVAL  # lse
+    assert A(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, ctypes.c_void_p(0x100008), FAKE,
+             None) == kvs.KVS_EUNSUPPORTED
+    assert A(ctypes.byref(d), FAKE, FAKE, FAKE, ctypes.c_void_p(0x100004), FAKE, FAKE, FAKE,
+             None) == kvs.KVS_EUNSUPPORTED
+
+
 def test_max_and_futuremass_reject(L):
     d = _desc()
     assert L.kvscore_max(ctypes.byref(d), FAKE, FAKE, FAKE, None, None, FAKE, 2, None) == kvs.KVS_EINVAL
