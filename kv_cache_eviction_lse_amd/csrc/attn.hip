@@ -67,7 +67,8 @@ struct ATile {
   static constexpr int DB = D / 32;            // output row blocks of O^T
   static constexpr int CHUNKS = 32 * D / 8;    // 16-byte pieces per tile, per tensor
   static constexpr int CPR = D / 8;            // pieces per row
-  static constexpr int CPT = 2 * CHUNKS / AT_THREADS;  // pieces per thread (K and V together)
+  static constexpr int KPT = CHUNKS / (AT_THREADS / 2);  // K pieces per K-loading thread
+  static constexpr int VUNITS = 16 * CPR;      // (key pair, piece) units of a V tile
 };
 
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
@@ -82,8 +83,8 @@ __device__ __forceinline__ bf16x8 pack_bf16(const f32x16& x, int base) {
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(AT_THREADS, 1) void attn_kernel(AttnParams p) {
   using T = ATile<D>;
-  static_assert((2 * T::CHUNKS) % AT_THREADS == 0 && T::CHUNKS % WAVE == 0,
-                "tile pieces must split evenly over the threads, K and V by whole waves");
+  static_assert(T::CHUNKS % (AT_THREADS / 2) == 0 && T::KPT <= 2 && T::VUNITS <= AT_THREADS / 2,
+                "K pieces must split evenly over half the workgroup, V pairs fit the other half");
   __shared__ __attribute__((aligned(16))) char s_tile[2][T::STAGE];
 
   const int tid = threadIdx.x;
@@ -127,7 +128,12 @@ __global__ __launch_bounds__(AT_THREADS, 1) void attn_kernel(AttnParams p) {
   const int n_ctx_s = (int)p.n_ctx, pos_end_s = (int)pos_end, self_lo_s = (int)self_lo;
   const int k_ts_s = (int)p.k_ts, ks_ts_s = CAUSAL ? k_ts_s : (int)p.ks_ts;
   const int64_t kh = (int64_t)h * p.k_hs, ksh = CAUSAL ? kh : (int64_t)h * p.ks_hs;
-  u32x4 pre[T::CPT];
+  // Waves 0..3 load K tiles (CHUNKS / 256 pieces each); waves 4..7 load V
+  // tiles as pairs of adjacent key rows (one 16-byte piece of keys 2m and
+  // 2m+1 per thread), which they store transposed as 32-bit key pairs.
+  const bool k_loader = wave < AT_WAVES / 2;
+  const int lt = tid & (AT_THREADS / 2 - 1);  // thread index within its half of the workgroup
+  u32x4 pre[2];
   auto load_tile = [&](int tt) {
     const bool ctx = tt < n_ctx_tiles;
     const int k0 = ctx ? tt * 32 : self_lo_s + (tt - n_ctx_tiles) * 32;
@@ -135,39 +141,39 @@ __global__ __launch_bounds__(AT_THREADS, 1) void attn_kernel(AttnParams p) {
     const int ts = ctx ? k_ts_s : ks_ts_s;
     const int rows = min(kend - k0, 32);
     const int64_t off = (ctx ? kh : ksh) + (int64_t)k0 * ts;
-    const __amdgpu_buffer_rsrc_t rk = tile_rsrc((ctx || CAUSAL ? p.K : p.Kself) + off, rows * ts * 2);
-    const __amdgpu_buffer_rsrc_t rv = tile_rsrc((ctx || CAUSAL ? p.V : p.Vself) + off, rows * ts * 2);
+    if (k_loader) {
+      const __amdgpu_buffer_rsrc_t rk = tile_rsrc((ctx || CAUSAL ? p.K : p.Kself) + off, rows * ts * 2);
 #pragma unroll
-    for (int c = 0; c < T::CPT; ++c) {
-      const int idx = tid + c * AT_THREADS;
-      // K or V is decided per wave (CHUNKS is a multiple of the wave size), so
-      // the resource stays wave-uniform
-      const bool is_v = wave * WAVE + c * AT_THREADS >= T::CHUNKS;
-      const int pc = is_v ? idx - T::CHUNKS : idx;
-      const int rr = pc / T::CPR, part = pc % T::CPR;
-      pre[c] = buf_ld16(is_v ? rv : rk, rr * ts * 2 + part * 16);
+      for (int c = 0; c < T::KPT; ++c) {
+        const int idx = lt + c * (AT_THREADS / 2);
+        pre[c] = buf_ld16(rk, (idx / T::CPR) * ts * 2 + (idx % T::CPR) * 16);
+      }
+    } else if (lt < T::VUNITS) {
+      const __amdgpu_buffer_rsrc_t rv = tile_rsrc((ctx || CAUSAL ? p.V : p.Vself) + off, rows * ts * 2);
+      const int m = lt & 15, part = lt >> 4;
+      pre[0] = buf_ld16(rv, (2 * m) * ts * 2 + part * 16);
+      pre[1] = buf_ld16(rv, (2 * m + 1) * ts * 2 + part * 16);
     }
   };
-  // K rows as they are (padded); V transposed: element (key rr, dim 8*part+t)
-  // goes to row 8*part+t, column rr of the value stage.
+  // K rows as they are (padded). V transposed: elements (2m, d) and (2m+1, d)
+  // form one 32-bit word of value row d at column pair m; a half-wave's
+  // stores hit 32 distinct banks with the 72-byte row stride.
   auto store_tile = [&](int buf) {
     char* st = s_tile[buf];
+    if (k_loader) {
 #pragma unroll
-    for (int c = 0; c < T::CPT; ++c) {
-      const int idx = tid + c * AT_THREADS;
-      const bool is_v = wave * WAVE + c * AT_THREADS >= T::CHUNKS;
-      const int pc = is_v ? idx - T::CHUNKS : idx;
-      const int rr = pc / T::CPR, part = pc % T::CPR;
-      if (!is_v) {
-        *reinterpret_cast<u32x4*>(st + rr * T::K_STRIDE + part * 16) = pre[c];
-      } else {
-        char* vt = st + T::K_BYTES + (8 * part) * T::VT_STRIDE + rr * 2;
+      for (int c = 0; c < T::KPT; ++c) {
+        const int idx = lt + c * (AT_THREADS / 2);
+        *reinterpret_cast<u32x4*>(st + (idx / T::CPR) * T::K_STRIDE + (idx % T::CPR) * 16) = pre[c];
+      }
+    } else if (lt < T::VUNITS) {
+      const int m = lt & 15, part = lt >> 4;
+      char* vt = st + T::K_BYTES + (8 * part) * T::VT_STRIDE + 4 * m;
 #pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          const uint32_t w = pre[c][t];
-          *reinterpret_cast<uint16_t*>(vt + (2 * t) * T::VT_STRIDE) = (uint16_t)(w & 0xffffu);
-          *reinterpret_cast<uint16_t*>(vt + (2 * t + 1) * T::VT_STRIDE) = (uint16_t)(w >> 16);
-        }
+      for (int w = 0; w < 4; ++w) {
+        // low halves (element 2w) and high halves (element 2w+1) of keys 2m, 2m+1
+        *reinterpret_cast<uint32_t*>(vt + (2 * w) * T::VT_STRIDE) = __builtin_amdgcn_perm(pre[1][w], pre[0][w], 0x05040100u);
+        *reinterpret_cast<uint32_t*>(vt + (2 * w + 1) * T::VT_STRIDE) = __builtin_amdgcn_perm(pre[1][w], pre[0][w], 0x07060302u);
       }
     }
   };
