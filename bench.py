@@ -12,8 +12,9 @@ value = context keys scored per second over whole steps (Hkv * n_ctx / step).
 
 Also reported: per-kernel times (HIP events on the launch stream), the score
 pass's TFLOP/s against the bf16 MFMA peak (roofline), the LSE pass's
-TFLOP/s, eviction GB/s against HBM peak, and the CPU oracle timed on a
-bounded sample of the same workload.
+TFLOP/s, eviction GB/s against HBM peak, the CPU oracle timed on a
+bounded sample of the same workload, and (under "adjacent", timed after the
+step and not part of it) the attention forward that also returns O.
 
     python bench.py [--gpus 1] [--steps 10] [--warmup 3] [--no-cpu-baseline]
 """
@@ -108,6 +109,8 @@ def main():
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-adjacent", action="store_true",
+                    help="skip the kernels timed after the step (attention forward with output)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy (for scaling HBM byte counters)")
     ap.add_argument("--workload", default="qwen3-8b-layer-kvzip+-32k",
@@ -206,6 +209,30 @@ def main():
     t_score = float(np.mean([a[1].elapsed_time(a[2]) for a in evs]))
     t_evict = float(np.mean([a[2].elapsed_time(a[3]) for a in evs]))
 
+    # Adjacent kernels, timed after the step (not part of it): the attention
+    # forward that returns O with the same LSE.
+    def timed(fn, reps=3):
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    adjacent = {}
+    if not args.no_adjacent:
+        Vs = dev_bf16(d["Vself"]) if "Vself" in d else None
+        O = torch.empty_like(Q)
+        L2 = torch.empty_like(L)
+        if sum_mode:
+            t_attn = timed(lambda: kvs.attention(Q, K, V, None, None, scale=scale, mask="causal", out=O, lse_out=L2))
+        else:
+            t_attn = timed(lambda: kvs.attention(Q, K, V, Ks, Vs, scale=scale, mask="repeat", chunk=r.chunk, out=O,
+                                                 lse_out=L2))
+        del O, L2, Vs
     offs = outs[1].cpu().numpy()
     kept = np.diff(offs)
     kept_total = int(offs[-1])
@@ -253,6 +280,11 @@ def main():
     if not args.no_cpu_baseline and not sum_mode:
         _log("[bench] timing the CPU oracle on a sample")
         out["cpu_baseline"] = cpu_baseline(d, wl)
+    if not args.no_adjacent:
+        attn_tflops = 2 * lse_flops / (t_attn * 1e-3) / 1e12
+        adjacent["attention"] = {"entry": "kvscore_attention", "ms": t_attn, "flops": 2 * lse_flops,
+                                 "tflops": attn_tflops, "frac_of_bf16_peak": attn_tflops / PEAK_BF16_TFLOPS}
+        out["adjacent"] = adjacent
     print(json.dumps(out), flush=True)
 
 

@@ -239,6 +239,28 @@ def future_mass(Q, K, lse_in, scale, window, n_kvheads, vnorm=None, hnorm=None, 
     return t
 
 
+def value_norms(V, W_O, n_kvheads):
+    """||W_O v_i|| per KV head and key, fp64 [Hkv, n].
+
+    [KVzap] §3.2, Eq. 3 and its variable table: the L2 norm of value vector
+    v_i after the attention output projection W_O, the weight KVzip+ puts on
+    a_ji. W_O is [d_model, Hkv * D] (bf16 bits); KV head h's values meet the
+    column block [h*D, (h+1)*D). Computed as the plain matrix-vector product
+    y = W_h v_i and its Euclidean norm.
+    """
+    Vf, Wf = bf16_bits_to_f64(V), bf16_bits_to_f64(W_O)
+    Hkv, n, D = Vf.shape
+    assert Hkv == n_kvheads and Wf.shape[1] == Hkv * D
+    out = np.empty((Hkv, n))
+    for h in range(Hkv):
+        W_h = Wf[:, h * D:(h + 1) * D]
+        for i0 in range(0, n, _ROWS):
+            i1 = min(i0 + _ROWS, n)
+            Y = Vf[h, i0:i1] @ W_h.T          # [rows, d_model]
+            out[h, i0:i1] = np.sqrt((Y * Y).sum(axis=1))
+    return out
+
+
 def select(scores, window, k=None, tau=None):
     """Kept positions per KV head, ascending, as a list of int64 arrays.
 

@@ -169,6 +169,65 @@ def pin_attn_linear_in_values():
     assert np.allclose(run(V1 + V2, S1 + S2), run(V1, S1) + run(V2, S2), rtol=0, atol=1e-11)
 
 
+# ---------------------------------------------------------------- value-norm pins
+
+def _vn_inputs(seed, Hkv, n, D, d_model):
+    V = synth.normal_bf16(seed, 1, (Hkv, n, D))
+    W = synth.normal_bf16(seed, 2, (d_model, Hkv * D), std=0.05)
+    return V, W
+
+
+def pin_vnorm_orthogonal_columns():
+    """Row f of W_h holds one entry +-c at column f mod D: W_h^T W_h = c^2 (d_model/D) I,
+    so ||W_h v|| = c sqrt(d_model/D) ||v||."""
+    Hkv, n, D, d_model, c = 2, 9, 64, 256, 0.25
+    V, _ = _vn_inputs(31, Hkv, n, D, d_model)
+    W = np.zeros((d_model, Hkv * D), dtype=np.float32)
+    sign = np.where(np.arange(d_model) % 3 == 0, -1.0, 1.0)
+    for h in range(Hkv):
+        W[np.arange(d_model), h * D + np.arange(d_model) % D] = c * sign
+    got = oracle.value_norms(V, _bits(W), Hkv)
+    Vf = _f64(V)
+    want = c * math.sqrt(d_model / D) * np.sqrt((Vf * Vf).sum(axis=2))
+    assert np.allclose(got, want, rtol=1e-13, atol=0)
+
+
+def pin_vnorm_gram_form():
+    """||W_h v||^2 = v^T (W_h^T W_h) v, evaluated through the D x D Gram matrix."""
+    Hkv, n, D, d_model = 3, 11, 64, 160
+    V, W = _vn_inputs(37, Hkv, n, D, d_model)
+    got = oracle.value_norms(V, W, Hkv)
+    Vf, Wf = _f64(V), _f64(W)
+    for h in range(Hkv):
+        Wh = Wf[:, h * D:(h + 1) * D]
+        G = Wh.T @ Wh
+        want = np.sqrt(np.einsum("nd,de,ne->n", Vf[h], G, Vf[h]))
+        assert np.allclose(got[h], want, rtol=1e-11, atol=0), h
+
+
+def pin_vnorm_single_row_brute_force():
+    """One nonzero row w in each head's block: ||W_h v|| = |w . v| (exact sum)."""
+    Hkv, n, D, d_model = 2, 5, 64, 96
+    V, W = _vn_inputs(41, Hkv, n, D, d_model)
+    Wz = np.zeros_like(W)
+    Wz[17] = W[17]
+    got = oracle.value_norms(V, Wz, Hkv)
+    Vf, wf = _f64(V), _f64(W[17])
+    for h, i in itertools.product(range(Hkv), range(n)):
+        want = abs(math.fsum(float(a) * float(b) for a, b in zip(wf[h * D:(h + 1) * D], Vf[h, i])))
+        assert abs(got[h, i] - want) <= 1e-12 * max(want, 1e-300), (h, i)
+
+
+def pin_vnorm_head_block_isolation():
+    """Only head h's column block of W_O acts on head h's values."""
+    Hkv, n, D, d_model = 3, 6, 64, 128
+    V, W = _vn_inputs(43, Hkv, n, D, d_model)
+    Wb = np.zeros_like(W)
+    Wb[:, D:2 * D] = W[:, D:2 * D]
+    got = oracle.value_norms(V, Wb, Hkv)
+    assert np.all(got[0] == 0) and np.all(got[2] == 0) and np.all(got[1] > 0)
+
+
 # ---------------------------------------------------------------- max-mode pins
 
 def pin_max_zero_queries():

@@ -34,6 +34,9 @@ MUTANTS = {
                                   "vals = np.concatenate([Vc[h], Vs[h][c0:c1][::-1]], axis=0)"),
     "attn-causal-value-head": ("if mask == REPEAT else Vc[h]", "if mask == REPEAT else Vc[(h + 1) % Hkv]"),
     "attn-lse-max-dropped": ("L_out[g, cols] = M[:, 0] + np.log(tot[:, 0])", "L_out[g, cols] = np.log(tot[:, 0])"),
+    "vnorm-next-head-block": ("W_h = Wf[:, h * D:(h + 1) * D]", "W_h = Wf[:, ((h + 1) % Hkv) * D:((h + 1) % Hkv + 1) * D]"),
+    "vnorm-no-sqrt": ("out[h, i0:i1] = np.sqrt((Y * Y).sum(axis=1))", "out[h, i0:i1] = (Y * Y).sum(axis=1)"),
+    "vnorm-l1-norm": ("out[h, i0:i1] = np.sqrt((Y * Y).sum(axis=1))", "out[h, i0:i1] = np.abs(Y).sum(axis=1)"),
     "window-not-kept": ("keep[n - w:] = True", "pass"),
     "threshold-strict": ("keep[cand] |= s[cand] >= float(np.float32(tau))", "keep[cand] |= s[cand] > float(np.float32(tau))"),
     "ties-higher-index-first": ("order = np.lexsort((cand, neg, is_nan))", "order = np.lexsort((-cand, neg, is_nan))"),
@@ -43,7 +46,7 @@ MUTANTS = {
                                 "offsets = np.concatenate([np.cumsum(counts), [0]])"),
 }
 
-EXPORTED = ["lse", "attention", "attention_weights", "max_scores", "future_mass", "select", "compact",
+EXPORTED = ["lse", "attention", "attention_weights", "max_scores", "future_mass", "value_norms", "select", "compact",
             "visible_logits", "kv_head_of", "outside_window"]
 
 
