@@ -14,7 +14,8 @@ Also reported: per-kernel times (HIP events on the launch stream), the score
 pass's TFLOP/s against the bf16 MFMA peak (roofline), the LSE pass's
 TFLOP/s, eviction GB/s against HBM peak, the CPU oracle timed on a
 bounded sample of the same workload, and (under "adjacent", timed after the
-step and not part of it) the attention forward that also returns O.
+step and not part of it) the attention forward that also returns O and the
+value-norm kernel that produces the vnorm input.
 
     python bench.py [--gpus 1] [--steps 10] [--warmup 3] [--no-cpu-baseline]
 """
@@ -233,6 +234,16 @@ def main():
             t_attn = timed(lambda: kvs.attention(Q, K, V, Ks, Vs, scale=scale, mask="repeat", chunk=r.chunk, out=O,
                                                  lse_out=L2))
         del O, L2, Vs
+        if "WO" in d:
+            WO = dev_bf16(d["WO"])
+            vn_out = torch.empty((r.Hkv, r.n_ctx), dtype=torch.float32, device="cuda")
+            t_vn = timed(lambda: kvs.value_norms(V, WO, out=vn_out))
+            vn_flops = 2 * r.Hkv * r.n_ctx * r.D * d["WO"].shape[0]
+            vn_tflops = vn_flops / (t_vn * 1e-3) / 1e12
+            adjacent["value_norms"] = {"entry": "kvscore_vnorm", "ms": t_vn, "flops": vn_flops, "tflops": vn_tflops,
+                                       "frac_of_bf16_peak": vn_tflops / PEAK_BF16_TFLOPS,
+                                       "d_model": int(d["WO"].shape[0])}
+            del WO, vn_out
     offs = outs[1].cpu().numpy()
     kept = np.diff(offs)
     kept_total = int(offs[-1])

@@ -150,6 +150,28 @@ int kvscore_futuremass(const kvs_attn_desc* d, const kvs_bf16* Q,
                        const float* vnorm, const float* hnorm, float* target,
                        void* stream);
 
+/* Value norms ||W_O v_i|| (KVzap page §3.2, Eq. 3 and its variable table),
+ * the vnorm input of kvscore_max / kvscore_futuremass:
+ *   vnorm[h][i] = || W_O[:, h*head_dim : (h+1)*head_dim] . v_i^h ||_2
+ * V      [n_kvheads, n_tok, head_dim] bf16, strides v_head_stride,
+ *        v_tok_stride (elements, multiples of 8, v_tok_stride >= head_dim);
+ * W_O    [d_model, n_kvheads * head_dim] bf16, row stride wo_row_stride
+ *        (elements, multiple of 8, >= n_kvheads * head_dim, <= 2^23);
+ * vnorm  [n_kvheads, n_tok] fp32, dense, overwritten (0 when d_model == 0).
+ * Products of bf16 values are exact; sums are fp32. */
+typedef struct kvs_vnorm_desc {
+  int32_t n_kvheads;
+  int32_t head_dim;
+  int64_t n_tok;
+  int32_t d_model;
+  int32_t reserved; /* set to 0 */
+  int64_t v_head_stride, v_tok_stride;
+  int64_t wo_row_stride;
+} kvs_vnorm_desc;
+
+int kvscore_vnorm(const kvs_vnorm_desc* d, const kvs_bf16* V,
+                  const kvs_bf16* W_O, float* vnorm, void* stream);
+
 /* Eviction of one layer's cache.
  *   scores [n_kvheads, n_tok] fp32, head stride score_head_stride (elements)
  *   K, V   [n_kvheads, n_tok, head_dim] bf16, strides kv_head_stride,

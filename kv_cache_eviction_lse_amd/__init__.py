@@ -7,6 +7,7 @@ the C ABI in ``include/kvscore.h``:
 
 * :func:`lse`          -> ``kvscore_lse``
 * :func:`attention`    -> ``kvscore_attention``
+* :func:`value_norms`  -> ``kvscore_vnorm``
 * :func:`max_scores`   -> ``kvscore_max``
 * :func:`future_mass`  -> ``kvscore_futuremass``
 * :func:`evict`        -> ``kv_evict`` (+ ``kv_evict_workspace_bytes``)
@@ -30,7 +31,7 @@ KVS_OK, KVS_EINVAL, KVS_EUNSUPPORTED, KVS_ECAPACITY, KVS_EWORKSPACE, KVS_EHIP, K
 MASK_REPEAT, MASK_CAUSAL = 0, 1
 
 EXPORTED_SYMBOLS = (
-    "kvscore_lse", "kvscore_attention", "kvscore_max", "kvscore_futuremass", "kv_evict_workspace_bytes", "kv_evict",
+    "kvscore_lse", "kvscore_attention", "kvscore_vnorm", "kvscore_max", "kvscore_futuremass", "kv_evict_workspace_bytes", "kv_evict",
     "kvs_strerror", "kvs_last_error", "kvs_version",
 )
 
@@ -58,6 +59,16 @@ class EvictDesc(ctypes.Structure):
     ]
 
 
+class VnormDesc(ctypes.Structure):
+    _fields_ = [
+        ("n_kvheads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+        ("n_tok", ctypes.c_int64),
+        ("d_model", ctypes.c_int32), ("reserved", ctypes.c_int32),
+        ("v_head_stride", ctypes.c_int64), ("v_tok_stride", ctypes.c_int64),
+        ("wo_row_stride", ctypes.c_int64),
+    ]
+
+
 class KvsError(RuntimeError):
     def __init__(self, status: int, message: str):
         super().__init__(f"[{status}] {message}")
@@ -80,6 +91,7 @@ def lib() -> ctypes.CDLL:
     pA, pE = ctypes.POINTER(AttnDesc), ctypes.POINTER(EvictDesc)
     L.kvscore_lse.argtypes = [pA, vp, vp, vp, vp, vp]
     L.kvscore_attention.argtypes = [pA, vp, vp, vp, vp, vp, vp, vp, vp]
+    L.kvscore_vnorm.argtypes = [ctypes.POINTER(VnormDesc), vp, vp, vp, vp]
     L.kvscore_max.argtypes = [pA, vp, vp, vp, vp, vp, vp, c, vp]
     L.kvscore_futuremass.argtypes = [pA, vp, vp, vp, i64, vp, vp, vp, vp]
     L.kv_evict_workspace_bytes.argtypes = [pE]
@@ -90,7 +102,7 @@ def lib() -> ctypes.CDLL:
     L.kvs_last_error.argtypes = []
     L.kvs_last_error.restype = ctypes.c_char_p
     L.kvs_version.restype = c
-    for name in ("kvscore_lse", "kvscore_attention", "kvscore_max", "kvscore_futuremass", "kv_evict"):
+    for name in ("kvscore_lse", "kvscore_attention", "kvscore_vnorm", "kvscore_max", "kvscore_futuremass", "kv_evict"):
         getattr(L, name).restype = c
     _lib = L
     return L
@@ -199,6 +211,26 @@ def attention(Q, K, V, Kself=None, Vself=None, *, scale: float, mask: str = "rep
     check(lib().kvscore_attention(ctypes.byref(d), _ptr(Q), _ptr(K), _ptr(Kself), _ptr(V), _ptr(Vself),
                                   _ptr(out), _ptr(lse_out), _stream(stream)))
     return out, lse_out
+
+
+def value_norms(V, W_O, *, out=None, stream=None):
+    """||W_O v_i|| per KV head and key, fp32 [Hkv, n] (``kvscore_vnorm``).
+    V bf16 [Hkv, n, D]; W_O bf16 [d_model, Hkv * D] with a contiguous last dimension."""
+    torch = _torch()
+    _bf16("V", V)
+    if W_O.dtype != torch.bfloat16 or W_O.dim() != 2 or W_O.stride(-1) != 1 or not W_O.is_cuda:
+        raise ValueError("W_O must be a bfloat16 GPU matrix [d_model, Hkv * D] with a contiguous last dimension")
+    Hkv, n, D = V.shape
+    if W_O.shape[1] != Hkv * D:
+        raise ValueError("W_O must have Hkv * D columns")
+    d = VnormDesc()
+    d.n_kvheads, d.head_dim, d.n_tok, d.d_model, d.reserved = Hkv, D, n, W_O.shape[0], 0
+    d.v_head_stride, d.v_tok_stride, d.wo_row_stride = V.stride(0), V.stride(1), W_O.stride(0)
+    if out is None:
+        out = torch.empty((Hkv, n), dtype=torch.float32, device=V.device)
+    _f32("out", out, (Hkv, n))
+    check(lib().kvscore_vnorm(ctypes.byref(d), _ptr(V), _ptr(W_O), _ptr(out), _stream(stream)))
+    return out
 
 
 def max_scores(Q, K, lse_vals, *, scale: float, vnorm=None, hnorm=None, out=None, accumulate: bool = False,

@@ -12,7 +12,7 @@ from concurrent.futures import ThreadPoolExecutor
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libkvscore.so")
-SOURCES = ["api.cpp", "lse.hip", "score.hip", "evict.hip", "attn.hip"]
+SOURCES = ["api.cpp", "lse.hip", "score.hip", "evict.hip", "attn.hip", "vnorm.hip"]
 ARCH = "gfx950"
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
@@ -33,6 +33,7 @@ COMMON = [
 FILE_FLAGS = {
     "lse.hip": ["-fno-honor-nans", "-mllvm", "-amdgpu-mfma-vgpr-form"],
     "score.hip": ["-fno-honor-nans", "-mllvm", "-amdgpu-mfma-vgpr-form"],
+    "vnorm.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
 }
 
 

@@ -171,6 +171,35 @@ KVS_API int kvscore_attention(const kvs_attn_desc* d, const kvs_bf16* Q, const k
                     "kvscore_attention");
 }
 
+KVS_API int kvscore_vnorm(const kvs_vnorm_desc* d, const kvs_bf16* V, const kvs_bf16* W_O, float* vnorm,
+                          void* stream) {
+  if (!d) return fail(KVS_EINVAL, "descriptor is NULL");
+  if (d->reserved != 0) return fail(KVS_EINVAL, "reserved field must be 0");
+  if (d->n_kvheads < 1 || d->n_kvheads > 65535) return fail(KVS_EINVAL, "n_kvheads must be in [1, 65535]");
+  if (d->head_dim != 64 && d->head_dim != 128)
+    return fail(KVS_EUNSUPPORTED, "head_dim %d is not supported (64 or 128)", d->head_dim);
+  if (d->n_tok < 0 || d->d_model < 0) return fail(KVS_EINVAL, "negative size");
+  if (d->n_tok > MAX_TOKENS) return fail(KVS_EUNSUPPORTED, "more than 2^30 tokens");
+  if (((d->n_tok + 511) / 512) * d->n_kvheads >= ((int64_t)1 << 31))
+    return fail(KVS_EUNSUPPORTED, "n_kvheads * n_tok is too large");
+  const int64_t st[3] = {d->v_head_stride, d->v_tok_stride, d->wo_row_stride};
+  for (int i = 0; i < 3; ++i) {
+    if (st[i] < 0) return fail(KVS_EINVAL, "negative stride");
+    if (st[i] % 8) return fail(KVS_EUNSUPPORTED, "strides must be multiples of 8 elements (16 bytes)");
+  }
+  if (d->n_tok > 0 && d->v_tok_stride < d->head_dim) return fail(KVS_EINVAL, "v_tok_stride is smaller than head_dim");
+  if (d->v_tok_stride > MAX_TOK_STRIDE || d->wo_row_stride > MAX_TOK_STRIDE)
+    return fail(KVS_EUNSUPPORTED, "row strides above 2^23 elements");
+  if (d->d_model > 0 && d->wo_row_stride < (int64_t)d->n_kvheads * d->head_dim)
+    return fail(KVS_EINVAL, "wo_row_stride is smaller than n_kvheads * head_dim");
+  if (d->n_tok > 0 && (!V || !vnorm)) return fail(KVS_EINVAL, "V or vnorm is NULL");
+  if (d->n_tok > 0 && d->d_model > 0 && !W_O) return fail(KVS_EINVAL, "W_O is NULL");
+  if (!aligned16(V) || !aligned16(W_O)) return fail(KVS_EUNSUPPORTED, "V and W_O must be 16-byte aligned");
+  int st_, cus;
+  if ((st_ = check_device(&cus))) return st_;
+  return hip_status(kvs::launch_vnorm(*d, V, W_O, vnorm, static_cast<hipStream_t>(stream)), "kvscore_vnorm");
+}
+
 KVS_API int kvscore_max(const kvs_attn_desc* d, const kvs_bf16* Q, const kvs_bf16* K, const float* lse,
                         const float* vnorm, const float* hnorm, float* scores, int accumulate, void* stream) {
   int st = check_attn(d, Q, K, nullptr, false);

@@ -22,6 +22,9 @@ hipError_t launch_score_sum(const kvs_attn_desc& d, const uint16_t* Q, const uin
 hipError_t launch_attn(const kvs_attn_desc& d, const uint16_t* Q, const uint16_t* K, const uint16_t* Kself,
                        const uint16_t* V, const uint16_t* Vself, uint16_t* O, float* lse, hipStream_t s);
 
+hipError_t launch_vnorm(const kvs_vnorm_desc& d, const uint16_t* V, const uint16_t* W_O, float* vnorm,
+                        hipStream_t s);
+
 size_t evict_workspace_bytes(const kvs_evict_desc& e);
 
 hipError_t launch_evict(const kvs_evict_desc& e, const float* scores, const uint16_t* K, const uint16_t* V,

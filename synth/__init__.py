@@ -11,6 +11,8 @@ to bfloat16, and lays them out the way the library expects:
 * ``V``      bf16 bits, uint16 ``[Hkv, n_ctx, D]``
 * ``Vself``  bf16 bits, uint16 ``[Hkv, n_q, D]`` (the repeated copy's own
   values; repeat workloads with values only)
+* ``WO``     bf16 bits, uint16 ``[d_model, Hkv * D]``: that random output
+  projection (value-norm workloads only)
 * ``vnorm``  fp32 ``[Hkv, n_ctx]``: the norm of a random output-projection
   block applied to each value row (the weight of the value-norm-normalised
   score); an *input* of the scoring call, synthesised here
@@ -245,6 +247,7 @@ def draw(recipe: Recipe, seed: int) -> dict:
             sq = np.einsum("nd,nd->n", v @ gram, v)
             vnorm[h] = np.sqrt(np.maximum(sq, 0.0)).astype(np.float32)
         out["vnorm"] = vnorm
+        out["WO"] = WO
         out["hnorm"] = np.exp(normal_f64(seed, S_HNORM, (r.n_q,), r.hnorm_mu, r.hnorm_sigma)).astype(np.float32)
     return out
 

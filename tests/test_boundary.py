@@ -146,6 +146,44 @@ def test_attention_rejects_pointers(L):
              None) == kvs.KVS_EUNSUPPORTED
 
 
+def _vdesc(**kw):
+    d = kvs.VnormDesc()
+    d.n_kvheads, d.head_dim, d.n_tok, d.d_model, d.reserved = 2, 128, 100, 512, 0
+    d.v_head_stride, d.v_tok_stride, d.wo_row_stride = 100 * 128, 128, 256
+    for k, v in kw.items():
+        setattr(d, k, v)
+    return d
+
+
+VNORM_BAD = [
+    (dict(reserved=3), kvs.KVS_EINVAL),
+    (dict(n_kvheads=0), kvs.KVS_EINVAL),
+    (dict(head_dim=80), kvs.KVS_EUNSUPPORTED),
+    (dict(n_tok=-1), kvs.KVS_EINVAL),
+    (dict(d_model=-5), kvs.KVS_EINVAL),
+    (dict(v_tok_stride=64), kvs.KVS_EINVAL),
+    (dict(v_tok_stride=132), kvs.KVS_EUNSUPPORTED),
+    (dict(wo_row_stride=248), kvs.KVS_EINVAL),
+    (dict(wo_row_stride=(1 << 23) + 8), kvs.KVS_EUNSUPPORTED),
+    (dict(n_tok=(1 << 30) + 1), kvs.KVS_EUNSUPPORTED),
+]
+
+
+@pytest.mark.parametrize("kw,code", VNORM_BAD)
+def test_vnorm_rejects(L, kw, code):
+    d = _vdesc(**kw)
+    assert L.kvscore_vnorm(ctypes.byref(d), FAKE, FAKE, FAKE, None) == code
+
+
+def test_vnorm_rejects_pointers(L):
+    d = _vdesc()
+    assert L.kvscore_vnorm(None, FAKE, FAKE, FAKE, None) == kvs.KVS_EINVAL
+    assert L.kvscore_vnorm(ctypes.byref(d), None, FAKE, FAKE, None) == kvs.KVS_EINVAL
+    assert L.kvscore_vnorm(ctypes.byref(d), FAKE, None, FAKE, None) == kvs.KVS_EINVAL
+    assert L.kvscore_vnorm(ctypes.byref(d), FAKE, FAKE, None, None) == kvs.KVS_EINVAL
+    assert L.kvscore_vnorm(ctypes.byref(d), FAKE, ctypes.c_void_p(0x100008), FAKE, None) == kvs.KVS_EUNSUPPORTED
+
+
 def test_max_and_futuremass_reject(L):
     d = _desc()
     assert L.kvscore_max(ctypes.byref(d), FAKE, FAKE, FAKE, None, None, FAKE, 2, None) == kvs.KVS_EINVAL
