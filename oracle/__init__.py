@@ -20,6 +20,7 @@ from .reference import (  # noqa: F401
     attention_weights,
     max_scores,
     future_mass,
+    decode_attention,
     value_norms,
     select,
     compact,

@@ -239,6 +239,42 @@ def future_mass(Q, K, lse_in, scale, window, n_kvheads, vnorm=None, hnorm=None, 
     return t
 
 
+def decode_attention(Q, K_cache, V_cache, head_offsets, scale):
+    """Decode queries attending to the compacted per-head cache, fp64:
+    (O [Hq, n_q, D], LSE [Hq, n_q]).
+
+    Eviction leaves each KV head its own number of rows, written head after
+    head ([KVzap] Algorithm 1: keys[indices], values[indices]); the pages name
+    that non-uniform cache as what a variable-length kernel must serve before
+    pruning pays off ([KVzap] "Limitation 3" and FAQ "Q4"). Query head g
+    (KV head h = g // G) sees rows head_offsets[h] .. head_offsets[h+1]-1 of
+    K_cache / V_cache ([rows, D] bf16 bits), every decode query all of them:
+    o_j = sum_r a_jr v_r, a_jr = exp(l_jr - LSE_j), l_jr = scale * q_j . k_r
+    (the per-head sum of [KVzap] §3.2 Eq. 2). A head that kept no rows gives
+    O = 0 and LSE = -inf.
+    """
+    Qf, Kf, Vf = bf16_bits_to_f64(Q), bf16_bits_to_f64(K_cache), bf16_bits_to_f64(V_cache)
+    Hq, n_q, D = Qf.shape
+    offs = np.asarray(head_offsets, dtype=np.int64)
+    Hkv = offs.size - 1
+    G = Hq // Hkv
+    scale = float(np.float32(scale))
+    O = np.zeros((Hq, n_q, D))
+    L_out = np.full((Hq, n_q), -np.inf)
+    for g in range(Hq):
+        h = kv_head_of(g, G)
+        r0, r1 = int(offs[h]), int(offs[h + 1])
+        if r1 == r0:
+            continue
+        L = scale * (Qf[g] @ Kf[r0:r1].T)          # [n_q, rows]
+        M = L.max(axis=1, keepdims=True)
+        E = np.exp(L - M)
+        tot = E.sum(axis=1, keepdims=True)
+        L_out[g] = M[:, 0] + np.log(tot[:, 0])
+        O[g] = (E / tot) @ Vf[r0:r1]
+    return O, L_out
+
+
 def value_norms(V, W_O, n_kvheads):
     """||W_O v_i|| per KV head and key, fp64 [Hkv, n].
 

@@ -169,6 +169,79 @@ def pin_attn_linear_in_values():
     assert np.allclose(run(V1 + V2, S1 + S2), run(V1, S1) + run(V2, S2), rtol=0, atol=1e-11)
 
 
+# ---------------------------------------------------------------- decode-over-cache pins
+
+def _decode_inputs(seed, Hq, Hkv, D, counts, n_q=1):
+    offs = np.concatenate([[0], np.cumsum(counts)]).astype(np.int64)
+    Q = synth.normal_bf16(seed, 1, (Hq, n_q, D))
+    Kc = synth.normal_bf16(seed, 2, (int(offs[-1]), D))
+    Vc = synth.normal_bf16(seed, 3, (int(offs[-1]), D))
+    return Q, Kc, Vc, offs
+
+
+def pin_decode_brute_force():
+    """Every kept row of the query's head enumerated one by one with exact sums;
+    a head with no rows gives O = 0, LSE = -inf."""
+    Hq, Hkv, D = 6, 3, 64
+    Q, Kc, Vc, offs = _decode_inputs(47, Hq, Hkv, D, [5, 0, 7], n_q=2)
+    O, L = oracle.decode_attention(Q, Kc, Vc, offs, 0.25)
+    Qf, Kf, Vf = _f64(Q), _f64(Kc), _f64(Vc)
+    for g, t in itertools.product(range(Hq), range(2)):
+        h = g // 2
+        rows = range(int(offs[h]), int(offs[h + 1]))
+        if not rows:
+            assert L[g, t] == -np.inf and np.all(O[g, t] == 0), (g, t)
+            continue
+        logits = [0.25 * math.fsum(float(a) * float(b) for a, b in zip(Qf[g, t], Kf[r])) for r in rows]
+        m = max(logits)
+        w = [math.exp(x - m) for x in logits]
+        tot = math.fsum(w)
+        assert abs(L[g, t] - (m + math.log(tot))) < 1e-12, (g, t)
+        for dd in range(D):
+            want = math.fsum(wi * float(Vf[r, dd]) for wi, r in zip(w, rows)) / tot
+            assert abs(O[g, t, dd] - want) < 1e-12, (g, t, dd)
+
+
+def pin_decode_single_row_and_constant_values():
+    """One kept row per head: O = that row's value, LSE = its logit. Every row
+    equal to c: O = c."""
+    Hq, Hkv, D = 4, 2, 64
+    Q, Kc, Vc, offs = _decode_inputs(53, Hq, Hkv, D, [1, 1])
+    O, L = oracle.decode_attention(Q, Kc, Vc, offs, 0.5)
+    Qf, Kf, Vf = _f64(Q), _f64(Kc), _f64(Vc)
+    for g in range(Hq):
+        h = g // 2
+        assert np.array_equal(O[g, 0], Vf[h])
+        assert abs(L[g, 0] - 0.5 * math.fsum(float(a) * float(b) for a, b in zip(Qf[g, 0], Kf[h]))) < 1e-12
+    Q, Kc, Vc, offs = _decode_inputs(59, Hq, Hkv, D, [9, 4])
+    c = Vc[3].copy()
+    Vconst = np.broadcast_to(c, Vc.shape).copy()
+    O, _ = oracle.decode_attention(Q, Kc, Vconst, offs, 0.5)
+    assert np.allclose(O, _f64(c)[None, None, :], rtol=1e-13, atol=1e-13)
+
+
+def pin_decode_over_compacted_equals_masked_layer():
+    """Decoding over select + compact equals attending, in the uncompacted
+    layer, to exactly the kept positions (brute force on the kept set)."""
+    Hkv, n, D, G = 2, 40, 64, 2
+    K = synth.normal_bf16(61, 1, (Hkv, n, D))
+    V = synth.normal_bf16(61, 2, (Hkv, n, D))
+    Q = synth.normal_bf16(61, 3, (Hkv * G, 1, D))
+    scores = synth.evict_scores(61, Hkv, n)
+    kept = oracle.select(scores, 6, k=9)
+    Kc, Vc, offs = oracle.compact(K, V, kept)
+    O, _ = oracle.decode_attention(Q, Kc, Vc, offs, 0.125)
+    Qf, Kf, Vf = _f64(Q), _f64(K), _f64(V)
+    for g in range(Hkv * G):
+        h = g // G
+        logits = [0.125 * math.fsum(float(a) * float(b) for a, b in zip(Qf[g, 0], Kf[h, i])) for i in kept[h]]
+        m = max(logits)
+        w = [math.exp(x - m) for x in logits]
+        tot = math.fsum(w)
+        want = np.array([math.fsum(wi * float(Vf[h, i, dd]) for wi, i in zip(w, kept[h])) / tot for dd in range(D)])
+        assert np.allclose(O[g, 0], want, rtol=0, atol=1e-12), g
+
+
 # ---------------------------------------------------------------- value-norm pins
 
 def _vn_inputs(seed, Hkv, n, D, d_model):

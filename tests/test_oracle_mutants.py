@@ -37,6 +37,10 @@ MUTANTS = {
     "vnorm-next-head-block": ("W_h = Wf[:, h * D:(h + 1) * D]", "W_h = Wf[:, ((h + 1) % Hkv) * D:((h + 1) % Hkv + 1) * D]"),
     "vnorm-no-sqrt": ("out[h, i0:i1] = np.sqrt((Y * Y).sum(axis=1))", "out[h, i0:i1] = (Y * Y).sum(axis=1)"),
     "vnorm-l1-norm": ("out[h, i0:i1] = np.sqrt((Y * Y).sum(axis=1))", "out[h, i0:i1] = np.abs(Y).sum(axis=1)"),
+    "decode-next-head-rows": ("r0, r1 = int(offs[h]), int(offs[h + 1])",
+                              "r0, r1 = int(offs[(h + 1) % Hkv]), int(offs[(h + 1) % Hkv + 1])"),
+    "decode-unnormalised": ("O[g] = (E / tot) @ Vf[r0:r1]", "O[g] = E @ Vf[r0:r1]"),
+    "decode-last-row-dropped": ("L = scale * (Qf[g] @ Kf[r0:r1].T)", "r1 = max(r0 + 1, r1 - 1)\n        L = scale * (Qf[g] @ Kf[r0:r1].T)"),
     "window-not-kept": ("keep[n - w:] = True", "pass"),
     "threshold-strict": ("keep[cand] |= s[cand] >= float(np.float32(tau))", "keep[cand] |= s[cand] > float(np.float32(tau))"),
     "ties-higher-index-first": ("order = np.lexsort((cand, neg, is_nan))", "order = np.lexsort((-cand, neg, is_nan))"),
@@ -46,7 +50,7 @@ MUTANTS = {
                                 "offsets = np.concatenate([np.cumsum(counts), [0]])"),
 }
 
-EXPORTED = ["lse", "attention", "attention_weights", "max_scores", "future_mass", "value_norms", "select", "compact",
+EXPORTED = ["lse", "attention", "attention_weights", "max_scores", "future_mass", "decode_attention", "value_norms", "select", "compact",
             "visible_logits", "kv_head_of", "outside_window"]
 
 
