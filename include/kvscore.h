@@ -213,6 +213,43 @@ int kv_evict(const kvs_evict_desc* e, const float* scores, const kvs_bf16* K,
              kvs_bf16* K_out, kvs_bf16* V_out, void* workspace,
              size_t workspace_bytes, void* stream);
 
+/* Decode attention over the compacted per-head cache (the cache kv_evict
+ * writes: KVzap page Algorithm 1 keys[indices], values[indices], head after
+ * head; the page's "Limitation 3" and FAQ "Q4" name this non-uniform,
+ * per-head-length cache as what a variable-length kernel must serve):
+ *   for query head g (KV head h = g / (n_qheads / n_kvheads)) and decode
+ *   query t, over the rows r in [head_offsets[h], head_offsets[h+1]):
+ *   O[g][t]   = sum_r exp(scale * q . k_r - lse[g][t]) * v_r
+ *   lse[g][t] = ln sum_r exp(scale * q . k_r)   (-inf, with O = 0, for a
+ *               head that kept no rows). Every decode query sees every row
+ *               of its head.
+ * Q        [n_qheads, n_q, head_dim] bf16, strides q_head_stride, q_tok_stride
+ * K_cache, V_cache [capacity, head_dim] bf16, dense rows (kv_evict's K_out, V_out)
+ * head_offsets [n_kvheads + 1] int64, device (kv_evict's); values are
+ *        clamped to [0, capacity] and made non-decreasing before use
+ * O        [n_qheads, n_q, head_dim] bf16 with Q's strides, overwritten
+ * lse      [n_qheads, n_q] fp32, dense, overwritten
+ * workspace: device memory of at least kvscore_decode_workspace_bytes(d)
+ *        bytes, 16-byte aligned, caller-owned, contents need not be set.
+ * Scores, exponentials and sums are fp32; O is rounded once to bf16. */
+typedef struct kvs_decode_desc {
+  int32_t n_qheads;
+  int32_t n_kvheads;
+  int32_t head_dim;
+  int32_t n_q;      /* decode queries per query head, >= 1 */
+  int64_t q_head_stride, q_tok_stride;
+  int64_t capacity; /* rows of K_cache / V_cache */
+  float scale;
+  int32_t reserved; /* set to 0 */
+} kvs_decode_desc;
+
+size_t kvscore_decode_workspace_bytes(const kvs_decode_desc* d);
+
+int kvscore_decode(const kvs_decode_desc* d, const kvs_bf16* Q,
+                   const kvs_bf16* K_cache, const kvs_bf16* V_cache,
+                   const int64_t* head_offsets, kvs_bf16* O, float* lse,
+                   void* workspace, size_t workspace_bytes, void* stream);
+
 /* ---- diagnostics ----------------------------------------------------- */
 const char* kvs_strerror(int status);   /* static text for a status code */
 const char* kvs_last_error(void);       /* this thread's last failure reason */

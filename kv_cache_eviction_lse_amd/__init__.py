@@ -8,6 +8,7 @@ the C ABI in ``include/kvscore.h``:
 * :func:`lse`          -> ``kvscore_lse``
 * :func:`attention`    -> ``kvscore_attention``
 * :func:`value_norms`  -> ``kvscore_vnorm``
+* :func:`decode`       -> ``kvscore_decode`` (+ ``kvscore_decode_workspace_bytes``)
 * :func:`max_scores`   -> ``kvscore_max``
 * :func:`future_mass`  -> ``kvscore_futuremass``
 * :func:`evict`        -> ``kv_evict`` (+ ``kv_evict_workspace_bytes``)
@@ -31,7 +32,8 @@ KVS_OK, KVS_EINVAL, KVS_EUNSUPPORTED, KVS_ECAPACITY, KVS_EWORKSPACE, KVS_EHIP, K
 MASK_REPEAT, MASK_CAUSAL = 0, 1
 
 EXPORTED_SYMBOLS = (
-    "kvscore_lse", "kvscore_attention", "kvscore_vnorm", "kvscore_max", "kvscore_futuremass", "kv_evict_workspace_bytes", "kv_evict",
+    "kvscore_lse", "kvscore_attention", "kvscore_vnorm", "kvscore_decode_workspace_bytes", "kvscore_decode",
+    "kvscore_max", "kvscore_futuremass", "kv_evict_workspace_bytes", "kv_evict",
     "kvs_strerror", "kvs_last_error", "kvs_version",
 )
 
@@ -69,6 +71,16 @@ class VnormDesc(ctypes.Structure):
     ]
 
 
+class DecodeDesc(ctypes.Structure):
+    _fields_ = [
+        ("n_qheads", ctypes.c_int32), ("n_kvheads", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32), ("n_q", ctypes.c_int32),
+        ("q_head_stride", ctypes.c_int64), ("q_tok_stride", ctypes.c_int64),
+        ("capacity", ctypes.c_int64),
+        ("scale", ctypes.c_float), ("reserved", ctypes.c_int32),
+    ]
+
+
 class KvsError(RuntimeError):
     def __init__(self, status: int, message: str):
         super().__init__(f"[{status}] {message}")
@@ -92,6 +104,10 @@ def lib() -> ctypes.CDLL:
     L.kvscore_lse.argtypes = [pA, vp, vp, vp, vp, vp]
     L.kvscore_attention.argtypes = [pA, vp, vp, vp, vp, vp, vp, vp, vp]
     L.kvscore_vnorm.argtypes = [ctypes.POINTER(VnormDesc), vp, vp, vp, vp]
+    pD = ctypes.POINTER(DecodeDesc)
+    L.kvscore_decode_workspace_bytes.argtypes = [pD]
+    L.kvscore_decode_workspace_bytes.restype = ctypes.c_size_t
+    L.kvscore_decode.argtypes = [pD, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
     L.kvscore_max.argtypes = [pA, vp, vp, vp, vp, vp, vp, c, vp]
     L.kvscore_futuremass.argtypes = [pA, vp, vp, vp, i64, vp, vp, vp, vp]
     L.kv_evict_workspace_bytes.argtypes = [pE]
@@ -102,7 +118,7 @@ def lib() -> ctypes.CDLL:
     L.kvs_last_error.argtypes = []
     L.kvs_last_error.restype = ctypes.c_char_p
     L.kvs_version.restype = c
-    for name in ("kvscore_lse", "kvscore_attention", "kvscore_vnorm", "kvscore_max", "kvscore_futuremass", "kv_evict"):
+    for name in ("kvscore_lse", "kvscore_attention", "kvscore_vnorm", "kvscore_decode", "kvscore_max", "kvscore_futuremass", "kv_evict"):
         getattr(L, name).restype = c
     _lib = L
     return L
@@ -231,6 +247,50 @@ def value_norms(V, W_O, *, out=None, stream=None):
     _f32("out", out, (Hkv, n))
     check(lib().kvscore_vnorm(ctypes.byref(d), _ptr(V), _ptr(W_O), _ptr(out), _stream(stream)))
     return out
+
+
+def decode_desc(Q, K_cache, n_kvheads, scale) -> DecodeDesc:
+    Hq, n_q, D = Q.shape
+    d = DecodeDesc()
+    d.n_qheads, d.n_kvheads, d.head_dim, d.n_q = Hq, n_kvheads, D, n_q
+    d.q_head_stride, d.q_tok_stride = Q.stride(0), Q.stride(1)
+    d.capacity = K_cache.shape[0]
+    d.scale, d.reserved = float(scale), 0
+    return d
+
+
+def decode_workspace_bytes(d: DecodeDesc) -> int:
+    return int(lib().kvscore_decode_workspace_bytes(ctypes.byref(d)))
+
+
+def decode(Q, K_cache, V_cache, head_offsets, *, scale: float, workspace=None, out=None, lse_out=None, stream=None):
+    """Decode attention of Q [Hq, n_q, D] over the compacted per-head cache
+    (``kvscore_decode``): K_cache/V_cache [capacity, D] bf16 rows and the
+    device int64 head_offsets [Hkv+1] that kv_evict wrote. Returns (O, lse)."""
+    torch = _torch()
+    _bf16("Q", Q)
+    for name, t in (("K_cache", K_cache), ("V_cache", V_cache)):
+        if t.dtype != torch.bfloat16 or t.dim() != 2 or not t.is_contiguous() or not t.is_cuda:
+            raise ValueError(f"{name} must be a contiguous bfloat16 GPU matrix [capacity, D]")
+    if K_cache.shape != V_cache.shape or K_cache.shape[1] != Q.shape[2]:
+        raise ValueError("K_cache and V_cache must be [capacity, D] with Q's D")
+    if head_offsets.dtype != torch.int64 or head_offsets.dim() != 1 or not head_offsets.is_cuda:
+        raise ValueError("head_offsets must be a GPU int64 vector [Hkv + 1]")
+    d = decode_desc(Q, K_cache, head_offsets.numel() - 1, scale)
+    need = decode_workspace_bytes(d)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=Q.device)
+    if out is None:
+        out = torch.empty_like(Q)
+    _bf16("out", out)
+    if tuple(out.shape) != tuple(Q.shape) or out.stride() != Q.stride():
+        raise ValueError("out must have Q's shape and strides")
+    if lse_out is None:
+        lse_out = torch.empty((d.n_qheads, d.n_q), dtype=torch.float32, device=Q.device)
+    _f32("lse_out", lse_out, (d.n_qheads, d.n_q))
+    check(lib().kvscore_decode(ctypes.byref(d), _ptr(Q), _ptr(K_cache), _ptr(V_cache), _ptr(head_offsets),
+                               _ptr(out), _ptr(lse_out), _ptr(workspace), workspace.numel(), _stream(stream)))
+    return out, lse_out
 
 
 def max_scores(Q, K, lse_vals, *, scale: float, vnorm=None, hnorm=None, out=None, accumulate: bool = False,

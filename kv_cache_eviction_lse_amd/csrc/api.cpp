@@ -200,6 +200,51 @@ KVS_API int kvscore_vnorm(const kvs_vnorm_desc* d, const kvs_bf16* V, const kvs_
   return hip_status(kvs::launch_vnorm(*d, V, W_O, vnorm, static_cast<hipStream_t>(stream)), "kvscore_vnorm");
 }
 
+namespace {
+int check_decode(const kvs_decode_desc* d) {
+  if (!d) return fail(KVS_EINVAL, "descriptor is NULL");
+  if (d->reserved != 0) return fail(KVS_EINVAL, "reserved field must be 0");
+  if (d->n_qheads < 1 || d->n_kvheads < 1 || d->n_kvheads > 65535)
+    return fail(KVS_EINVAL, "head counts must be >= 1 (n_kvheads <= 65535)");
+  if (d->n_qheads % d->n_kvheads) return fail(KVS_EINVAL, "n_qheads is not a multiple of n_kvheads");
+  if (d->head_dim != 64 && d->head_dim != 128)
+    return fail(KVS_EUNSUPPORTED, "head_dim %d is not supported (64 or 128)", d->head_dim);
+  if (d->n_q < 1 || d->n_q > 4096) return fail(KVS_EINVAL, "n_q must be in [1, 4096]");
+  if ((int64_t)d->n_qheads * d->n_q > 65535) return fail(KVS_EUNSUPPORTED, "n_qheads * n_q above 65535");
+  if (d->capacity < 0 || d->capacity > MAX_TOKENS * 64) return fail(KVS_EINVAL, "capacity out of range");
+  if (!(d->scale > 0.f) || !std::isfinite(d->scale)) return fail(KVS_EINVAL, "scale must be finite and > 0");
+  if (d->q_head_stride < 0 || d->q_tok_stride < 0) return fail(KVS_EINVAL, "negative stride");
+  if (d->q_head_stride % 8 || d->q_tok_stride % 8)
+    return fail(KVS_EUNSUPPORTED, "strides must be multiples of 8 elements (16 bytes)");
+  if (d->n_q > 1 && d->q_tok_stride < d->head_dim) return fail(KVS_EINVAL, "q_tok_stride is smaller than head_dim");
+  return KVS_OK;
+}
+}  // namespace
+
+KVS_API size_t kvscore_decode_workspace_bytes(const kvs_decode_desc* d) {
+  if (check_decode(d)) return 0;
+  return kvs::decode_workspace_bytes(*d);
+}
+
+KVS_API int kvscore_decode(const kvs_decode_desc* d, const kvs_bf16* Q, const kvs_bf16* K_cache,
+                           const kvs_bf16* V_cache, const int64_t* head_offsets, kvs_bf16* O, float* lse,
+                           void* workspace, size_t workspace_bytes, void* stream) {
+  int st = check_decode(d);
+  if (st) return st;
+  if (!Q || !O || !lse || !head_offsets) return fail(KVS_EINVAL, "Q, O, lse or head_offsets is NULL");
+  if (d->capacity > 0 && (!K_cache || !V_cache)) return fail(KVS_EINVAL, "K_cache or V_cache is NULL");
+  if (!aligned16(Q) || !aligned16(O) || !aligned16(K_cache) || !aligned16(V_cache))
+    return fail(KVS_EUNSUPPORTED, "Q, O, K_cache and V_cache must be 16-byte aligned");
+  const size_t need = kvs::decode_workspace_bytes(*d);
+  if (workspace_bytes < need) return fail(KVS_EWORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes, need);
+  if (need > 0 && (!workspace || !aligned16(workspace))) return fail(KVS_EWORKSPACE, "workspace is NULL or misaligned");
+  int cus;
+  if ((st = check_device(&cus))) return st;
+  return hip_status(kvs::launch_decode(*d, Q, K_cache, V_cache, head_offsets, O, lse, workspace,
+                                       static_cast<hipStream_t>(stream)),
+                    "kvscore_decode");
+}
+
 KVS_API int kvscore_max(const kvs_attn_desc* d, const kvs_bf16* Q, const kvs_bf16* K, const float* lse,
                         const float* vnorm, const float* hnorm, float* scores, int accumulate, void* stream) {
   int st = check_attn(d, Q, K, nullptr, false);

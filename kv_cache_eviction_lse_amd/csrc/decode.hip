@@ -1,0 +1,326 @@
+// Decode attention over the compacted per-head cache that kv_evict writes:
+// query head g (KV head h = g / G) attends to rows head_offsets[h] ..
+// head_offsets[h+1]-1 of K_cache / V_cache ([rows, D], head after head, as
+// Algorithm 1 of "KVzap: Fast, Adaptive, and Faithful KV Cache Pruning"
+// returns keys[indices], values[indices]). Every KV head keeps its own number
+// of rows; the pages name that non-uniform cache as what a variable-length
+// kernel has to serve before pruning saves time or memory ("Limitation 3",
+// FAQ "Q4"). Output: o_j = sum_r a_jr v_r and LSE_j per decode query.
+//
+// The work is HBM-bound (each kept K and V row is read once per call), so it
+// is split by rows, flash-decoding style:
+//   * decode_partial: a wave owns a chunk of WROWS consecutive rows of one
+//     head and up to 8 of the head's query vectors (G heads x n_q tokens).
+//     A row is read by D/8 lanes, 16 bytes each (coalesced); the lanes'
+//     fp32 partial dot products are reduce-scattered in log2(D/8) shuffle
+//     steps so one lane ends with each query's score, which goes to LDS.
+//     The chunk max per query comes from LDS; then the value rows are read
+//     and o += exp2(s - m) v in fp32 (the lanes of a row own 8 dimensions
+//     each). The row groups of a wave are added with shuffles and the wave
+//     writes one partial (m, l, o) per query to the workspace.
+//   * decode_combine: one workgroup per decode query merges its head's
+//     partials (max, rescaled sums) and writes O (bf16) and LSE.
+//   Scores are kept in the exp2 domain (q is pre-scaled by scale * log2 e).
+//   Offsets are clamped to [0, capacity] and made monotone, so no offset
+//   can send a read outside the cache.
+#include <cmath>
+
+#include "common.hpp"
+#include "internal.hpp"
+
+namespace kvs {
+namespace {
+
+constexpr int DC_WAVES = 4;
+constexpr int DC_THREADS = DC_WAVES * WAVE;
+constexpr int WROWS = 256;  // rows per wave chunk
+constexpr int QG = 8;       // query vectors per wave
+
+struct DecParams {
+  const uint16_t* Q;
+  const uint16_t* K;
+  const uint16_t* V;
+  const int64_t* offs;
+  uint16_t* O;
+  float* lse;
+  float* part;  // [n_wchunks_max][G * n_q][2 + D]: m, l, o
+  int64_t q_hs, q_ts;
+  int64_t capacity;
+  int Hkv, G, n_q, nqg, n_wc_max;
+  float c2;  // scale * log2 e
+};
+
+__device__ __forceinline__ int64_t clamp_off(const DecParams& p, int h, int64_t prev) {
+  int64_t o = p.offs[h];
+  o = o < 0 ? 0 : (o > p.capacity ? p.capacity : o);
+  return o < prev ? prev : o;
+}
+
+// Head and chunk of global wave chunk wc; false past the last chunk.
+__device__ bool find_chunk(const DecParams& p, int wc, int& h, int64_t& r0, int64_t& r1) {
+  int64_t lo = clamp_off(p, 0, 0);
+  int cum = 0;
+  for (int k = 0; k < p.Hkv; ++k) {
+    const int64_t hi = clamp_off(p, k + 1, lo);
+    const int nc = (int)((hi - lo + WROWS - 1) / WROWS);
+    if (wc < cum + nc) {
+      h = k;
+      r0 = lo + (int64_t)(wc - cum) * WROWS;
+      r1 = min(r0 + WROWS, hi);
+      return true;
+    }
+    cum += nc;
+    lo = hi;
+  }
+  return false;
+}
+
+// Reduce-scatter of v[0..NV) over the LPR lanes of a row group (xor masks
+// LPR/2 .. 1): afterwards lane li holds the group sum of query
+// (li >> (log2 LPR - log2 NV)), in v[0].
+template <int LPR, int NV>
+__device__ __forceinline__ float reduce_scatter(float (&v)[NV], int li) {
+  static_assert(LPR >= NV, "at least one lane per query");
+  float* x = v;
+  int n = NV;
+  int mask = LPR / 2;
+#pragma unroll
+  for (int step = 0; step < 3; ++step) {  // NV = 8 -> 4 -> 2 -> 1
+    const int hf = n / 2;
+    const bool upper = (li & mask) != 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      if (j < hf) {
+        const float send = upper ? x[j] : x[hf + j];
+        const float keep = upper ? x[hf + j] : x[j];
+        x[j] = keep + __shfl_xor(send, mask);
+      }
+    }
+    n = hf;
+    mask >>= 1;
+  }
+  float s = x[0];
+  for (; mask >= 1; mask >>= 1) s += __shfl_xor(s, mask);
+  return s;
+}
+
+template <int D>
+__global__ __launch_bounds__(DC_THREADS) void decode_partial(DecParams p) {
+  constexpr int LPR = D / 8;            // lanes per row
+  constexpr int GPW = WAVE / LPR;       // row groups per wave
+  constexpr int UNROLL = 4;
+  __shared__ float s_score[DC_WAVES][WROWS][QG];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int li = lane % LPR, grp = lane / LPR;
+  const int wc = blockIdx.x * DC_WAVES + wave;
+  const int qg = blockIdx.y;
+  int h = 0;
+  int64_t r0 = 0, r1 = 0;
+  // waves past the last chunk do no work (nr = 0) but still reach the barrier
+  const bool active = find_chunk(p, wc, h, r0, r1);
+  const int nr = active ? (int)(r1 - r0) : 0;
+  const int nq_head = p.G * p.n_q;
+
+  // this wave's queries (f = qg*8 + t < G*n_q), 8 dims per lane, pre-scaled; absent ones are 0
+  float q[QG][8];
+#pragma unroll
+  for (int t = 0; t < QG; ++t) {
+    const int f = qg * QG + t;
+    if (f < nq_head) {
+      const int g = h * p.G + f / p.n_q, tok = f % p.n_q;
+      const u32x4 w = ld16(p.Q + (int64_t)g * p.q_hs + (int64_t)tok * p.q_ts + 8 * li);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        q[t][2 * e] = __uint_as_float(w[e] << 16) * p.c2;
+        q[t][2 * e + 1] = __uint_as_float(w[e] & 0xffff0000u) * p.c2;
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) q[t][e] = 0.f;
+    }
+  }
+
+  // ---- scores: rows r0 + grp + GPW*k
+  const uint16_t* Kb = p.K + r0 * D + 8 * li;
+  for (int k0 = 0; k0 * GPW < nr; k0 += UNROLL) {
+    u32x4 kv[UNROLL];
+#pragma unroll
+    for (int u = 0; u < UNROLL; ++u) {
+      const int rr = (k0 + u) * GPW + grp;
+      kv[u] = rr < nr ? __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(Kb + (int64_t)rr * D)) : u32x4{};
+    }
+#pragma unroll
+    for (int u = 0; u < UNROLL; ++u) {
+      const int rr = (k0 + u) * GPW + grp;
+      float kf[8];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        kf[2 * e] = __uint_as_float(kv[u][e] << 16);
+        kf[2 * e + 1] = __uint_as_float(kv[u][e] & 0xffff0000u);
+      }
+      float v[QG];
+#pragma unroll
+      for (int t = 0; t < QG; ++t) {
+        float a = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) a = __builtin_fmaf(q[t][e], kf[e], a);
+        v[t] = a;
+      }
+      const float s = reduce_scatter<LPR, QG>(v, li);
+      constexpr int SH = (LPR == 16) ? 1 : 0;  // lanes per query after the scatter: 2 (D=128) or 1 (D=64)
+      if (rr < nr && (li & ((1 << SH) - 1)) == 0) s_score[wave][rr][li >> SH] = s;
+    }
+  }
+  __syncthreads();  // scores visible (each wave reads only its own region)
+
+  // ---- chunk max per query: lane handles query lane/8 and rows lane%8 + 8k
+  float m;
+  {
+    const int t = lane >> 3, j0 = lane & 7;
+    float mx = -INFINITY;
+    for (int j = j0; j < nr; j += 8) mx = fmaxf(mx, s_score[wave][j][t]);
+    mx = fmaxf(mx, __shfl_xor(mx, 1));
+    mx = fmaxf(mx, __shfl_xor(mx, 2));
+    mx = fmaxf(mx, __shfl_xor(mx, 4));
+    m = mx;
+  }
+  float mq[QG];
+#pragma unroll
+  for (int t = 0; t < QG; ++t) mq[t] = __shfl(m, 8 * t);
+
+  // ---- values: o[t][e] += exp2(s - m) * v for this lane's 8 dimensions
+  float o[QG][8], l[QG];
+#pragma unroll
+  for (int t = 0; t < QG; ++t) {
+    l[t] = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o[t][e] = 0.f;
+  }
+  const uint16_t* Vb = p.V + r0 * D + 8 * li;
+  for (int k0 = 0; k0 * GPW < nr; k0 += UNROLL) {
+    u32x4 vv[UNROLL];
+#pragma unroll
+    for (int u = 0; u < UNROLL; ++u) {
+      const int rr = (k0 + u) * GPW + grp;
+      vv[u] = rr < nr ? __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(Vb + (int64_t)rr * D)) : u32x4{};
+    }
+#pragma unroll
+    for (int u = 0; u < UNROLL; ++u) {
+      const int rr = (k0 + u) * GPW + grp;
+      if (rr < nr) {
+        float vf[8];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          vf[2 * e] = __uint_as_float(vv[u][e] << 16);
+          vf[2 * e + 1] = __uint_as_float(vv[u][e] & 0xffff0000u);
+        }
+        const float4 sa = *reinterpret_cast<const float4*>(&s_score[wave][rr][0]);
+        const float4 sb = *reinterpret_cast<const float4*>(&s_score[wave][rr][4]);
+        const float sc[QG] = {sa.x, sa.y, sa.z, sa.w, sb.x, sb.y, sb.z, sb.w};
+#pragma unroll
+        for (int t = 0; t < QG; ++t) {
+          const float pr = fast_exp2(sc[t] - mq[t]);
+          l[t] += pr;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) o[t][e] = __builtin_fmaf(pr, vf[e], o[t][e]);
+        }
+      }
+    }
+  }
+
+  // ---- add the row groups of the wave (lanes li, li + LPR, ...) and write the partials
+#pragma unroll
+  for (int msk = LPR; msk < WAVE; msk <<= 1) {
+#pragma unroll
+    for (int t = 0; t < QG; ++t) {
+      l[t] += __shfl_xor(l[t], msk);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) o[t][e] += __shfl_xor(o[t][e], msk);
+    }
+  }
+  if (active && grp == 0) {
+#pragma unroll
+    for (int t = 0; t < QG; ++t) {
+      const int f = qg * QG + t;
+      if (f < nq_head) {
+        float* rec = p.part + ((int64_t)wc * nq_head + f) * (2 + D);
+        if (li == 0) {
+          rec[0] = mq[t];
+          rec[1] = l[t];
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) rec[2 + 8 * li + e] = o[t][e];
+      }
+    }
+  }
+}
+
+// One workgroup (D threads) per decode query: merge the head's partials.
+template <int D>
+__global__ __launch_bounds__(D) void decode_combine(DecParams p) {
+  const int g = blockIdx.x / p.n_q, tok = blockIdx.x % p.n_q;
+  const int h = g / p.G;
+  const int f = (g % p.G) * p.n_q + tok;
+  const int nq_head = p.G * p.n_q;
+  const int d = threadIdx.x;
+  // this head's wave chunks: [wc0, wc0 + nwc)
+  int64_t lo = clamp_off(p, 0, 0);
+  int wc0 = 0, nwc = 0;
+  for (int k = 0; k <= h; ++k) {
+    const int64_t hi = clamp_off(p, k + 1, lo);
+    const int nc = (int)((hi - lo + WROWS - 1) / WROWS);
+    if (k < h) wc0 += nc; else nwc = nc;
+    lo = hi;
+  }
+  float M = -INFINITY, L = 0.f, acc = 0.f;
+  for (int c = 0; c < nwc; ++c) {
+    const float* rec = p.part + ((int64_t)(wc0 + c) * nq_head + f) * (2 + D);
+    const float mc = rec[0], lc = rec[1], oc = rec[2 + d];
+    const float Mn = fmaxf(M, mc);
+    const float a = fast_exp2(M - Mn), b = fast_exp2(mc - Mn);  // M = -inf on the first chunk: a = 0
+    L = L * a + lc * b;
+    acc = acc * a + oc * b;
+    M = Mn;
+  }
+  uint16_t* orow = p.O + (int64_t)g * p.q_hs + (int64_t)tok * p.q_ts;
+  const float out = nwc > 0 ? acc / L : 0.f;
+  orow[d] = __builtin_bit_cast(uint16_t, (__bf16)out);
+  if (d == 0) p.lse[(int64_t)g * p.n_q + tok] = nwc > 0 ? (M + __log2f(L)) * LN2 : -INFINITY;
+}
+
+}  // namespace
+
+int64_t decode_wave_chunks_max(const kvs_decode_desc& d) { return d.capacity / WROWS + d.n_kvheads; }
+
+size_t decode_workspace_bytes(const kvs_decode_desc& d) {
+  const int64_t nq_head = (int64_t)(d.n_qheads / d.n_kvheads) * d.n_q;
+  return (size_t)decode_wave_chunks_max(d) * (size_t)nq_head * (size_t)(2 + d.head_dim) * sizeof(float);
+}
+
+hipError_t launch_decode(const kvs_decode_desc& d, const uint16_t* Q, const uint16_t* K, const uint16_t* V,
+                         const int64_t* offs, uint16_t* O, float* lse, void* workspace, hipStream_t s) {
+  DecParams p{};
+  p.Q = Q; p.K = K; p.V = V; p.offs = offs; p.O = O; p.lse = lse;
+  p.part = static_cast<float*>(workspace);
+  p.q_hs = d.q_head_stride; p.q_ts = d.q_tok_stride;
+  p.capacity = d.capacity;
+  p.Hkv = d.n_kvheads; p.G = d.n_qheads / d.n_kvheads; p.n_q = d.n_q;
+  p.nqg = (p.G * p.n_q + QG - 1) / QG;
+  p.n_wc_max = (int)decode_wave_chunks_max(d);
+  p.c2 = d.scale * LOG2E;
+  const dim3 grid1((unsigned)((p.n_wc_max + DC_WAVES - 1) / DC_WAVES), (unsigned)p.nqg);
+  const dim3 grid2((unsigned)(d.n_qheads * d.n_q));
+  if (d.head_dim == 128) {
+    hipLaunchKernelGGL(decode_partial<128>, grid1, dim3(DC_THREADS), 0, s, p);
+    hipLaunchKernelGGL(decode_combine<128>, grid2, dim3(128), 0, s, p);
+  } else {
+    hipLaunchKernelGGL(decode_partial<64>, grid1, dim3(DC_THREADS), 0, s, p);
+    hipLaunchKernelGGL(decode_combine<64>, grid2, dim3(64), 0, s, p);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace kvs

@@ -25,6 +25,11 @@ hipError_t launch_attn(const kvs_attn_desc& d, const uint16_t* Q, const uint16_t
 hipError_t launch_vnorm(const kvs_vnorm_desc& d, const uint16_t* V, const uint16_t* W_O, float* vnorm,
                         hipStream_t s);
 
+size_t decode_workspace_bytes(const kvs_decode_desc& d);
+
+hipError_t launch_decode(const kvs_decode_desc& d, const uint16_t* Q, const uint16_t* K, const uint16_t* V,
+                         const int64_t* offs, uint16_t* O, float* lse, void* workspace, hipStream_t s);
+
 size_t evict_workspace_bytes(const kvs_evict_desc& e);
 
 hipError_t launch_evict(const kvs_evict_desc& e, const float* scores, const uint16_t* K, const uint16_t* V,

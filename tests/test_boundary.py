@@ -184,6 +184,49 @@ def test_vnorm_rejects_pointers(L):
     assert L.kvscore_vnorm(ctypes.byref(d), FAKE, ctypes.c_void_p(0x100008), FAKE, None) == kvs.KVS_EUNSUPPORTED
 
 
+def _ddesc(**kw):
+    d = kvs.DecodeDesc()
+    d.n_qheads, d.n_kvheads, d.head_dim, d.n_q = 8, 2, 128, 1
+    d.q_head_stride, d.q_tok_stride, d.capacity = 128, 128, 1000
+    d.scale, d.reserved = 0.088, 0
+    for k, v in kw.items():
+        setattr(d, k, v)
+    return d
+
+
+DECODE_BAD = [
+    (dict(reserved=1), kvs.KVS_EINVAL),
+    (dict(n_qheads=7), kvs.KVS_EINVAL),
+    (dict(head_dim=96), kvs.KVS_EUNSUPPORTED),
+    (dict(n_q=0), kvs.KVS_EINVAL),
+    (dict(capacity=-1), kvs.KVS_EINVAL),
+    (dict(scale=float("inf")), kvs.KVS_EINVAL),
+    (dict(q_head_stride=100), kvs.KVS_EUNSUPPORTED),
+    (dict(n_q=2, q_tok_stride=64), kvs.KVS_EINVAL),
+]
+
+
+@pytest.mark.parametrize("kw,code", DECODE_BAD)
+def test_decode_rejects(L, kw, code):
+    d = _ddesc(**kw)
+    assert L.kvscore_decode(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 30, None) == code
+    assert L.kvscore_decode_workspace_bytes(ctypes.byref(d)) == 0
+
+
+def test_decode_workspace_and_pointers(L):
+    d = _ddesc()
+    need = L.kvscore_decode_workspace_bytes(ctypes.byref(d))
+    # (1000 // 256 + 2) wave chunks x 4 queries per KV head x (2 + 128) floats
+    assert need == (1000 // 256 + 2) * 4 * 130 * 4
+    D = L.kvscore_decode
+    assert D(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, need - 1, None) == kvs.KVS_EWORKSPACE
+    assert D(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, need, None) == kvs.KVS_EWORKSPACE
+    assert D(ctypes.byref(d), FAKE, None, FAKE, FAKE, FAKE, FAKE, FAKE, need, None) == kvs.KVS_EINVAL
+    assert D(ctypes.byref(d), FAKE, FAKE, FAKE, None, FAKE, FAKE, FAKE, need, None) == kvs.KVS_EINVAL
+    assert D(ctypes.byref(d), ctypes.c_void_p(0x100008), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, need,
+             None) == kvs.KVS_EUNSUPPORTED
+
+
 def test_max_and_futuremass_reject(L):
     d = _desc()
     assert L.kvscore_max(ctypes.byref(d), FAKE, FAKE, FAKE, None, None, FAKE, 2, None) == kvs.KVS_EINVAL
