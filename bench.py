@@ -14,8 +14,9 @@ Also reported: per-kernel times (HIP events on the launch stream), the score
 pass's TFLOP/s against the bf16 MFMA peak (roofline), the LSE pass's
 TFLOP/s, eviction GB/s against HBM peak, the CPU oracle timed on a
 bounded sample of the same workload, and (under "adjacent", timed after the
-step and not part of it) the attention forward that also returns O and the
-value-norm kernel that produces the vnorm input.
+step and not part of it) the attention forward that also returns O, the
+value-norm kernel that produces the vnorm input, and decode attention of one
+new token per query head over the cache this step compacted.
 
     python bench.py [--gpus 1] [--steps 10] [--warmup 3] [--no-cpu-baseline]
 """
@@ -244,6 +245,14 @@ def main():
                                        "frac_of_bf16_peak": vn_tflops / PEAK_BF16_TFLOPS,
                                        "d_model": int(d["WO"].shape[0])}
             del WO, vn_out
+        # decode over the cache this step compacted: one new token per query head
+        Qd = Q[:, -1:, :].contiguous()
+        dd = kvs.decode_desc(Qd, outs[2], r.Hkv, scale)
+        dws = torch.empty(max(kvs.decode_workspace_bytes(dd), 16), dtype=torch.uint8, device="cuda")
+        Od, Ld = torch.empty_like(Qd), torch.empty((r.Hq, 1), dtype=torch.float32, device="cuda")
+        t_dec = timed(lambda: kvs.decode(Qd, outs[2], outs[3], outs[1], scale=scale, workspace=dws, out=Od, lse_out=Ld),
+                      reps=20)
+        del Qd, dws, Od, Ld
     offs = outs[1].cpu().numpy()
     kept = np.diff(offs)
     kept_total = int(offs[-1])
@@ -295,6 +304,10 @@ def main():
         attn_tflops = 2 * lse_flops / (t_attn * 1e-3) / 1e12
         adjacent["attention"] = {"entry": "kvscore_attention", "ms": t_attn, "flops": 2 * lse_flops,
                                  "tflops": attn_tflops, "frac_of_bf16_peak": attn_tflops / PEAK_BF16_TFLOPS}
+        dec_bytes = kept_total * 2 * r.D * 2 + r.Hq * r.D * 2 * 2  # kept K and V rows, plus Q and O
+        adjacent["decode"] = {"entry": "kvscore_decode", "ms": t_dec, "queries_per_head": 1, "rows": kept_total,
+                              "bytes": dec_bytes, "gbs": dec_bytes / (t_dec * 1e-3) / 1e9,
+                              "frac_of_hbm_peak": dec_bytes / (t_dec * 1e-3) / 1e9 / PEAK_HBM_GBS}
         out["adjacent"] = adjacent
     print(json.dumps(out), flush=True)
 
