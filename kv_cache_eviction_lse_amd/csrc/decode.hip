@@ -10,16 +10,19 @@
 // The work is HBM-bound (each kept K and V row is read once per call), so it
 // is split by rows, flash-decoding style:
 //   * decode_partial: a wave owns a chunk of WROWS consecutive rows of one
-//     head and up to 8 of the head's query vectors (G heads x n_q tokens).
-//     A row is read by D/8 lanes, 16 bytes each (coalesced); the lanes'
-//     fp32 partial dot products are reduce-scattered in log2(D/8) shuffle
-//     steps so one lane ends with each query's score, which goes to LDS.
-//     The chunk max per query comes from LDS; then the value rows are read
-//     and o += exp2(s - m) v in fp32 (the lanes of a row own 8 dimensions
+//     head and 4 or 8 of the head's query vectors (G heads x n_q tokens;
+//     4 when the head has at most 4). A row is read by D/8 lanes, 16 bytes
+//     each (coalesced); the lanes' fp32 partial dot products are
+//     reduce-scattered in shuffle steps so one lane ends with each query's
+//     score, which goes to LDS. The chunk max and p = exp2(s - m) are then
+//     computed once per (row, query) in LDS, with l = sum p; the value rows
+//     are read and o += p v in fp32 (the lanes of a row own 8 dimensions
 //     each). The row groups of a wave are added with shuffles and the wave
 //     writes one partial (m, l, o) per query to the workspace.
 //   * decode_combine: one workgroup per decode query merges its head's
-//     partials (max, rescaled sums) and writes O (bf16) and LSE.
+//     partials (max, rescaled sums; 1024 threads = chunk groups x
+//     dimensions, groups merged through LDS in a fixed order) and writes O
+//     (bf16) and LSE.
 //   Scores are kept in the exp2 domain (q is pre-scaled by scale * log2 e).
 //   Offsets are clamped to [0, capacity] and made monotone, so no offset
 //   can send a read outside the cache.
@@ -33,8 +36,8 @@ namespace {
 
 constexpr int DC_WAVES = 4;
 constexpr int DC_THREADS = DC_WAVES * WAVE;
-constexpr int WROWS = 256;  // rows per wave chunk
-constexpr int QG = 8;       // query vectors per wave
+constexpr int WROWS = 128;  // rows per wave chunk
+constexpr int QG_MAX = 8;   // query vectors per wave (4 when a head has at most 4)
 
 struct DecParams {
   const uint16_t* Q;
@@ -76,40 +79,40 @@ __device__ bool find_chunk(const DecParams& p, int wc, int& h, int64_t& r0, int6
 }
 
 // Reduce-scatter of v[0..NV) over the LPR lanes of a row group (xor masks
-// LPR/2 .. 1): afterwards lane li holds the group sum of query
-// (li >> (log2 LPR - log2 NV)), in v[0].
+// LPR/2, LPR/4, ...): each step hands the partner the half of the values it
+// keeps and adds the half it receives, so after log2(NV) steps lane li holds
+// the partial sum of query (li >> (log2 LPR - log2 NV)); the remaining masks
+// complete the sum. Returned in v[0].
 template <int LPR, int NV>
 __device__ __forceinline__ float reduce_scatter(float (&v)[NV], int li) {
-  static_assert(LPR >= NV, "at least one lane per query");
-  float* x = v;
-  int n = NV;
+  static_assert(LPR >= NV && (NV == 4 || NV == 8), "4 or 8 values, at least one lane per value");
   int mask = LPR / 2;
 #pragma unroll
-  for (int step = 0; step < 3; ++step) {  // NV = 8 -> 4 -> 2 -> 1
+  for (int n = NV; n > 1; n /= 2) {
     const int hf = n / 2;
     const bool upper = (li & mask) != 0;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int j = 0; j < NV / 2; ++j) {
       if (j < hf) {
-        const float send = upper ? x[j] : x[hf + j];
-        const float keep = upper ? x[hf + j] : x[j];
-        x[j] = keep + __shfl_xor(send, mask);
+        const float send = upper ? v[j] : v[hf + j];
+        const float keep = upper ? v[hf + j] : v[j];
+        v[j] = keep + __shfl_xor(send, mask);
       }
     }
-    n = hf;
     mask >>= 1;
   }
-  float s = x[0];
+  float s = v[0];
   for (; mask >= 1; mask >>= 1) s += __shfl_xor(s, mask);
   return s;
 }
 
-template <int D>
+template <int D, int QG>
 __global__ __launch_bounds__(DC_THREADS) void decode_partial(DecParams p) {
   constexpr int LPR = D / 8;            // lanes per row
   constexpr int GPW = WAVE / LPR;       // row groups per wave
-  constexpr int UNROLL = 4;
-  __shared__ float s_score[DC_WAVES][WROWS][QG];
+  constexpr int UNROLL = 8;             // rows per group in flight per batch
+  constexpr int LPQ = WAVE / QG;        // lanes per query in the softmax phase
+  __shared__ __attribute__((aligned(16))) float s_score[DC_WAVES][WROWS][QG];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -170,35 +173,45 @@ __global__ __launch_bounds__(DC_THREADS) void decode_partial(DecParams p) {
         v[t] = a;
       }
       const float s = reduce_scatter<LPR, QG>(v, li);
-      constexpr int SH = (LPR == 16) ? 1 : 0;  // lanes per query after the scatter: 2 (D=128) or 1 (D=64)
+      constexpr int SH = (LPR / QG == 4) ? 2 : ((LPR / QG == 2) ? 1 : 0);  // log2 lanes per query after the scatter
       if (rr < nr && (li & ((1 << SH) - 1)) == 0) s_score[wave][rr][li >> SH] = s;
     }
   }
   __syncthreads();  // scores visible (each wave reads only its own region)
 
-  // ---- chunk max per query: lane handles query lane/8 and rows lane%8 + 8k
-  float m;
+  // ---- softmax of the chunk, once per (row, query): lane handles query
+  // lane / LPQ and rows lane % LPQ + LPQ*k; the scores become p = exp2(s - m)
+  // in place, and l = sum p
+  float m, lsum = 0.f;
   {
-    const int t = lane >> 3, j0 = lane & 7;
+    const int t = lane / LPQ, j0 = lane % LPQ;
     float mx = -INFINITY;
-    for (int j = j0; j < nr; j += 8) mx = fmaxf(mx, s_score[wave][j][t]);
-    mx = fmaxf(mx, __shfl_xor(mx, 1));
-    mx = fmaxf(mx, __shfl_xor(mx, 2));
-    mx = fmaxf(mx, __shfl_xor(mx, 4));
-    m = mx;
-  }
-  float mq[QG];
+    for (int j = j0; j < nr; j += LPQ) mx = fmaxf(mx, s_score[wave][j][t]);
 #pragma unroll
-  for (int t = 0; t < QG; ++t) mq[t] = __shfl(m, 8 * t);
-
-  // ---- values: o[t][e] += exp2(s - m) * v for this lane's 8 dimensions
-  float o[QG][8], l[QG];
+    for (int msk = 1; msk < LPQ; msk <<= 1) mx = fmaxf(mx, __shfl_xor(mx, msk));
+    m = mx;
+    for (int j = j0; j < nr; j += LPQ) {
+      const float pr = fast_exp2(s_score[wave][j][t] - mx);
+      s_score[wave][j][t] = pr;
+      lsum += pr;
+    }
+#pragma unroll
+    for (int msk = 1; msk < LPQ; msk <<= 1) lsum += __shfl_xor(lsum, msk);
+  }
+  __syncthreads();  // probabilities visible
+  float mq[QG], l[QG];
 #pragma unroll
   for (int t = 0; t < QG; ++t) {
-    l[t] = 0.f;
+    mq[t] = __shfl(m, LPQ * t);
+    l[t] = __shfl(lsum, LPQ * t);
+  }
+
+  // ---- values: o[t][e] += exp2(s - m) * v for this lane's 8 dimensions
+  float o[QG][8];
+#pragma unroll
+  for (int t = 0; t < QG; ++t)
 #pragma unroll
     for (int e = 0; e < 8; ++e) o[t][e] = 0.f;
-  }
   const uint16_t* Vb = p.V + r0 * D + 8 * li;
   for (int k0 = 0; k0 * GPW < nr; k0 += UNROLL) {
     u32x4 vv[UNROLL];
@@ -217,16 +230,19 @@ __global__ __launch_bounds__(DC_THREADS) void decode_partial(DecParams p) {
           vf[2 * e] = __uint_as_float(vv[u][e] << 16);
           vf[2 * e + 1] = __uint_as_float(vv[u][e] & 0xffff0000u);
         }
-        const float4 sa = *reinterpret_cast<const float4*>(&s_score[wave][rr][0]);
-        const float4 sb = *reinterpret_cast<const float4*>(&s_score[wave][rr][4]);
-        const float sc[QG] = {sa.x, sa.y, sa.z, sa.w, sb.x, sb.y, sb.z, sb.w};
+        float pr[QG];
 #pragma unroll
-        for (int t = 0; t < QG; ++t) {
-          const float pr = fast_exp2(sc[t] - mq[t]);
-          l[t] += pr;
-#pragma unroll
-          for (int e = 0; e < 8; ++e) o[t][e] = __builtin_fmaf(pr, vf[e], o[t][e]);
+        for (int t4 = 0; t4 < QG; t4 += 4) {
+          const float4 pa = *reinterpret_cast<const float4*>(&s_score[wave][rr][t4]);
+          pr[t4] = pa.x;
+          pr[t4 + 1] = pa.y;
+          pr[t4 + 2] = pa.z;
+          pr[t4 + 3] = pa.w;
         }
+#pragma unroll
+        for (int t = 0; t < QG; ++t)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) o[t][e] = __builtin_fmaf(pr[t], vf[e], o[t][e]);
       }
     }
   }
@@ -235,11 +251,9 @@ __global__ __launch_bounds__(DC_THREADS) void decode_partial(DecParams p) {
 #pragma unroll
   for (int msk = LPR; msk < WAVE; msk <<= 1) {
 #pragma unroll
-    for (int t = 0; t < QG; ++t) {
-      l[t] += __shfl_xor(l[t], msk);
+    for (int t = 0; t < QG; ++t)
 #pragma unroll
       for (int e = 0; e < 8; ++e) o[t][e] += __shfl_xor(o[t][e], msk);
-    }
   }
   if (active && grp == 0) {
 #pragma unroll
@@ -258,14 +272,20 @@ __global__ __launch_bounds__(DC_THREADS) void decode_partial(DecParams p) {
   }
 }
 
-// One workgroup (D threads) per decode query: merge the head's partials.
+// One workgroup of 1024 threads per decode query merges the head's partials:
+// NG = 1024 / D chunk groups (thread = group x dimension) each merge every
+// NG-th chunk, then the groups are merged through LDS, in a fixed order.
+constexpr int CB_THREADS = 1024;
+
 template <int D>
-__global__ __launch_bounds__(D) void decode_combine(DecParams p) {
+__global__ __launch_bounds__(CB_THREADS) void decode_combine(DecParams p) {
+  constexpr int NG = CB_THREADS / D;
+  __shared__ float s_m[NG], s_l[NG], s_o[NG][D];
   const int g = blockIdx.x / p.n_q, tok = blockIdx.x % p.n_q;
   const int h = g / p.G;
   const int f = (g % p.G) * p.n_q + tok;
   const int nq_head = p.G * p.n_q;
-  const int d = threadIdx.x;
+  const int d = threadIdx.x % D, cg = threadIdx.x / D;
   // this head's wave chunks: [wc0, wc0 + nwc)
   int64_t lo = clamp_off(p, 0, 0);
   int wc0 = 0, nwc = 0;
@@ -276,19 +296,38 @@ __global__ __launch_bounds__(D) void decode_combine(DecParams p) {
     lo = hi;
   }
   float M = -INFINITY, L = 0.f, acc = 0.f;
-  for (int c = 0; c < nwc; ++c) {
+#pragma unroll 4
+  for (int c = cg; c < nwc; c += NG) {
     const float* rec = p.part + ((int64_t)(wc0 + c) * nq_head + f) * (2 + D);
     const float mc = rec[0], lc = rec[1], oc = rec[2 + d];
     const float Mn = fmaxf(M, mc);
-    const float a = fast_exp2(M - Mn), b = fast_exp2(mc - Mn);  // M = -inf on the first chunk: a = 0
+    const float a = fast_exp2(M - Mn), b = fast_exp2(mc - Mn);  // M = -inf on a group's first chunk: a = 0
     L = L * a + lc * b;
     acc = acc * a + oc * b;
     M = Mn;
   }
-  uint16_t* orow = p.O + (int64_t)g * p.q_hs + (int64_t)tok * p.q_ts;
-  const float out = nwc > 0 ? acc / L : 0.f;
-  orow[d] = __builtin_bit_cast(uint16_t, (__bf16)out);
-  if (d == 0) p.lse[(int64_t)g * p.n_q + tok] = nwc > 0 ? (M + __log2f(L)) * LN2 : -INFINITY;
+  if (d == 0) {
+    s_m[cg] = M;
+    s_l[cg] = L;
+  }
+  s_o[cg][d] = acc;
+  __syncthreads();
+  if (cg == 0) {
+    float Mt = -INFINITY;
+#pragma unroll
+    for (int k = 0; k < NG; ++k) Mt = fmaxf(Mt, s_m[k]);
+    float Lt = 0.f, ot = 0.f;
+#pragma unroll
+    for (int k = 0; k < NG; ++k) {
+      const float w = s_m[k] == -INFINITY ? 0.f : fast_exp2(s_m[k] - Mt);  // groups with no chunk count 0
+      Lt += s_l[k] * w;
+      ot += s_o[k][d] * w;
+    }
+    uint16_t* orow = p.O + (int64_t)g * p.q_hs + (int64_t)tok * p.q_ts;
+    const float out = nwc > 0 ? ot / Lt : 0.f;
+    orow[d] = __builtin_bit_cast(uint16_t, (__bf16)out);
+    if (d == 0) p.lse[(int64_t)g * p.n_q + tok] = nwc > 0 ? (Mt + __log2f(Lt)) * LN2 : -INFINITY;
+  }
 }
 
 }  // namespace
@@ -308,17 +347,24 @@ hipError_t launch_decode(const kvs_decode_desc& d, const uint16_t* Q, const uint
   p.q_hs = d.q_head_stride; p.q_ts = d.q_tok_stride;
   p.capacity = d.capacity;
   p.Hkv = d.n_kvheads; p.G = d.n_qheads / d.n_kvheads; p.n_q = d.n_q;
-  p.nqg = (p.G * p.n_q + QG - 1) / QG;
+  const int qg = p.G * p.n_q <= 4 ? 4 : QG_MAX;
+  p.nqg = (p.G * p.n_q + qg - 1) / qg;
   p.n_wc_max = (int)decode_wave_chunks_max(d);
   p.c2 = d.scale * LOG2E;
   const dim3 grid1((unsigned)((p.n_wc_max + DC_WAVES - 1) / DC_WAVES), (unsigned)p.nqg);
   const dim3 grid2((unsigned)(d.n_qheads * d.n_q));
   if (d.head_dim == 128) {
-    hipLaunchKernelGGL(decode_partial<128>, grid1, dim3(DC_THREADS), 0, s, p);
-    hipLaunchKernelGGL(decode_combine<128>, grid2, dim3(128), 0, s, p);
+    if (qg == 4)
+      hipLaunchKernelGGL((decode_partial<128, 4>), grid1, dim3(DC_THREADS), 0, s, p);
+    else
+      hipLaunchKernelGGL((decode_partial<128, 8>), grid1, dim3(DC_THREADS), 0, s, p);
+    hipLaunchKernelGGL(decode_combine<128>, grid2, dim3(CB_THREADS), 0, s, p);
   } else {
-    hipLaunchKernelGGL(decode_partial<64>, grid1, dim3(DC_THREADS), 0, s, p);
-    hipLaunchKernelGGL(decode_combine<64>, grid2, dim3(64), 0, s, p);
+    if (qg == 4)
+      hipLaunchKernelGGL((decode_partial<64, 4>), grid1, dim3(DC_THREADS), 0, s, p);
+    else
+      hipLaunchKernelGGL((decode_partial<64, 8>), grid1, dim3(DC_THREADS), 0, s, p);
+    hipLaunchKernelGGL(decode_combine<64>, grid2, dim3(CB_THREADS), 0, s, p);
   }
   return hipGetLastError();
 }

@@ -216,8 +216,8 @@ def test_decode_rejects(L, kw, code):
 def test_decode_workspace_and_pointers(L):
     d = _ddesc()
     need = L.kvscore_decode_workspace_bytes(ctypes.byref(d))
-    # (1000 // 256 + 2) wave chunks x 4 queries per KV head x (2 + 128) floats
-    assert need == (1000 // 256 + 2) * 4 * 130 * 4
+    # (1000 // 128 + 2) wave chunks x 4 queries per KV head x (2 + 128) floats
+    assert need == (1000 // 128 + 2) * 4 * 130 * 4
     D = L.kvscore_decode
     assert D(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, need - 1, None) == kvs.KVS_EWORKSPACE
     assert D(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, need, None) == kvs.KVS_EWORKSPACE

@@ -3,7 +3,7 @@ the CPU oracle through the C ABI: ragged and empty heads, D = 64 and 128,
 several query groups per head, clamped offsets, and the full pipeline
 kv_evict -> kvscore_decode against oracle select -> compact -> decode.
 
-Tolerance: scores, exponentials and sums are fp32 (chunks of 256 rows, then a
+Tolerance: scores, exponentials and sums are fp32 (chunks of 128 rows, then a
 merge over chunks), so the summation error stays far below 2^-12 of
 sum_r a_r |v_r|; O is rounded once to bf16 (2^-8 |O|):
     |O_gpu - O_ref| <= 2^-8 |O_ref| + 2^-12 sum_r a_r |v_r|,  |LSE err| <= 1e-3,
@@ -48,7 +48,7 @@ def _case(seed, Hq, Hkv, D, counts, n_q):
 CASES = [
     # name, Hq, Hkv, D, rows per head, n_q
     ("d64-ragged-and-empty-head", 6, 3, 64, [300, 0, 517], 2),
-    ("d128-g4-chunk-edges", 16, 4, 128, [1, 256, 257, 1000], 1),
+    ("d128-g4-chunk-edges", 16, 4, 128, [1, 128, 129, 3000], 1),
     ("g5-three-tokens-two-query-groups", 10, 2, 128, [700, 45], 3),
     ("mha-one-row", 4, 4, 128, [1, 2, 3, 4], 1),
 ]
