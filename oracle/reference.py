@@ -297,7 +297,7 @@ def value_norms(V, W_O, n_kvheads):
     return out
 
 
-def select(scores, window, k=None, tau=None):
+def select(scores, window, k=None, tau=None, scope="head"):
     """Kept positions per KV head, ascending, as a list of int64 arrays.
 
     The last ``window`` positions are always kept ([KVzap] thresholding rule and
@@ -306,12 +306,32 @@ def select(scores, window, k=None, tau=None):
       "Thresholding"): the min(k, candidates) best by (score descending,
       position ascending);
     * threshold: keep iff score >= tau ([KVzap] thresholding rule, Algorithm 1).
+    ``scope="layer"`` (top-k only) ranks the candidates of all heads together,
+    the layer-wise top-k that [KVzap] §4.6 "threshold vs fixed ratio"
+    compares against: the min(k, all candidates) best by (score descending,
+    head ascending, position ascending), so each head keeps its own share.
     NaN scores rank below every number and never pass the threshold; -0 and +0
     are equal. Output order is ascending position, as a where() over the mask.
     """
     if (k is None) == (tau is None):
         raise ValueError("give exactly one of k, tau")
+    if scope not in ("head", "layer"):
+        raise ValueError(scope)
     s_all = np.asarray(scores, dtype=np.float64)
+    if scope == "layer" and k is not None:
+        Hkv, n = s_all.shape
+        w = min(max(int(window), 0), n)
+        heads = np.repeat(np.arange(Hkv), n - w)
+        pos = np.tile(np.arange(n - w), Hkv)
+        vals = s_all[:, : n - w].reshape(-1)
+        is_nan = np.isnan(vals)
+        neg = np.where(is_nan, 0.0, -vals)
+        kk = min(max(int(k), 0), vals.size)
+        order = np.lexsort((pos, heads, neg, is_nan))  # NaN last, then -score, head, position
+        keep = np.zeros((Hkv, n), dtype=bool)
+        keep[:, n - w:] = True
+        keep[heads[order[:kk]], pos[order[:kk]]] = True
+        return [np.nonzero(keep[h])[0].astype(np.int64) for h in range(Hkv)]
     out = []
     for h in range(s_all.shape[0]):
         s = s_all[h]

@@ -494,6 +494,38 @@ def pin_select_ties_lower_index_first():
     assert oracle.select(z, 0, tau=0.0)[0].tolist() == [0, 1, 2, 3]
 
 
+def pin_select_layer_scope_library_order():
+    """Layer scope: Python's sort of (-score, head, position) over every head's
+    candidates, first k, plus each head's window."""
+    s = _sel_scores()
+    Hkv, n = s.shape
+    for k, w in [(0, 3), (7, 0), (25, 5), (10 ** 6, 4)]:
+        got = oracle.select(s, w, k=k, scope="layer")
+        cand = [(h, i) for h in range(Hkv) for i in range(n - w)]
+        rank = sorted(cand, key=lambda hi: (math.isnan(s[hi]), 0.0 if math.isnan(s[hi]) else -float(s[hi]),
+                                            hi[0], hi[1]))
+        want = [set(range(n - w, n)) for _ in range(Hkv)]
+        for h, i in rank[:min(k, len(cand))]:
+            want[h].add(i)
+        for h in range(Hkv):
+            assert list(got[h]) == sorted(want[h]), (k, w, h)
+
+
+def pin_select_layer_scope_budget_follows_scores():
+    """Head h's candidates all outscore head h+1's: a layer budget of k fills
+    the heads in order (head 0 first), whatever the per-head share."""
+    Hkv, n, w = 3, 20, 2
+    s = np.stack([np.linspace(1.0, 0.9, n) + (Hkv - h) for h in range(Hkv)]).astype(np.float32)
+    got = oracle.select(s, w, k=25, scope="layer")
+    assert [g.size for g in got] == [18 + w, 7 + w, w]
+    # equal scores in every head: ties go to the lower head, then the lower position
+    t = np.tile(np.array([5, 9, 9, 1, 7, 3], dtype=np.float32), (3, 1))
+    got = oracle.select(t, 0, k=4, scope="layer")
+    assert [list(g) for g in got] == [[1, 2], [1, 2], []]
+    same = oracle.select(s, w, tau=2.5, scope="layer")  # scope plays no part under a threshold
+    assert all(np.array_equal(a, b) for a, b in zip(same, oracle.select(s, w, tau=2.5)))
+
+
 def pin_select_threshold_is_ge():
     """Keep iff score >= tau (Algorithm 1's comparison), window always kept."""
     s = np.array([[0.1, 0.2, 0.3, 0.2, 0.05, 0.0]], dtype=np.float32)

@@ -41,6 +41,9 @@ MUTANTS = {
                               "r0, r1 = int(offs[(h + 1) % Hkv]), int(offs[(h + 1) % Hkv + 1])"),
     "decode-unnormalised": ("O[g] = (E / tot) @ Vf[r0:r1]", "O[g] = E @ Vf[r0:r1]"),
     "decode-last-row-dropped": ("L = scale * (Qf[g] @ Kf[r0:r1].T)", "r1 = max(r0 + 1, r1 - 1)\n        L = scale * (Qf[g] @ Kf[r0:r1].T)"),
+    "layer-ties-head-descending": ("order = np.lexsort((pos, heads, neg, is_nan))",
+                                   "order = np.lexsort((pos, -heads, neg, is_nan))"),
+    "layer-scope-per-head-k": ("kk = min(max(int(k), 0), vals.size)", "kk = min(max(int(k), 0), n - w)"),
     "window-not-kept": ("keep[n - w:] = True", "pass"),
     "threshold-strict": ("keep[cand] |= s[cand] >= float(np.float32(tau))", "keep[cand] |= s[cand] > float(np.float32(tau))"),
     "ties-higher-index-first": ("order = np.lexsort((cand, neg, is_nan))", "order = np.lexsort((-cand, neg, is_nan))"),
