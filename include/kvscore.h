@@ -69,6 +69,9 @@ enum { KVS_MASK_REPEAT = 0, KVS_MASK_CAUSAL = 1 };
 
 typedef uint16_t kvs_bf16; /* bfloat16 bit pattern */
 
+/* Eviction budget scope (kvs_evict_desc.scope). */
+enum { KVS_SCOPE_HEAD = 0, KVS_SCOPE_LAYER = 1 };
+
 /* Shape of one layer's attention, shared by the three scoring calls.
  *   Q      [n_qheads, n_q, head_dim]    strides q_head_stride, q_tok_stride
  *   K      [n_kvheads, n_ctx, head_dim] strides k_head_stride, k_tok_stride
@@ -182,6 +185,12 @@ int kvscore_vnorm(const kvs_vnorm_desc* d, const kvs_bf16* V,
  *            highest scores; equal scores are taken lowest position first,
  *            -0 equals +0 and NaN ranks below every number;
  *   threshold (k < 0): plus the other positions with score >= tau.
+ * scope = KVS_SCOPE_LAYER with k >= 0 (the layer-wise top-k the KVzap page's
+ *   §4.6 ablation compares thresholds against): one budget of min(k, all
+ *   candidates) for the whole layer instead of k per head; the candidates of
+ *   all heads are ranked together (equal scores: lower head first, then
+ *   lower position), each head keeps its window and its share. Needs
+ *   n_kvheads * n_tok < 2^31. Under a threshold the scope plays no part.
  * Outputs (device):
  *   head_offsets [n_kvheads + 1] int64: rows of head h are
  *                head_offsets[h] .. head_offsets[h+1]-1; [n_kvheads] = total
@@ -189,7 +198,8 @@ int kvscore_vnorm(const kvs_vnorm_desc* d, const kvs_bf16* V,
  *                within a head
  *   K_out, V_out [capacity, head_dim] bf16, dense: bit copies of the rows.
  * capacity must cover the worst case: n_kvheads * (min(k, n_tok - w) + w) in
- * top-k mode, n_kvheads * n_tok in threshold mode (where the count is only
+ * top-k mode (n_kvheads * w + min(k, n_kvheads * (n_tok - w)) with a layer
+ * budget), n_kvheads * n_tok in threshold mode (where the count is only
  * known on the device; read head_offsets after synchronising).
  * workspace: device memory of at least kv_evict_workspace_bytes(e) bytes,
  * 256-byte aligned, owned by the caller, contents need not be initialised. */
@@ -199,7 +209,7 @@ typedef struct kvs_evict_desc {
   int64_t n_tok;
   int64_t k;
   float tau;
-  int32_t reserved; /* set to 0 */
+  int32_t scope;    /* KVS_SCOPE_HEAD (0) or KVS_SCOPE_LAYER (1), see above */
   int64_t window;
   int64_t capacity;
   int64_t kv_head_stride, kv_tok_stride;

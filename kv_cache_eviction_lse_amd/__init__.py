@@ -54,7 +54,7 @@ class EvictDesc(ctypes.Structure):
     _fields_ = [
         ("n_kvheads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
         ("n_tok", ctypes.c_int64), ("k", ctypes.c_int64),
-        ("tau", ctypes.c_float), ("reserved", ctypes.c_int32),
+        ("tau", ctypes.c_float), ("scope", ctypes.c_int32),
         ("window", ctypes.c_int64), ("capacity", ctypes.c_int64),
         ("kv_head_stride", ctypes.c_int64), ("kv_tok_stride", ctypes.c_int64),
         ("score_head_stride", ctypes.c_int64),
@@ -328,18 +328,28 @@ def future_mass(Q, K, lse_vals, *, scale: float, window: int, vnorm=None, hnorm=
     return out
 
 
-def evict_desc(scores, K, *, window: int, k=None, tau=None, capacity=None) -> EvictDesc:
+SCOPE_HEAD, SCOPE_LAYER = 0, 1
+
+
+def evict_desc(scores, K, *, window: int, k=None, tau=None, capacity=None, scope: str = "head") -> EvictDesc:
     if (k is None) == (tau is None):
         raise ValueError("give exactly one of k, tau")
+    if scope not in ("head", "layer"):
+        raise ValueError("scope must be 'head' or 'layer'")
     Hkv, n, D = K.shape
     e = EvictDesc()
     e.n_kvheads, e.head_dim, e.n_tok = Hkv, D, n
     e.k = int(k) if k is not None else -1
     e.tau = float(tau) if tau is not None else 0.0
-    e.reserved = 0
+    e.scope = SCOPE_LAYER if scope == "layer" else SCOPE_HEAD
     e.window = int(window)
     w = min(int(window), n)
-    need = Hkv * (w + min(int(k), n - w)) if k is not None else Hkv * n
+    if k is None:
+        need = Hkv * n
+    elif scope == "layer":
+        need = Hkv * w + min(int(k), Hkv * (n - w))
+    else:
+        need = Hkv * (w + min(int(k), n - w))
     e.capacity = need if capacity is None else int(capacity)
     e.kv_head_stride, e.kv_tok_stride = K.stride(0), K.stride(1)
     e.score_head_stride = scores.stride(0)
@@ -351,9 +361,10 @@ def evict_workspace_bytes(desc: EvictDesc) -> int:
 
 
 def evict(scores, K, V, *, window: int, k=None, tau=None, capacity=None, workspace=None, outputs=None,
-          stream=None):
+          scope: str = "head", stream=None):
     """Keep the window plus top-k / tau-passing keys per KV head and compact K, V
-    (``kv_evict``). Returns (kept_idx int32 [capacity], head_offsets int64 [Hkv+1],
+    (``kv_evict``); ``scope="layer"`` makes k one budget for all heads together.
+    Returns (kept_idx int32 [capacity], head_offsets int64 [Hkv+1],
     K_out, V_out bf16 [capacity, D]); rows past head_offsets[-1] are unused."""
     torch = _torch()
     _bf16("K", K), _bf16("V", V)
@@ -361,7 +372,7 @@ def evict(scores, K, V, *, window: int, k=None, tau=None, capacity=None, workspa
         raise ValueError("K and V must have the same shape and strides")
     if scores.dtype != torch.float32 or scores.dim() != 2 or (scores.numel() and scores.stride(1) != 1):
         raise ValueError("scores must be float32 [Hkv, n] with contiguous rows")
-    e = evict_desc(scores, K, window=window, k=k, tau=tau, capacity=capacity)
+    e = evict_desc(scores, K, window=window, k=k, tau=tau, capacity=capacity, scope=scope)
     dev = K.device
     if outputs is None:
         kept = torch.empty(max(e.capacity, 1), dtype=torch.int32, device=dev)

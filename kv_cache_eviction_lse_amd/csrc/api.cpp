@@ -278,7 +278,7 @@ KVS_API int kvscore_futuremass(const kvs_attn_desc* d, const kvs_bf16* Q, const 
 namespace {
 int check_evict(const kvs_evict_desc* e) {
   if (!e) return fail(KVS_EINVAL, "descriptor is NULL");
-  if (e->reserved != 0) return fail(KVS_EINVAL, "reserved field must be 0");
+  if (e->scope != KVS_SCOPE_HEAD && e->scope != KVS_SCOPE_LAYER) return fail(KVS_EINVAL, "unknown scope %d", e->scope);
   if (e->n_kvheads < 1) return fail(KVS_EINVAL, "n_kvheads must be >= 1");
   if (e->n_kvheads > 65535) return fail(KVS_EUNSUPPORTED, "more than 65535 KV heads");
   if (e->head_dim != 64 && e->head_dim != 128)
@@ -292,6 +292,8 @@ int check_evict(const kvs_evict_desc* e) {
   if (e->n_tok > 0 && e->kv_tok_stride < e->head_dim) return fail(KVS_EINVAL, "kv_tok_stride is smaller than head_dim");
   if (e->n_kvheads > 1 && e->score_head_stride < e->n_tok)
     return fail(KVS_EINVAL, "score_head_stride is smaller than n_tok");
+  if (e->scope == KVS_SCOPE_LAYER && (int64_t)e->n_kvheads * e->n_tok > (int64_t)INT32_MAX)
+    return fail(KVS_EUNSUPPORTED, "a layer budget needs n_kvheads * n_tok < 2^31");
   return KVS_OK;
 }
 }  // namespace
@@ -308,8 +310,15 @@ KVS_API int kv_evict(const kvs_evict_desc* e, const float* scores, const kvs_bf1
   if (st) return st;
   const int64_t w = e->window < e->n_tok ? e->window : e->n_tok;
   const int64_t cand = e->n_tok - w;
-  const int64_t per_head = e->k >= 0 ? w + (e->k < cand ? e->k : cand) : e->n_tok;
-  const int64_t need = per_head * e->n_kvheads;
+  int64_t need;
+  if (e->k < 0) {
+    need = e->n_tok * e->n_kvheads;
+  } else if (e->scope == KVS_SCOPE_LAYER) {
+    const int64_t all = cand * e->n_kvheads;
+    need = w * e->n_kvheads + (e->k < all ? e->k : all);
+  } else {
+    need = (w + (e->k < cand ? e->k : cand)) * e->n_kvheads;
+  }
   if (e->capacity < need)
     return fail(KVS_ECAPACITY, "capacity %lld < %lld rows needed", (long long)e->capacity, (long long)need);
   if (!head_offsets) return fail(KVS_EINVAL, "head_offsets is NULL");

@@ -15,7 +15,10 @@
 //     launch is needed. After the last pass the k-th key T is exact; keys > T
 //     are kept, and among keys == T the lowest positions up to the quota.
 //   evict_count: per block, rows kept for sure and rows tied at T.
-//   evict_scan (one block per head): block offsets and the head's total.
+//   evict_scan (one block per head): block offsets and the head's total. With
+//     a layer budget the k-th key and the tie quota are the layer's (one
+//     histogram for all heads); the scan gives each head its share of the
+//     ties, lowest heads first.
 //   evict_write: predicate, tie ranks and prefix scan, kept indices; block
 //     (0, 0) writes the per-head offsets.
 //   evict_gather (a grid over output rows): coalesced copy of the kept K and
@@ -46,8 +49,9 @@ struct EvictParams {
   uint32_t* hist;   // [3][Hkv][NBINS]
   int32_t* blk;     // [Hkv][nb][4]: kept-for-sure, tied, offset in head, ties before
   int32_t* state;   // [Hkv][4]: threshold key T (bits), quota
-  int64_t n, n_cand, kprime;
+  int64_t n, n_cand, kprime;  // kprime: per head, or for the whole layer when layer != 0
   int Hkv, D, nb, mode;
+  int layer;  // top-k over all heads' candidates together (one histogram, one quota)
   float tau;
 };
 
@@ -135,9 +139,10 @@ __global__ __launch_bounds__(EV_THREADS) void evict_hist(EvictParams p) {
   __shared__ uint32_t s_hist[NBINS];
   const int h = blockIdx.y, b = blockIdx.x;
   for (int i = threadIdx.x; i < NBINS; i += EV_THREADS) s_hist[i] = 0u;
+  const int hh = p.layer ? 0 : h;  // histogram of this head, or the layer's
   uint32_t prefix = 0;
   int above, rank;
-  if (PASS > 0) radix_state(p, h, PASS, prefix, above, rank);
+  if (PASS > 0) radix_state(p, hh, PASS, prefix, above, rank);
   __syncthreads();
   const int hs = PASS > 0 ? digit_shift(PASS - 1) : 32;
   const int64_t i0 = (int64_t)b * EPB + threadIdx.x * EV_PER_THREAD;
@@ -152,7 +157,7 @@ __global__ __launch_bounds__(EV_THREADS) void evict_hist(EvictParams p) {
     }
   }
   __syncthreads();
-  uint32_t* g = p.hist + ((int64_t)PASS * p.Hkv + h) * NBINS;
+  uint32_t* g = p.hist + ((int64_t)PASS * p.Hkv + hh) * NBINS;
   for (int i = threadIdx.x; i < NBINS; i += EV_THREADS)
     if (s_hist[i]) atomicAdd(&g[i], s_hist[i]);
 }
@@ -178,9 +183,9 @@ __global__ __launch_bounds__(EV_THREADS) void evict_count(EvictParams p) {
   if (p.mode == MODE_TOPK) {
     uint32_t prefix;
     int above, rank;
-    radix_state(p, h, 3, prefix, above, rank);
+    radix_state(p, p.layer ? 0 : h, 3, prefix, above, rank);
     T = prefix;
-    quota = (int)p.kprime - above;
+    quota = (int)p.kprime - above;  // ties kept: per head, or for the layer (split by evict_scan)
   }
   if (b == 0 && threadIdx.x == 0) {
     p.state[h * 4 + 0] = (int32_t)T;
@@ -212,7 +217,20 @@ __global__ __launch_bounds__(EV_THREADS) void evict_count(EvictParams p) {
 // the head) and tie ranks, and store the head's total kept rows.
 __global__ __launch_bounds__(EV_THREADS) void evict_scan(EvictParams p) {
   const int h = blockIdx.x;
-  const int quota = p.mode == MODE_TOPK ? p.state[h * 4 + 1] : 0;
+  int quota = p.mode == MODE_TOPK ? p.state[h * 4 + 1] : 0;
+  if (p.mode == MODE_TOPK && p.layer) {
+    // The layer's tie quota goes to the lowest heads first: this head keeps
+    // what is left after the ties of heads 0 .. h-1, at most its own ties.
+    int before = 0, mine = 0;
+    for (int i = threadIdx.x; i < (h + 1) * p.nb; i += EV_THREADS) {
+      const int t = p.blk[(int64_t)i * 4 + 1];
+      if (i < h * p.nb) before += t; else mine += t;
+    }
+    int tot_before, tot_mine;
+    block_exclusive_scan(before, &tot_before);
+    block_exclusive_scan(mine, &tot_mine);
+    quota = min(max(quota - tot_before, 0), tot_mine);
+  }
   int sure_base = 0, tied_base = 0;
   for (int b0 = 0; b0 < p.nb; b0 += EV_THREADS) {
     const int b = b0 + (int)threadIdx.x;
@@ -229,7 +247,10 @@ __global__ __launch_bounds__(EV_THREADS) void evict_scan(EvictParams p) {
     sure_base += ts;
     tied_base += tt;
   }
-  if (threadIdx.x == 0) p.state[h * 4 + 2] = sure_base + min(tied_base, quota);
+  if (threadIdx.x == 0) {
+    p.state[h * 4 + 1] = quota;  // this head's share (evict_write reads it)
+    p.state[h * 4 + 2] = sure_base + min(tied_base, quota);
+  }
 }
 
 // first output row of head h: the totals of the heads before it
@@ -377,11 +398,13 @@ hipError_t launch_evict(const kvs_evict_desc& e, const float* scores, const uint
   p.n_cand = e.n_tok - w;
   p.nb = (int)((e.n_tok + EPB - 1) / EPB);
   p.tau = e.tau;
+  p.layer = e.scope == KVS_SCOPE_LAYER && e.k >= 0;
   if (e.k < 0) {
     p.mode = MODE_TAU;
   } else {
-    p.kprime = e.k < p.n_cand ? e.k : p.n_cand;
-    p.mode = p.kprime == 0 ? MODE_WINDOW : (p.kprime == p.n_cand ? MODE_ALL : MODE_TOPK);
+    const int64_t cand = p.layer ? p.n_cand * p.Hkv : p.n_cand;
+    p.kprime = e.k < cand ? e.k : cand;
+    p.mode = p.kprime == 0 ? MODE_WINDOW : (p.kprime == cand ? MODE_ALL : MODE_TOPK);
   }
   const WsLayout L = ws_layout(p.Hkv, p.nb);
   char* ws = static_cast<char*>(workspace);

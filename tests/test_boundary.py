@@ -239,7 +239,7 @@ def test_max_and_futuremass_reject(L):
 
 def _edesc(**kw):
     e = kvs.EvictDesc()
-    e.n_kvheads, e.head_dim, e.n_tok, e.k, e.tau, e.reserved = 2, 128, 1000, 100, 0.0, 0
+    e.n_kvheads, e.head_dim, e.n_tok, e.k, e.tau, e.scope = 2, 128, 1000, 100, 0.0, kvs.SCOPE_HEAD
     e.window, e.capacity = 32, 2 * 132
     e.kv_head_stride, e.kv_tok_stride, e.score_head_stride = 1000 * 128, 128, 1000
     for k, v in kw.items():
@@ -257,7 +257,11 @@ EVICT_BAD = [
     (dict(kv_tok_stride=132), kvs.KVS_EUNSUPPORTED),
     (dict(kv_tok_stride=120), kvs.KVS_EINVAL),
     (dict(score_head_stride=999), kvs.KVS_EINVAL),
-    (dict(reserved=3), kvs.KVS_EINVAL),
+    (dict(scope=3), kvs.KVS_EINVAL),
+    # layer budget: 2 windows of 32 + min(100, 2 * 968) = 164 rows
+    (dict(scope=kvs.SCOPE_LAYER, capacity=163), kvs.KVS_ECAPACITY),
+    (dict(scope=kvs.SCOPE_LAYER, n_kvheads=4096, n_tok=1 << 20, kv_head_stride=(1 << 20) * 128,
+          score_head_stride=1 << 20, capacity=1 << 40), kvs.KVS_EUNSUPPORTED),
 ]
 
 

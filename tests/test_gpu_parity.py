@@ -246,6 +246,42 @@ def test_evict_parity(name, Hkv, n, D, window, k, tau):
     assert np.array_equal(host_bits(Ko)[:total], Kr) and np.array_equal(host_bits(Vo)[:total], Vr)
 
 
+LAYER_CASES = [
+    # name, Hkv, n, D, window, k (one budget for the layer), identical heads
+    ("layer-multiblock", 4, 5000, 128, 128, 3000, False),
+    ("layer-identical-heads-ties", 5, 3000, 64, 16, 2501, True),
+    ("layer-k0", 3, 2000, 128, 32, 0, False),
+    ("layer-keep-all", 3, 2000, 128, 32, 10 ** 6, False),
+    ("layer-many-heads", 300, 700, 64, 16, 50000, False),
+    ("layer-long-heads", 2, 140000, 64, 128, 70001, False),
+]
+
+
+@pytest.mark.parametrize("name,Hkv,n,D,window,k,same", LAYER_CASES, ids=[c[0] for c in LAYER_CASES])
+def test_evict_layer_budget_parity(name, Hkv, n, D, window, k, same):
+    """One top-k budget over all heads' candidates (ties: lower head, then
+    lower position), exactly as the oracle ranks them."""
+    s, K, V = _evict_case(810, Hkv, n, D)
+    if same:
+        s[:] = s[0]
+    s[0, 3] = np.nan
+    s[-1, 5] = -0.0
+    s[-1, 6] = 0.0
+    s[0, 7] = np.inf
+    say(f"[evict-layer] {name}")
+    kept, offs, Ko, Vo = kvs.evict(dev_f32(s), dev_bf16(K), dev_bf16(V), window=window, k=k, scope="layer")
+    torch.cuda.synchronize()
+    offs = host(offs)
+    ref = oracle.select(s, window, k=k, scope="layer")
+    gk = kept_from_gpu(host(kept), offs)
+    for h in range(Hkv):
+        assert np.array_equal(gk[h], ref[h]), f"{name}: head {h} differs"
+    Kr, Vr, offr = oracle.compact(K, V, ref)
+    assert np.array_equal(offs, offr)
+    total = int(offs[-1])
+    assert np.array_equal(host_bits(Ko)[:total], Kr) and np.array_equal(host_bits(Vo)[:total], Vr)
+
+
 def test_evict_strided_inputs():
     """Scores with a padded head stride; K/V views with padded token rows."""
     Hkv, n, D = 2, 3000, 128
