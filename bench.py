@@ -15,8 +15,9 @@ pass's TFLOP/s against the bf16 MFMA peak (roofline), the LSE pass's
 TFLOP/s, eviction GB/s against HBM peak, the CPU oracle timed on a
 bounded sample of the same workload, and (under "adjacent", timed after the
 step and not part of it) the attention forward that also returns O, the
-value-norm kernel that produces the vnorm input, and decode attention of one
-new token per query head over the cache this step compacted.
+value-norm kernel that produces the vnorm input, decode attention of one
+new token per query head over the cache this step compacted, and eviction
+with one layer-wide top-k budget keeping as many rows as the step did.
 
     python bench.py [--gpus 1] [--steps 10] [--warmup 3] [--no-cpu-baseline]
 """
@@ -253,6 +254,17 @@ def main():
         t_dec = timed(lambda: kvs.decode(Qd, outs[2], outs[3], outs[1], scale=scale, workspace=dws, out=Od, lse_out=Ld),
                       reps=20)
         del Qd, dws, Od, Ld
+        # the same number of kept rows under one layer-wide top-k budget
+        kept_now = int(outs[1][-1].item())
+        w_eff = min(wl.window, r.n_ctx)
+        k_layer = max(kept_now - r.Hkv * w_eff, 0)
+        lay_outs = tuple(torch.empty_like(t) for t in outs)
+        el = kvs.evict_desc(S, K, window=wl.window, k=k_layer, scope="layer")
+        lws = torch.empty(max(kvs.evict_workspace_bytes(el), 256), dtype=torch.uint8, device="cuda")
+        t_lay = timed(lambda: kvs.evict(S, K, V, window=wl.window, k=k_layer, scope="layer", workspace=lws,
+                                        outputs=lay_outs), reps=20)
+        lay_total = int(lay_outs[1][-1].item())
+        del lay_outs, lws
     offs = outs[1].cpu().numpy()
     kept = np.diff(offs)
     kept_total = int(offs[-1])
@@ -308,6 +320,11 @@ def main():
         adjacent["decode"] = {"entry": "kvscore_decode", "ms": t_dec, "queries_per_head": 1, "rows": kept_total,
                               "bytes": dec_bytes, "gbs": dec_bytes / (t_dec * 1e-3) / 1e9,
                               "frac_of_hbm_peak": dec_bytes / (t_dec * 1e-3) / 1e9 / PEAK_HBM_GBS}
+        lay_bytes = acc.evict_bytes(r.Hkv, r.n_ctx, lay_total, r.D)
+        adjacent["evict_layer_budget"] = {"entry": "kv_evict (scope layer)", "ms": t_lay, "k": k_layer,
+                                          "kept_rows": lay_total, "bytes": lay_bytes,
+                                          "gbs": lay_bytes / (t_lay * 1e-3) / 1e9,
+                                          "frac_of_hbm_peak": lay_bytes / (t_lay * 1e-3) / 1e9 / PEAK_HBM_GBS}
         out["adjacent"] = adjacent
     print(json.dumps(out), flush=True)
 

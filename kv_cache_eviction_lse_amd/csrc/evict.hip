@@ -20,7 +20,9 @@
 //     histogram for all heads); the scan gives each head its share of the
 //     ties, lowest heads first.
 //   evict_write: predicate, tie ranks and prefix scan, kept indices; block
-//     (0, 0) writes the per-head offsets.
+//     (0, 0) writes the per-head offsets. Up to FUSED_HEADS heads and
+//     FUSED_ENTRIES count entries, evict_write_fused does the scan's work in
+//     every block instead (no evict_scan launch).
 //   evict_gather (a grid over output rows): coalesced copy of the kept K and
 //     V rows, 16-byte pieces, non-temporal loads and stores.
 #include "common.hpp"
@@ -260,21 +262,10 @@ __device__ __forceinline__ int64_t head_start(const EvictParams& p, int h) {
   return off;
 }
 
-// Predicate, tie ranks, positions, and the kept indices of one block of keys.
-// Block (0, 0) also writes the per-head offsets.
-__global__ __launch_bounds__(EV_THREADS) void evict_write(EvictParams p) {
-  const int h = blockIdx.y, b = blockIdx.x;
-  if (b == 0 && h == 0) {
-    for (int k = threadIdx.x; k <= p.Hkv; k += EV_THREADS) p.head_offsets[k] = head_start(p, k);
-  }
-  if (p.nb == 0) return;  // no keys: only the (zero) offsets
-  const uint32_t T = (uint32_t)p.state[h * 4 + 0];
-  const int quota = p.state[h * 4 + 1];
-  const int32_t* e = p.blk + ((int64_t)h * p.nb + b) * 4;
-  const int blk_off = e[2];
-  const int ties_before = e[3];
-  const int64_t out0 = head_start(p, h) + blk_off;
-
+// Predicate, tie ranks, positions and the kept indices of one block of keys,
+// given the block's first output row and the head's ties before the block.
+__device__ void write_block(const EvictParams& p, int h, int b, uint32_t T, int quota, int64_t out0,
+                            int ties_before) {
   const int64_t i0 = (int64_t)b * EPB + threadIdx.x * EV_PER_THREAD;
   const float* sc = p.scores + (int64_t)h * p.s_hs;
   int cls[EV_PER_THREAD];
@@ -302,6 +293,100 @@ __global__ __launch_bounds__(EV_THREADS) void evict_write(EvictParams p) {
   for (int k = 0; k < EV_PER_THREAD; ++k) {
     if (cls[k] == 2) p.kept_idx[out0 + pos++] = (int32_t)(i0 + k);
   }
+}
+
+// After evict_scan: block offsets and head totals are in the workspace.
+// Block (0, 0) also writes the per-head offsets.
+__global__ __launch_bounds__(EV_THREADS) void evict_write(EvictParams p) {
+  const int h = blockIdx.y, b = blockIdx.x;
+  if (b == 0 && h == 0) {
+    for (int k = threadIdx.x; k <= p.Hkv; k += EV_THREADS) p.head_offsets[k] = head_start(p, k);
+  }
+  if (p.nb == 0) return;  // no keys: only the (zero) offsets
+  const int32_t* e = p.blk + ((int64_t)h * p.nb + b) * 4;
+  write_block(p, h, b, (uint32_t)p.state[h * 4 + 0], p.state[h * 4 + 1], head_start(p, h) + e[2], e[3]);
+}
+
+// Scan and write in one launch, for layers with at most FUSED_HEADS heads and
+// FUSED_ENTRIES (head, block) count entries: every block reduces the count
+// entries itself (per-head totals in LDS, its own head's prefix before it),
+// derives each head's tie quota (its own, or its share of the layer's, lowest
+// heads first) and kept total, and from them its output rows.
+constexpr int FUSED_HEADS = 1024;
+constexpr int FUSED_ENTRIES = 8192;
+constexpr int HPT = FUSED_HEADS / EV_THREADS;  // heads per thread in the head scans
+
+__global__ __launch_bounds__(EV_THREADS) void evict_write_fused(EvictParams p) {
+  __shared__ int s_sure[FUSED_HEADS], s_tied[FUSED_HEADS];
+  __shared__ int64_t s_start;
+  __shared__ int s_quota;
+  const int h = blockIdx.y, b = blockIdx.x;
+  const int tid = threadIdx.x;
+  for (int k = tid; k < p.Hkv; k += EV_THREADS) s_sure[k] = s_tied[k] = 0;
+  __syncthreads();
+  int sb = 0, tb = 0;  // this head's counts in blocks before b
+  for (int i = tid; i < p.Hkv * p.nb; i += EV_THREADS) {
+    const int hh = i / p.nb, bb = i - hh * p.nb;
+    const int sure = p.blk[(int64_t)i * 4 + 0], tied = p.blk[(int64_t)i * 4 + 1];
+    atomicAdd(&s_sure[hh], sure);
+    atomicAdd(&s_tied[hh], tied);
+    if (hh == h && bb < b) {
+      sb += sure;
+      tb += tied;
+    }
+  }
+  int t_sb, t_tb;
+  block_exclusive_scan(sb, &t_sb);
+  block_exclusive_scan(tb, &t_tb);  // also orders the LDS atomics before the reads below
+  // thread t owns heads [t*HPT, t*HPT + HPT): their ties before them, then quotas and totals
+  int my_tied = 0;
+#pragma unroll
+  for (int j = 0; j < HPT; ++j) {
+    const int k = tid * HPT + j;
+    if (k < p.Hkv) my_tied += s_tied[k];
+  }
+  int tot_tied;
+  int tied_before = block_exclusive_scan(my_tied, &tot_tied);
+  const bool topk = p.mode == MODE_TOPK;
+  int quota_h = 0, my_total = 0;
+  int64_t totals[HPT];
+#pragma unroll
+  for (int j = 0; j < HPT; ++j) {
+    const int k = tid * HPT + j;
+    totals[j] = 0;
+    if (k < p.Hkv) {
+      int q = 0;
+      if (topk) {
+        q = p.state[k * 4 + 1];
+        if (p.layer) q = min(max(q - tied_before, 0), s_tied[k]);
+      }
+      tied_before += s_tied[k];
+      totals[j] = s_sure[k] + min(s_tied[k], q);
+      if (k == h) quota_h = q;
+      my_total += (int)totals[j];
+    }
+  }
+  int tot_rows;
+  const int my_first = block_exclusive_scan(my_total, &tot_rows);  // rows of the heads before this thread's
+  // head h's first row and quota (published by the thread that owns head h),
+  // and (block (0, 0)) every head's offset
+  int64_t start = my_first;
+#pragma unroll
+  for (int j = 0; j < HPT; ++j) {
+    const int k = tid * HPT + j;
+    if (k < p.Hkv) {
+      if (k == h) {
+        s_start = start;
+        s_quota = quota_h;
+      }
+      if (b == 0 && h == 0) p.head_offsets[k] = start;
+      start += totals[j];
+    }
+  }
+  if (b == 0 && h == 0 && tid == 0) p.head_offsets[p.Hkv] = tot_rows;
+  __syncthreads();
+  if (p.nb == 0) return;
+  write_block(p, h, b, (uint32_t)p.state[h * 4 + 0], s_quota, s_start + t_sb + min(t_tb, s_quota), t_tb);
 }
 
 // Coalesced copy of the kept K and V rows: GROWS output rows per block, D/8
@@ -421,13 +506,14 @@ hipError_t launch_evict(const kvs_evict_desc& e, const float* scores, const uint
     hipLaunchKernelGGL(evict_hist<2>, grid, dim3(EV_THREADS), 0, s, p);
   }
   if (p.nb > 0) hipLaunchKernelGGL(evict_count, grid, dim3(EV_THREADS), 0, s, p);
-  hipLaunchKernelGGL(evict_scan, dim3(p.Hkv), dim3(EV_THREADS), 0, s, p);
   if ((err = hipGetLastError()) != hipSuccess) return err;
-  if (p.nb > 0) {
-    hipLaunchKernelGGL(evict_write, grid, dim3(EV_THREADS), 0, s, p);
+  const bool fused = p.Hkv <= FUSED_HEADS && (int64_t)p.Hkv * p.nb <= FUSED_ENTRIES;
+  const dim3 wgrid = p.nb > 0 ? grid : dim3(1, 1);  // no keys: one block writes the (zero) offsets
+  if (fused) {
+    hipLaunchKernelGGL(evict_write_fused, wgrid, dim3(EV_THREADS), 0, s, p);
   } else {
-    // nothing to select: only the offsets (all zero)
-    hipLaunchKernelGGL(evict_write, dim3(1, 1), dim3(EV_THREADS), 0, s, p);
+    hipLaunchKernelGGL(evict_scan, dim3(p.Hkv), dim3(EV_THREADS), 0, s, p);
+    hipLaunchKernelGGL(evict_write, wgrid, dim3(EV_THREADS), 0, s, p);
   }
   const int64_t cap_rows = e.capacity;
   if (cap_rows > 0 && p.nb > 0) {
