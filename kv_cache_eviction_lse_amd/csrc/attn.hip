@@ -69,6 +69,8 @@ struct ATile {
   static constexpr int CPR = D / 8;            // pieces per row
   static constexpr int KPT = CHUNKS / (AT_THREADS / 2);  // K pieces per K-loading thread
   static constexpr int VUNITS = 16 * CPR;      // (key pair, piece) units of a V tile
+  static constexpr int VPT = (VUNITS + AT_THREADS / 2 - 1) / (AT_THREADS / 2);  // per V-loading thread
+  static constexpr int NPRE = KPT > 2 * VPT ? KPT : 2 * VPT;
 };
 
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
@@ -83,8 +85,7 @@ __device__ __forceinline__ bf16x8 pack_bf16(const f32x16& x, int base) {
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(AT_THREADS, 1) void attn_kernel(AttnParams p) {
   using T = ATile<D>;
-  static_assert(T::CHUNKS % (AT_THREADS / 2) == 0 && T::KPT <= 2 && T::VUNITS <= AT_THREADS / 2,
-                "K pieces must split evenly over half the workgroup, V pairs fit the other half");
+  static_assert(T::CHUNKS % (AT_THREADS / 2) == 0, "K pieces must split evenly over half the workgroup");
   __shared__ __attribute__((aligned(16))) char s_tile[2][T::STAGE];
 
   const int tid = threadIdx.x;
@@ -133,7 +134,7 @@ __global__ __launch_bounds__(AT_THREADS, 1) void attn_kernel(AttnParams p) {
   // 2m+1 per thread), which they store transposed as 32-bit key pairs.
   const bool k_loader = wave < AT_WAVES / 2;
   const int lt = tid & (AT_THREADS / 2 - 1);  // thread index within its half of the workgroup
-  u32x4 pre[2];
+  u32x4 pre[T::NPRE];
   auto load_tile = [&](int tt) {
     const bool ctx = tt < n_ctx_tiles;
     const int k0 = ctx ? tt * 32 : self_lo_s + (tt - n_ctx_tiles) * 32;
@@ -148,11 +149,17 @@ __global__ __launch_bounds__(AT_THREADS, 1) void attn_kernel(AttnParams p) {
         const int idx = lt + c * (AT_THREADS / 2);
         pre[c] = buf_ld16(rk, (idx / T::CPR) * ts * 2 + (idx % T::CPR) * 16);
       }
-    } else if (lt < T::VUNITS) {
+    } else {
       const __amdgpu_buffer_rsrc_t rv = tile_rsrc((ctx || CAUSAL ? p.V : p.Vself) + off, rows * ts * 2);
-      const int m = lt & 15, part = lt >> 4;
-      pre[0] = buf_ld16(rv, (2 * m) * ts * 2 + part * 16);
-      pre[1] = buf_ld16(rv, (2 * m + 1) * ts * 2 + part * 16);
+#pragma unroll
+      for (int u = 0; u < T::VPT; ++u) {
+        const int unit = lt + u * (AT_THREADS / 2);
+        if (unit < T::VUNITS) {
+          const int m = unit & 15, part = unit >> 4;
+          pre[2 * u] = buf_ld16(rv, (2 * m) * ts * 2 + part * 16);
+          pre[2 * u + 1] = buf_ld16(rv, (2 * m + 1) * ts * 2 + part * 16);
+        }
+      }
     }
   };
   // K rows as they are (padded). V transposed: elements (2m, d) and (2m+1, d)
@@ -166,14 +173,22 @@ __global__ __launch_bounds__(AT_THREADS, 1) void attn_kernel(AttnParams p) {
         const int idx = lt + c * (AT_THREADS / 2);
         *reinterpret_cast<u32x4*>(st + (idx / T::CPR) * T::K_STRIDE + (idx % T::CPR) * 16) = pre[c];
       }
-    } else if (lt < T::VUNITS) {
-      const int m = lt & 15, part = lt >> 4;
-      char* vt = st + T::K_BYTES + (8 * part) * T::VT_STRIDE + 4 * m;
+    } else {
 #pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        // low halves (element 2w) and high halves (element 2w+1) of keys 2m, 2m+1
-        *reinterpret_cast<uint32_t*>(vt + (2 * w) * T::VT_STRIDE) = __builtin_amdgcn_perm(pre[1][w], pre[0][w], 0x05040100u);
-        *reinterpret_cast<uint32_t*>(vt + (2 * w + 1) * T::VT_STRIDE) = __builtin_amdgcn_perm(pre[1][w], pre[0][w], 0x07060302u);
+      for (int u = 0; u < T::VPT; ++u) {
+        const int unit = lt + u * (AT_THREADS / 2);
+        if (unit < T::VUNITS) {
+          const int m = unit & 15, part = unit >> 4;
+          char* vt = st + T::K_BYTES + (8 * part) * T::VT_STRIDE + 4 * m;
+#pragma unroll
+          for (int w = 0; w < 4; ++w) {
+            // low halves (element 2w) and high halves (element 2w+1) of keys 2m, 2m+1
+            *reinterpret_cast<uint32_t*>(vt + (2 * w) * T::VT_STRIDE) =
+                __builtin_amdgcn_perm(pre[2 * u + 1][w], pre[2 * u][w], 0x05040100u);
+            *reinterpret_cast<uint32_t*>(vt + (2 * w + 1) * T::VT_STRIDE) =
+                __builtin_amdgcn_perm(pre[2 * u + 1][w], pre[2 * u][w], 0x07060302u);
+          }
+        }
       }
     }
   };
