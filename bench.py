@@ -62,7 +62,7 @@ def stored_traffic(kernel_src: str):
     return t.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(d, wl, n_heads_sample=1, n_chunks_sample=2):
+def cpu_baseline(d, wl, n_heads_sample=1, n_chunks_sample=6):
     """The oracle as it stands on a bounded sample: LSE + max score for one KV
     head's query heads over `n_chunks_sample` repeat chunks against the whole
     context, then selection + compaction of the full layer; scaled to the
