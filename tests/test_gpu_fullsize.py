@@ -8,7 +8,11 @@ The oracle cannot afford a whole 32k-120k layer, so at full size:
 * eviction: seeded full-size scores with ties, compared exactly;
 * the GPU's own pipeline: properties that hold at any size (scores bounded
   by vnorm / min hnorm, window kept, threshold respected, rows bit-exact, and
-  for the future mass with window 0, total mass = G * T).
+  for the future mass with window 0, total mass = G * T);
+* attention forward: sampled query rows against the oracle restricted to
+  those rows; decode: over the cache that eviction of seeded scores leaves
+  (identical to the oracle's), every query head against the oracle;
+* layer-wide budget: seeded full-size scores, compared exactly.
 """
 import numpy as np
 import pytest
@@ -24,8 +28,8 @@ if not torch.cuda.is_available():  # pragma: no cover
     pytest.skip("needs a GPU", allow_module_level=True)
 
 import kv_cache_eviction_lse_amd as kvs  # noqa: E402
-from gpu_util import (check_kept, check_lse, check_rows, check_scores, dev_bf16, dev_f32, host,  # noqa: E402
-                      host_bits, kept_from_gpu, say)
+from gpu_util import (bf16_abs, bf16_to_f64, check_attn_out, check_kept, check_lse, check_rows,  # noqa: E402
+                      check_scores, dev_bf16, dev_f32, host, host_bits, kept_from_gpu, say)
 
 SAMPLE_KEYS = 48
 
@@ -160,3 +164,72 @@ def test_kvpop_causal_16k():
         offs = _evict_properties(wl, d, t, K, V, k=k)
         assert np.all(np.diff(offs) == k + wl.window)
         _evict_on_seeded_scores(wl, d, K, V, k=k)
+
+
+def _attention_rows(wl, d, Q, K, V, Ks, Vs, rows, mask, chunk):
+    O, L = kvs.attention(Q, K, V, Ks, Vs, scale=d["scale"], mask=mask, chunk=chunk)
+    torch.cuda.synchronize()
+    args = (d["Q"], d["Kctx"], d.get("Kself"))
+    ref_O, ref_L = oracle.attention(*args, d["V"], d.get("Vself"), d["scale"], mask, chunk, rows=rows)
+    ref_abs, _ = oracle.attention(*args, bf16_abs(d["V"]), bf16_abs(d["Vself"]) if "Vself" in d else None,
+                                  d["scale"], mask, chunk, rows=rows)
+    check_lse(host(L)[:, rows], ref_L, f"{wl.name} attention lse rows")
+    check_attn_out(host_bits(O)[:, rows], ref_O, ref_abs, f"{wl.name} attention rows")
+
+
+def test_qwen3_8b_32k_attention_and_decode():
+    wl = QWEN3_8B_32K
+    r = wl.recipe
+    say(f"[full] {wl.name}: drawing (attention, decode)")
+    d = synth.draw(r, wl.seed)
+    Q, K, V = dev_bf16(d["Q"]), dev_bf16(d["Kctx"]), dev_bf16(d["V"])
+    Ks, Vs = dev_bf16(d["Kself"]), dev_bf16(d["Vself"])
+    say(f"[full] {wl.name}: attention on sampled rows")
+    _attention_rows(wl, d, Q, K, V, Ks, Vs, _sample_rows(r.n_q, r.chunk), "repeat", r.chunk)
+    # decode: one new token per query head over the cache eviction leaves
+    say(f"[full] {wl.name}: evict seeded scores, then decode")
+    sc = synth.evict_scores(wl.seed + 300, r.Hkv, r.n_ctx, tie_frac=0.05, zero_frac=0.01)
+    kept, offs, Ko, Vo = kvs.evict(dev_f32(sc), K, V, window=wl.window, tau=wl.tau)
+    Qd_bits = np.ascontiguousarray(d["Q"][:, -1:, :])
+    Od, Ld = kvs.decode(dev_bf16(Qd_bits), Ko, Vo, offs, scale=d["scale"])
+    torch.cuda.synchronize()
+    ref_kept = oracle.select(sc, wl.window, tau=wl.tau)
+    Kc, Vc, ref_offs = oracle.compact(d["Kctx"], d["V"], ref_kept)
+    assert np.array_equal(host(offs), ref_offs)
+    ref_O, ref_L = oracle.decode_attention(Qd_bits, Kc, Vc, ref_offs, d["scale"])
+    ref_abs, _ = oracle.decode_attention(Qd_bits, Kc, bf16_abs(Vc), ref_offs, d["scale"])
+    check_lse(host(Ld), ref_L, "32k decode lse")
+    g = bf16_to_f64(host_bits(Od))
+    tol = 2.0 ** -8 * np.abs(ref_O) + 2.0 ** -12 * ref_abs
+    assert np.all(np.abs(g - ref_O) <= tol), "32k decode O"
+
+
+def test_kvpop_causal_16k_attention():
+    wl = KVPOP_CAUSAL_16K
+    r = wl.recipe
+    say(f"[full] {wl.name}: drawing (attention)")
+    d = synth.draw(r, wl.seed)
+    rows = np.unique(np.r_[0:6, 5000:5006, r.n_q - 6:r.n_q])
+    _attention_rows(wl, d, dev_bf16(d["Q"]), dev_bf16(d["Kctx"]), dev_bf16(d["V"]), None, None, rows, "causal", 0)
+
+
+def test_qwen25_14b_120k_layer_budget():
+    """One top-k budget over the 8 heads of the 120k layer (25 % of all
+    candidates), on seeded scores with ties, compared exactly."""
+    wl = QWEN25_14B_120K
+    r = wl.recipe
+    say(f"[full] {wl.name}: layer budget on seeded scores")
+    sc = synth.evict_scores(wl.seed + 400, r.Hkv, r.n_ctx, tie_frac=0.05, zero_frac=0.01)
+    sc[3] = sc[1]  # two heads with identical scores: ties across heads at every level
+    K = synth.normal_bf16(wl.seed, 500, (r.Hkv, r.n_ctx, r.D))
+    V = synth.normal_bf16(wl.seed, 501, (r.Hkv, r.n_ctx, r.D))
+    k = wl.ks()[0] * r.Hkv
+    kept, offs, Ko, Vo = kvs.evict(dev_f32(sc), dev_bf16(K), dev_bf16(V), window=wl.window, k=k, scope="layer")
+    torch.cuda.synchronize()
+    ref = oracle.select(sc, wl.window, k=k, scope="layer")
+    gk = kept_from_gpu(host(kept), host(offs))
+    for h in range(r.Hkv):
+        assert np.array_equal(gk[h], ref[h]), f"layer budget: head {h} differs"
+    assert int(host(offs)[-1]) == k + r.Hkv * wl.window
+    check_rows(K, V, gk, host_bits(Ko), host_bits(Vo), host(offs), "120k layer budget")
+
