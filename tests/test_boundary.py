@@ -302,3 +302,28 @@ def test_binding_requires_library(monkeypatch, tmp_path):
     monkeypatch.setattr(kvs, "_lib", None)
     with pytest.raises(ImportError):
         kvs.lib()
+
+
+def test_last_error_is_per_thread(L):
+    """kvs_last_error keeps each calling thread's own message."""
+    import threading
+
+    results = {}
+
+    def worker(name, kw, expect):
+        d = _desc(**kw)
+        got = []
+        for _ in range(200):
+            code = L.kvscore_lse(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, None)
+            got.append((code, L.kvs_last_error().decode()))
+        results[name] = (got, expect)
+
+    threads = [threading.Thread(target=worker, args=("dim", dict(head_dim=96), "head_dim 96")),
+               threading.Thread(target=worker, args=("mask", dict(mask=7), "unknown mask 7"))]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    for name, (got, expect) in results.items():
+        assert all(expect in msg for _, msg in got), name
+

@@ -342,3 +342,53 @@ def test_pipeline_is_deterministic():
     torch.cuda.synchronize()
     for a, b in zip(*outs):
         assert torch.equal(a, b)
+
+
+def test_step_replays_from_a_hip_graph():
+    """LSE + max score + top-k eviction captured once in a HIP graph (no
+    allocation, no host sync inside) and replayed three times, with eager
+    work between the replays: every replay equals the eager step bit for bit."""
+    wl = QWEN25_1P5B_2K
+    r = wl.recipe
+    d = synth.draw(r, wl.seed)
+    Q, K, Ks, V = dev_bf16(d["Q"]), dev_bf16(d["Kctx"]), dev_bf16(d["Kself"]), dev_bf16(d["V"])
+    vn, hn = dev_f32(d["vnorm"]), dev_f32(d["hnorm"])
+    k = wl.ks()[1]
+    L = torch.empty((r.Hq, r.n_q), dtype=torch.float32, device="cuda")
+    S = torch.empty((r.Hkv, r.n_ctx), dtype=torch.float32, device="cuda")
+    e = kvs.evict_desc(S, K, window=wl.window, k=k)
+    ws = torch.empty(max(kvs.evict_workspace_bytes(e), 256), dtype=torch.uint8, device="cuda")
+    outs = (torch.empty(e.capacity, dtype=torch.int32, device="cuda"),
+            torch.empty(r.Hkv + 1, dtype=torch.int64, device="cuda"),
+            torch.empty((e.capacity, r.D), dtype=torch.bfloat16, device="cuda"),
+            torch.empty((e.capacity, r.D), dtype=torch.bfloat16, device="cuda"))
+
+    def step():
+        kvs.lse(Q, K, Ks, scale=d["scale"], mask="repeat", chunk=r.chunk, out=L)
+        kvs.max_scores(Q, K, L, scale=d["scale"], vnorm=vn, hnorm=hn, out=S)
+        kvs.evict(S, K, V, window=wl.window, k=k, workspace=ws, outputs=outs)
+
+    say("[graph] eager step")
+    step()
+    torch.cuda.synchronize()
+    ref = [t.clone() for t in (L, S, *outs)]
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    say("[graph] capture")
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    for rep in range(3):
+        for t in (L, S, *outs):
+            t.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for name, a, b in zip(("lse", "scores", "kept", "offsets", "K_out", "V_out"), (L, S, *outs), ref):
+            assert torch.equal(a.view(torch.uint8) if a.dtype != torch.bfloat16 else a.view(torch.int16),
+                               b.view(torch.uint8) if b.dtype != torch.bfloat16 else b.view(torch.int16)), \
+                f"replay {rep}: {name} differs"
