@@ -96,7 +96,10 @@ __global__ __launch_bounds__(AT_THREADS, 1) void attn_kernel(AttnParams p) {
 
   const int b = blockIdx.x;
   const int h = b % p.Hkv;
-  const int bx = b / p.Hkv;
+  // Causal work grows with position: dispatch the last positions (longest
+  // workgroups) first, so the short ones fill in at the end.
+  const int nbx = (p.n_sub + AT_WAVES - 1) / AT_WAVES;
+  const int bx = CAUSAL ? nbx - 1 - b / p.Hkv : b / p.Hkv;
   const int u_lo = bx * AT_WAVES;
   const int u_hi = min(u_lo + AT_WAVES, p.n_sub) - 1;
 

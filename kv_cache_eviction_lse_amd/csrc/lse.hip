@@ -80,7 +80,10 @@ __global__ __launch_bounds__(LSE_WAVES * WAVE, 3) void lse_kernel(LseParams p) {
 
   const int b = blockIdx.x;
   const int h = b % p.Hkv;
-  const int bx = b / p.Hkv;
+  // Causal work grows with position: dispatch the last positions (longest
+  // workgroups) first, so the short ones fill in at the end.
+  const int nbx = (p.n_sub + SUB_PER_BLOCK - 1) / SUB_PER_BLOCK;
+  const int bx = CAUSAL ? nbx - 1 - b / p.Hkv : b / p.Hkv;
   const int u_lo = bx * SUB_PER_BLOCK;
   const int u_hi = min(u_lo + SUB_PER_BLOCK, p.n_sub) - 1;
 
