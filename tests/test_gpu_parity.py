@@ -224,26 +224,65 @@ EVICT_CASES = [
 ]
 
 
-@pytest.mark.parametrize("name,Hkv,n,D,window,k,tau", EVICT_CASES, ids=[c[0] for c in EVICT_CASES])
-def test_evict_parity(name, Hkv, n, D, window, k, tau):
-    s, K, V = _evict_case(808, Hkv, n, D)
-    if n > 10:
+def _evict_special_scores(s):
+    if s.shape[1] > 10:
         s[0, 3] = np.nan
         s[-1, 5] = -0.0
         s[-1, 6] = 0.0
         s[0, 7] = np.inf
-    say(f"[evict] {name}")
-    kept, offs, Ko, Vo = kvs.evict(dev_f32(s), dev_bf16(K), dev_bf16(V), window=window, k=k, tau=tau)
-    torch.cuda.synchronize()
+
+
+def _check_evict_exact(name, s, K, V, window, k, tau, kept, offs, Ko, Vo):
     offs = host(offs)
     ref = oracle.select(s, window, k=k, tau=tau)
     gk = kept_from_gpu(host(kept), offs)
-    for h in range(Hkv):
+    for h in range(s.shape[0]):
         assert np.array_equal(gk[h], ref[h]), f"{name}: head {h} differs"
     Kr, Vr, offr = oracle.compact(K, V, ref)
-    assert np.array_equal(offs, offr)
+    assert np.array_equal(offs, offr), f"{name}: head offsets differ"
     total = int(offs[-1])
-    assert np.array_equal(host_bits(Ko)[:total], Kr) and np.array_equal(host_bits(Vo)[:total], Vr)
+    assert np.array_equal(host_bits(Ko)[:total], Kr) and np.array_equal(host_bits(Vo)[:total], Vr), \
+        f"{name}: compacted rows differ"
+
+
+@pytest.mark.parametrize("name,Hkv,n,D,window,k,tau", EVICT_CASES, ids=[c[0] for c in EVICT_CASES])
+def test_evict_parity(name, Hkv, n, D, window, k, tau):
+    s, K, V = _evict_case(808, Hkv, n, D)
+    _evict_special_scores(s)
+    say(f"[evict] {name}")
+    kept, offs, Ko, Vo = kvs.evict(dev_f32(s), dev_bf16(K), dev_bf16(V), window=window, k=k, tau=tau)
+    torch.cuda.synchronize()
+    _check_evict_exact(name, s, K, V, window, k, tau, kept, offs, Ko, Vo)
+
+
+def test_evict_reuses_one_workspace():
+    """One workspace (left uninitialised) through a sequence of calls of
+    every mode and of different shapes (more blocks, then fewer): each call
+    matches the oracle, whatever the calls before left in the workspace."""
+    seq = [
+        ("tau", 4, 9000, 128, 128, None, float(np.exp(-6.0))),
+        ("tau-again", 4, 9000, 128, 128, None, float(np.exp(-6.0))),
+        ("topk", 3, 5000, 128, 128, 1000, None),
+        ("tau-more-blocks", 8, 20000, 64, 64, None, float(np.exp(-5.0))),
+        ("window-only", 2, 3000, 128, 16, 0, None),
+        ("tau-fewer-blocks", 2, 700, 128, 16, None, float(np.exp(-6.0))),
+        ("keep-all", 3, 2000, 128, 16, 10 ** 6, None),
+        ("tau-last", 4, 9000, 128, 128, None, float(np.exp(-7.0))),
+    ]
+    cases = []
+    for i, (name, Hkv, n, D, window, k, tau) in enumerate(seq):
+        s, K, V = _evict_case(820 + i, Hkv, n, D)
+        _evict_special_scores(s)
+        sd, Kd, Vd = dev_f32(s), dev_bf16(K), dev_bf16(V)
+        cases.append((name, s, K, V, sd, Kd, Vd, window, k, tau))
+    nbytes = max(kvs.evict_workspace_bytes(kvs.evict_desc(c[4], c[5], window=c[7], k=c[8], tau=c[9]))
+                 for c in cases)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    for name, s, K, V, sd, Kd, Vd, window, k, tau in cases:
+        say(f"[evict-reuse] {name}")
+        kept, offs, Ko, Vo = kvs.evict(sd, Kd, Vd, window=window, k=k, tau=tau, workspace=ws)
+        torch.cuda.synchronize()
+        _check_evict_exact(name, s, K, V, window, k, tau, kept, offs, Ko, Vo)
 
 
 LAYER_CASES = [
@@ -344,19 +383,21 @@ def test_pipeline_is_deterministic():
         assert torch.equal(a, b)
 
 
-def test_step_replays_from_a_hip_graph():
-    """LSE + max score + top-k eviction captured once in a HIP graph (no
-    allocation, no host sync inside) and replayed three times, with eager
-    work between the replays: every replay equals the eager step bit for bit."""
+@pytest.mark.parametrize("selection", ["topk", "tau"])
+def test_step_replays_from_a_hip_graph(selection):
+    """LSE + max score + eviction (top-k, or threshold) captured once in a
+    HIP graph (no allocation, no host sync inside) and replayed three times,
+    with eager work between the replays: every replay equals the eager step
+    bit for bit."""
     wl = QWEN25_1P5B_2K
     r = wl.recipe
     d = synth.draw(r, wl.seed)
     Q, K, Ks, V = dev_bf16(d["Q"]), dev_bf16(d["Kctx"]), dev_bf16(d["Kself"]), dev_bf16(d["V"])
     vn, hn = dev_f32(d["vnorm"]), dev_f32(d["hnorm"])
-    k = wl.ks()[1]
+    k, tau = (wl.ks()[1], None) if selection == "topk" else (None, float(np.exp(-6.0)))
     L = torch.empty((r.Hq, r.n_q), dtype=torch.float32, device="cuda")
     S = torch.empty((r.Hkv, r.n_ctx), dtype=torch.float32, device="cuda")
-    e = kvs.evict_desc(S, K, window=wl.window, k=k)
+    e = kvs.evict_desc(S, K, window=wl.window, k=k, tau=tau)
     ws = torch.empty(max(kvs.evict_workspace_bytes(e), 256), dtype=torch.uint8, device="cuda")
     outs = (torch.empty(e.capacity, dtype=torch.int32, device="cuda"),
             torch.empty(r.Hkv + 1, dtype=torch.int64, device="cuda"),
@@ -366,9 +407,9 @@ def test_step_replays_from_a_hip_graph():
     def step():
         kvs.lse(Q, K, Ks, scale=d["scale"], mask="repeat", chunk=r.chunk, out=L)
         kvs.max_scores(Q, K, L, scale=d["scale"], vnorm=vn, hnorm=hn, out=S)
-        kvs.evict(S, K, V, window=wl.window, k=k, workspace=ws, outputs=outs)
+        kvs.evict(S, K, V, window=wl.window, k=k, tau=tau, workspace=ws, outputs=outs)
 
-    say("[graph] eager step")
+    say(f"[graph] {selection}: eager step")
     step()
     torch.cuda.synchronize()
     ref = [t.clone() for t in (L, S, *outs)]
