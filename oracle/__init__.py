@@ -24,4 +24,5 @@ from .reference import (  # noqa: F401
     value_norms,
     select,
     compact,
+    stream_states,
 )

@@ -352,6 +352,45 @@ def select(scores, window, k=None, tau=None, scope="head"):
     return out
 
 
+def stream_states(scores, window, tau, steps):
+    """Threshold pruning applied as tokens arrive, simulated token by token.
+
+    [KVzap] thresholding rule: at sequence length T, token t is kept iff
+    score_t >= tau or t >= T - w. The page asks for a criterion that also
+    works while decoding (its phase-agnostic criterion), so the rule is
+    re-applied at every length T: when the token at position p arrives
+    (T = p + 1), the token at p - w leaves the window and stays only if its
+    score passes; a token once dropped never returns. With w = 0 the arriving
+    token is decided at once.
+
+    Storage this returns, per KV head (the layout the cache keeps): a ring of
+    w window slots, slot p mod w holding the window token at position p
+    (-1 while empty), and the kept tokens that left the window, ascending.
+    ``scores`` is [Hkv, T_total]; ``steps`` lists the tokens appended by each
+    call. Returns one (n_seen, slot_pos [Hkv, w], kept list) per call.
+    """
+    s = np.asarray(scores, dtype=np.float64)
+    Hkv = s.shape[0]
+    w = max(int(window), 0)
+    tau32 = float(np.float32(tau))
+    slot_pos = np.full((Hkv, w), -1, dtype=np.int64)
+    kept = [[] for _ in range(Hkv)]
+    n = 0
+    out = []
+    for m in steps:
+        for _ in range(int(m)):
+            p = n  # the arriving token; the sequence length becomes p + 1
+            for h in range(Hkv):
+                q = p - w  # the token that has just left the last w positions
+                if q >= 0 and s[h, q] >= tau32:
+                    kept[h].append(q)
+                if w > 0:
+                    slot_pos[h, p % w] = p
+            n += 1
+        out.append((n, slot_pos.copy(), [np.array(k, dtype=np.int64) for k in kept]))
+    return out
+
+
 def compact(K, V, kept):
     """Copy the kept rows of K and V per head into one dense cache.
 

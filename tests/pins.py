@@ -549,6 +549,68 @@ def pin_compact_rows_bitwise():
             r += 1
 
 
+# ---------------------------------------------------------------- streaming threshold
+
+def pin_stream_hand_example():
+    """Worked by hand from the keep rule (w = 2, tau = 3, one head), scores
+    5, 1, 7, 2, 9, 0 arriving in calls of 2, 1 and 3 tokens: position 0
+    (score 5) stays when it leaves at length 3, position 1 (score 1) goes at
+    length 4, position 2 (7) stays at length 5, position 3 (2) goes at 6."""
+    st = oracle.stream_states(np.array([[5, 1, 7, 2, 9, 0]], dtype=np.float32), 2, 3.0, [2, 1, 3])
+    (n1, sl1, k1), (n2, sl2, k2), (n3, sl3, k3) = st
+    assert (n1, sl1.tolist(), k1[0].tolist()) == (2, [[0, 1]], [])
+    assert (n2, sl2.tolist(), k2[0].tolist()) == (3, [[2, 1]], [0])
+    assert (n3, sl3.tolist(), k3[0].tolist()) == (6, [[4, 5]], [0, 2])
+
+
+def _stream_scores(seed, Hkv, T):
+    rng = np.random.default_rng(seed)
+    s = rng.normal(size=(Hkv, T)).astype(np.float32)
+    s[0, 2] = np.nan
+    s[-1, 4] = np.inf
+    s[0, 6] = 0.25  # equal to tau below
+    s[-1, 9] = 0.25
+    return s
+
+
+def pin_stream_equals_rule_at_every_length():
+    """After every call, the window slots plus the kept tokens are exactly
+    what the keep rule gives for the tokens seen so far (the batch selection
+    with the same window and threshold)."""
+    for w, steps in ((0, [1, 4, 1, 20]), (1, [1, 1, 7, 3]), (3, [2, 1, 1, 9, 1]), (7, [1, 30, 2])):
+        s = _stream_scores(100 + w, 3, sum(steps))
+        for n, slots, kept in oracle.stream_states(s, w, 0.25, steps):
+            ref = oracle.select(s[:, :n], w, tau=0.25)
+            for h in range(3):
+                live = np.sort(np.concatenate([slots[h][slots[h] >= 0], kept[h]]))
+                assert np.array_equal(live, ref[h]), (w, n, h)
+
+
+def pin_stream_slots_and_order():
+    """Slot s holds the window token p with p mod w = s, the window is the
+    last min(n, w) positions, and kept tokens are ascending and older."""
+    w, steps = 5, [3, 1, 1, 11, 2]
+    s = _stream_scores(7, 2, sum(steps))
+    for n, slots, kept in oracle.stream_states(s, w, 0.25, steps):
+        for h in range(2):
+            win = sorted(int(p) for p in slots[h] if p >= 0)
+            assert win == list(range(max(0, n - w), n))
+            for sl, p in enumerate(slots[h]):
+                assert p < 0 or p % w == sl
+            k = kept[h].tolist()
+            assert k == sorted(k) and all(p < n - w for p in k)
+
+
+def pin_stream_window_zero():
+    """w = 0: every token is decided on arrival; the kept tokens are those
+    whose score passes, in order."""
+    s = _stream_scores(9, 2, 12)
+    n, slots, kept = oracle.stream_states(s, 0, 0.25, [5, 7])[-1]
+    assert n == 12 and slots.shape == (2, 0)
+    for h in range(2):
+        assert kept[h].tolist() == [p for p in range(12) if s[h, p] >= np.float32(0.25)]
+
+
 # ---------------------------------------------------------------- sampling
 
 def pin_sampled_rows_and_keys_match_full():

@@ -49,11 +49,15 @@ MUTANTS = {
     "ties-higher-index-first": ("order = np.lexsort((cand, neg, is_nan))", "order = np.lexsort((-cand, neg, is_nan))"),
     "topk-ascending": ("neg = np.where(is_nan, 0.0, -s[cand])", "neg = np.where(is_nan, 0.0, s[cand])"),
     "compact-reversed": ("K_out[offsets[h]:offsets[h + 1]] = K[h, idx]", "K_out[offsets[h]:offsets[h + 1]] = K[h, idx[::-1]]"),
+    "stream-leaves-late": ("q = p - w  # the token that has just left", "q = p - w - 1  # the token that has just left"),
+    "stream-strict": ("if q >= 0 and s[h, q] >= tau32:", "if q >= 0 and s[h, q] > tau32:"),
+    "stream-slot-offset": ("slot_pos[h, p % w] = p", "slot_pos[h, (p + 1) % w] = p"),
     "compact-offsets-shifted": ("offsets = np.concatenate([[0], np.cumsum(counts)])",
                                 "offsets = np.concatenate([np.cumsum(counts), [0]])"),
 }
 
 EXPORTED = ["lse", "attention", "attention_weights", "max_scores", "future_mass", "decode_attention", "value_norms", "select", "compact",
+            "stream_states",
             "visible_logits", "kv_head_of", "outside_window"]
 
 
