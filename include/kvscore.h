@@ -236,7 +236,11 @@ int kv_evict(const kvs_evict_desc* e, const float* scores, const kvs_bf16* K,
  * Q        [n_qheads, n_q, head_dim] bf16, strides q_head_stride, q_tok_stride
  * K_cache, V_cache [capacity, head_dim] bf16, dense rows (kv_evict's K_out, V_out)
  * head_offsets [n_kvheads + 1] int64, device (kv_evict's); values are
- *        clamped to [0, capacity] and made non-decreasing before use
+ *        clamped to [0, capacity] and made non-decreasing before use.
+ *        With head_stride_rows = S > 0 it is instead [n_kvheads] live row
+ *        counts, head h's rows being [h*S, h*S + head_offsets[h]) (the
+ *        per-head regions kv_stream_append keeps, its head_len; counts
+ *        are clamped to [0, S]); then capacity must be >= n_kvheads * S.
  * O        [n_qheads, n_q, head_dim] bf16 with Q's strides, overwritten
  * lse      [n_qheads, n_q] fp32, dense, overwritten
  * workspace: device memory of at least kvscore_decode_workspace_bytes(d)
@@ -251,6 +255,7 @@ typedef struct kvs_decode_desc {
   int64_t capacity; /* rows of K_cache / V_cache */
   float scale;
   int32_t reserved; /* set to 0 */
+  int64_t head_stride_rows; /* 0: head_offsets is [n_kvheads + 1] offsets; S > 0: see above */
 } kvs_decode_desc;
 
 size_t kvscore_decode_workspace_bytes(const kvs_decode_desc* d);
@@ -259,6 +264,53 @@ int kvscore_decode(const kvs_decode_desc* d, const kvs_bf16* Q,
                    const kvs_bf16* K_cache, const kvs_bf16* V_cache,
                    const int64_t* head_offsets, kvs_bf16* O, float* lse,
                    void* workspace, size_t workspace_bytes, void* stream);
+
+/* Threshold pruning as tokens arrive, for decoding. The KVzap page's keep
+ * rule (keep token t iff score_t >= tau or t >= T - w, its thresholding
+ * rule with the sliding window) re-applied at every sequence length T, as
+ * its phase-agnostic criterion asks of a pruner that also runs while
+ * decoding: when the token at position p arrives, the token at p - w leaves
+ * the window and stays only if its score passes (NaN never does); a dropped
+ * token never returns.
+ * Cache of one layer, per KV head h a region of `capacity` rows of K_cache
+ * and V_cache ([n_kvheads, capacity, head_dim] bf16, dense):
+ *   rows [0, w)           the window ring: the window token at position p
+ *                         is in row p mod w;
+ *   rows [w, w + kept_h)  the tokens that left the window with a passing
+ *                         score, in ascending position.
+ * The live rows of head h are rows [0, head_len[h]) of its region, with
+ * head_len[h] = min(n_seen, w) + kept_h: kvscore_decode reads the cache
+ * directly with head_stride_rows = capacity and head_offsets = head_len.
+ *   pos_cache  [n_kvheads, capacity] int32: position of each live row
+ *   win_scores [n_kvheads, w] fp32: the score of each ring row's token
+ *   head_len   [n_kvheads] int64: read and rewritten by each call; all
+ *              zero for an empty cache (n_seen = 0). Values outside what
+ *              the state allows are clamped, so no write leaves a region.
+ * A call appends n_new tokens per head, positions n_seen .. n_seen+n_new-1:
+ *   new_scores [n_kvheads, n_new] fp32, head stride score_head_stride;
+ *   K_new, V_new [n_kvheads, n_new, head_dim] bf16, strides
+ *              new_head_stride, new_tok_stride (shared).
+ * capacity must be >= max(w, n_seen + n_new) (room for every token);
+ * n_seen + n_new <= 2^30. The caller tracks n_seen (the same for every
+ * head). One workgroup per head does the call: it is meant for the few
+ * tokens of a decoding step, while kv_evict serves a whole prefill. */
+typedef struct kvs_stream_desc {
+  int32_t n_kvheads;
+  int32_t head_dim;
+  int64_t n_seen;   /* tokens appended before this call */
+  int64_t n_new;    /* tokens appended by this call (0: nothing to do) */
+  int64_t window;   /* w >= 0 */
+  float tau;
+  int32_t reserved; /* set to 0 */
+  int64_t capacity; /* rows per head region */
+  int64_t new_head_stride, new_tok_stride;
+  int64_t score_head_stride;
+} kvs_stream_desc;
+
+int kv_stream_append(const kvs_stream_desc* d, const float* new_scores,
+                     const kvs_bf16* K_new, const kvs_bf16* V_new,
+                     kvs_bf16* K_cache, kvs_bf16* V_cache, int32_t* pos_cache,
+                     float* win_scores, int64_t* head_len, void* stream);
 
 /* ---- diagnostics ----------------------------------------------------- */
 const char* kvs_strerror(int status);   /* static text for a status code */

@@ -12,6 +12,7 @@ the C ABI in ``include/kvscore.h``:
 * :func:`max_scores`   -> ``kvscore_max``
 * :func:`future_mass`  -> ``kvscore_futuremass``
 * :func:`evict`        -> ``kv_evict`` (+ ``kv_evict_workspace_bytes``)
+* :class:`StreamCache` -> ``kv_stream_append`` (threshold pruning as tokens arrive)
 
 Tensors: bf16 ``[heads, tokens, head_dim]`` with a contiguous last dimension
 (any head/token strides that keep rows 16-byte aligned), fp32 normalisers and
@@ -33,7 +34,7 @@ MASK_REPEAT, MASK_CAUSAL = 0, 1
 
 EXPORTED_SYMBOLS = (
     "kvscore_lse", "kvscore_attention", "kvscore_vnorm", "kvscore_decode_workspace_bytes", "kvscore_decode",
-    "kvscore_max", "kvscore_futuremass", "kv_evict_workspace_bytes", "kv_evict",
+    "kvscore_max", "kvscore_futuremass", "kv_evict_workspace_bytes", "kv_evict", "kv_stream_append",
     "kvs_strerror", "kvs_last_error", "kvs_version",
 )
 
@@ -78,6 +79,18 @@ class DecodeDesc(ctypes.Structure):
         ("q_head_stride", ctypes.c_int64), ("q_tok_stride", ctypes.c_int64),
         ("capacity", ctypes.c_int64),
         ("scale", ctypes.c_float), ("reserved", ctypes.c_int32),
+        ("head_stride_rows", ctypes.c_int64),
+    ]
+
+
+class StreamDesc(ctypes.Structure):
+    _fields_ = [
+        ("n_kvheads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+        ("n_seen", ctypes.c_int64), ("n_new", ctypes.c_int64), ("window", ctypes.c_int64),
+        ("tau", ctypes.c_float), ("reserved", ctypes.c_int32),
+        ("capacity", ctypes.c_int64),
+        ("new_head_stride", ctypes.c_int64), ("new_tok_stride", ctypes.c_int64),
+        ("score_head_stride", ctypes.c_int64),
     ]
 
 
@@ -113,12 +126,14 @@ def lib() -> ctypes.CDLL:
     L.kv_evict_workspace_bytes.argtypes = [pE]
     L.kv_evict_workspace_bytes.restype = ctypes.c_size_t
     L.kv_evict.argtypes = [pE, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
+    L.kv_stream_append.argtypes = [ctypes.POINTER(StreamDesc), vp, vp, vp, vp, vp, vp, vp, vp, vp]
     L.kvs_strerror.argtypes = [i32]
     L.kvs_strerror.restype = ctypes.c_char_p
     L.kvs_last_error.argtypes = []
     L.kvs_last_error.restype = ctypes.c_char_p
     L.kvs_version.restype = c
-    for name in ("kvscore_lse", "kvscore_attention", "kvscore_vnorm", "kvscore_decode", "kvscore_max", "kvscore_futuremass", "kv_evict"):
+    for name in ("kvscore_lse", "kvscore_attention", "kvscore_vnorm", "kvscore_decode", "kvscore_max", "kvscore_futuremass", "kv_evict",
+                 "kv_stream_append"):
         getattr(L, name).restype = c
     _lib = L
     return L
@@ -249,13 +264,14 @@ def value_norms(V, W_O, *, out=None, stream=None):
     return out
 
 
-def decode_desc(Q, K_cache, n_kvheads, scale) -> DecodeDesc:
+def decode_desc(Q, K_cache, n_kvheads, scale, head_stride_rows: int = 0) -> DecodeDesc:
     Hq, n_q, D = Q.shape
     d = DecodeDesc()
     d.n_qheads, d.n_kvheads, d.head_dim, d.n_q = Hq, n_kvheads, D, n_q
     d.q_head_stride, d.q_tok_stride = Q.stride(0), Q.stride(1)
     d.capacity = K_cache.shape[0]
     d.scale, d.reserved = float(scale), 0
+    d.head_stride_rows = int(head_stride_rows)
     return d
 
 
@@ -263,10 +279,13 @@ def decode_workspace_bytes(d: DecodeDesc) -> int:
     return int(lib().kvscore_decode_workspace_bytes(ctypes.byref(d)))
 
 
-def decode(Q, K_cache, V_cache, head_offsets, *, scale: float, workspace=None, out=None, lse_out=None, stream=None):
+def decode(Q, K_cache, V_cache, head_offsets, *, scale: float, workspace=None, out=None, lse_out=None,
+           head_stride_rows: int = 0, stream=None):
     """Decode attention of Q [Hq, n_q, D] over the compacted per-head cache
     (``kvscore_decode``): K_cache/V_cache [capacity, D] bf16 rows and the
-    device int64 head_offsets [Hkv+1] that kv_evict wrote. Returns (O, lse)."""
+    device int64 head_offsets [Hkv+1] that kv_evict wrote; or, with
+    ``head_stride_rows`` = S > 0, per-head regions of S rows and live row
+    counts head_offsets [Hkv] (a StreamCache's layout). Returns (O, lse)."""
     torch = _torch()
     _bf16("Q", Q)
     for name, t in (("K_cache", K_cache), ("V_cache", V_cache)):
@@ -275,8 +294,9 @@ def decode(Q, K_cache, V_cache, head_offsets, *, scale: float, workspace=None, o
     if K_cache.shape != V_cache.shape or K_cache.shape[1] != Q.shape[2]:
         raise ValueError("K_cache and V_cache must be [capacity, D] with Q's D")
     if head_offsets.dtype != torch.int64 or head_offsets.dim() != 1 or not head_offsets.is_cuda:
-        raise ValueError("head_offsets must be a GPU int64 vector [Hkv + 1]")
-    d = decode_desc(Q, K_cache, head_offsets.numel() - 1, scale)
+        raise ValueError("head_offsets must be a GPU int64 vector ([Hkv + 1], or [Hkv] with head_stride_rows)")
+    n_kv = head_offsets.numel() - (0 if head_stride_rows else 1)
+    d = decode_desc(Q, K_cache, n_kv, scale, head_stride_rows)
     need = decode_workspace_bytes(d)
     if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=Q.device)
@@ -387,3 +407,57 @@ def evict(scores, K, V, *, window: int, k=None, tau=None, capacity=None, workspa
     check(lib().kv_evict(ctypes.byref(e), _ptr(scores), _ptr(K), _ptr(V), _ptr(kept), _ptr(offs), _ptr(Ko),
                          _ptr(Vo), _ptr(workspace), workspace.numel(), _stream(stream)))
     return kept, offs, Ko, Vo
+
+
+class StreamCache:
+    """One layer's cache under threshold pruning as tokens arrive
+    (``kv_stream_append``): per KV head a region of ``capacity`` rows, the
+    window ring in rows [0, window) (position p in row p mod window), then
+    the kept tokens that left the window, ascending. ``head_len`` [Hkv]
+    (device) holds each head's live rows, rows [0, head_len[h]) of its
+    region; ``decode`` attends to exactly those. The library allocates
+    nothing: the tensors are allocated here with torch."""
+
+    def __init__(self, n_kvheads: int, head_dim: int, capacity: int, *, window: int, tau: float, device="cuda"):
+        torch = _torch()
+        self.n_kvheads, self.head_dim, self.capacity = int(n_kvheads), int(head_dim), int(capacity)
+        self.window, self.tau, self.n_seen = int(window), float(tau), 0
+        self.K = torch.zeros((self.n_kvheads, self.capacity, self.head_dim), dtype=torch.bfloat16, device=device)
+        self.V = torch.zeros_like(self.K)
+        self.pos = torch.full((self.n_kvheads, self.capacity), -1, dtype=torch.int32, device=device)
+        self.win_scores = torch.zeros((self.n_kvheads, max(self.window, 1)), dtype=torch.float32, device=device)
+        self.head_len = torch.zeros(self.n_kvheads, dtype=torch.int64, device=device)
+
+    def desc(self, new_scores, K_new) -> StreamDesc:
+        d = StreamDesc()
+        d.n_kvheads, d.head_dim = self.n_kvheads, self.head_dim
+        d.n_seen, d.n_new, d.window = self.n_seen, K_new.shape[1], self.window
+        d.tau, d.reserved = self.tau, 0
+        d.capacity = self.capacity
+        d.new_head_stride, d.new_tok_stride = K_new.stride(0), K_new.stride(1)
+        d.score_head_stride = new_scores.stride(0)
+        return d
+
+    def append(self, new_scores, K_new, V_new, stream=None) -> None:
+        """Append n_new tokens per head: new_scores fp32 [Hkv, n_new] (contiguous
+        rows), K_new / V_new bf16 [Hkv, n_new, D] with equal strides."""
+        torch = _torch()
+        _bf16("K_new", K_new), _bf16("V_new", V_new)
+        if K_new.shape != V_new.shape or K_new.stride() != V_new.stride():
+            raise ValueError("K_new and V_new must have the same shape and strides")
+        if tuple(K_new.shape[::2]) != (self.n_kvheads, self.head_dim):
+            raise ValueError("K_new must be [n_kvheads, n_new, head_dim]")
+        if new_scores.dtype != torch.float32 or tuple(new_scores.shape) != tuple(K_new.shape[:2]) \
+                or (new_scores.numel() and new_scores.stride(1) != 1):
+            raise ValueError("new_scores must be float32 [n_kvheads, n_new] with contiguous rows")
+        d = self.desc(new_scores, K_new)
+        check(lib().kv_stream_append(ctypes.byref(d), _ptr(new_scores), _ptr(K_new), _ptr(V_new), _ptr(self.K),
+                                     _ptr(self.V), _ptr(self.pos), _ptr(self.win_scores), _ptr(self.head_len),
+                                     _stream(stream)))
+        self.n_seen += int(K_new.shape[1])
+
+    def decode(self, Q, *, scale: float, workspace=None, out=None, lse_out=None, stream=None):
+        """Decode attention of Q [Hq, n_q, D] over every head's live rows."""
+        flat = (self.n_kvheads * self.capacity, self.head_dim)
+        return decode(Q, self.K.view(flat), self.V.view(flat), self.head_len, scale=scale, workspace=workspace,
+                      out=out, lse_out=lse_out, head_stride_rows=self.capacity, stream=stream)

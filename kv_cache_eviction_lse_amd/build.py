@@ -12,7 +12,7 @@ from concurrent.futures import ThreadPoolExecutor
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libkvscore.so")
-SOURCES = ["api.cpp", "lse.hip", "score.hip", "evict.hip", "attn.hip", "vnorm.hip", "decode.hip"]
+SOURCES = ["api.cpp", "lse.hip", "score.hip", "evict.hip", "attn.hip", "vnorm.hip", "decode.hip", "stream.hip"]
 ARCH = "gfx950"
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

@@ -217,6 +217,9 @@ int check_decode(const kvs_decode_desc* d) {
   if (d->q_head_stride % 8 || d->q_tok_stride % 8)
     return fail(KVS_EUNSUPPORTED, "strides must be multiples of 8 elements (16 bytes)");
   if (d->n_q > 1 && d->q_tok_stride < d->head_dim) return fail(KVS_EINVAL, "q_tok_stride is smaller than head_dim");
+  if (d->head_stride_rows < 0) return fail(KVS_EINVAL, "head_stride_rows must be >= 0");
+  if (d->head_stride_rows > 0 && d->capacity / d->n_kvheads < d->head_stride_rows)
+    return fail(KVS_EINVAL, "capacity is smaller than n_kvheads * head_stride_rows");
   return KVS_OK;
 }
 }  // namespace
@@ -243,6 +246,49 @@ KVS_API int kvscore_decode(const kvs_decode_desc* d, const kvs_bf16* Q, const kv
   return hip_status(kvs::launch_decode(*d, Q, K_cache, V_cache, head_offsets, O, lse, workspace,
                                        static_cast<hipStream_t>(stream)),
                     "kvscore_decode");
+}
+
+namespace {
+int check_stream(const kvs_stream_desc* d) {
+  if (!d) return fail(KVS_EINVAL, "descriptor is NULL");
+  if (d->reserved != 0) return fail(KVS_EINVAL, "reserved field must be 0");
+  if (d->n_kvheads < 1 || d->n_kvheads > 65535) return fail(KVS_EINVAL, "n_kvheads must be in [1, 65535]");
+  if (d->head_dim != 64 && d->head_dim != 128)
+    return fail(KVS_EUNSUPPORTED, "head_dim %d is not supported (64 or 128)", d->head_dim);
+  if (d->n_seen < 0 || d->n_new < 0 || d->window < 0) return fail(KVS_EINVAL, "negative size");
+  if (d->n_seen + d->n_new > MAX_TOKENS) return fail(KVS_EUNSUPPORTED, "more than 2^30 tokens");
+  if (d->window > MAX_TOKENS) return fail(KVS_EUNSUPPORTED, "window above 2^30");
+  const int64_t need = d->window > d->n_seen + d->n_new ? d->window : d->n_seen + d->n_new;
+  if (d->capacity < need)
+    return fail(KVS_ECAPACITY, "capacity %lld < %lld rows (window or every token)", (long long)d->capacity,
+                (long long)need);
+  if (d->capacity > MAX_TOKENS) return fail(KVS_EUNSUPPORTED, "capacity above 2^30 rows per head");
+  if (d->new_head_stride < 0 || d->new_tok_stride < 0 || d->score_head_stride < 0)
+    return fail(KVS_EINVAL, "negative stride");
+  if (d->new_head_stride % 8 || d->new_tok_stride % 8)
+    return fail(KVS_EUNSUPPORTED, "K_new/V_new strides must be multiples of 8 elements (16 bytes)");
+  if (d->n_new > 1 && d->new_tok_stride < d->head_dim) return fail(KVS_EINVAL, "new_tok_stride is smaller than head_dim");
+  if (d->n_kvheads > 1 && d->n_new > 0 && d->score_head_stride < d->n_new)
+    return fail(KVS_EINVAL, "score_head_stride is smaller than n_new");
+  return KVS_OK;
+}
+}  // namespace
+
+KVS_API int kv_stream_append(const kvs_stream_desc* d, const float* new_scores, const kvs_bf16* K_new,
+                             const kvs_bf16* V_new, kvs_bf16* K_cache, kvs_bf16* V_cache, int32_t* pos_cache,
+                             float* win_scores, int64_t* head_len, void* stream) {
+  int st = check_stream(d);
+  if (st) return st;
+  if (!K_cache || !V_cache || !pos_cache || !head_len) return fail(KVS_EINVAL, "a cache pointer is NULL");
+  if (d->window > 0 && !win_scores) return fail(KVS_EINVAL, "win_scores is NULL");
+  if (d->n_new > 0 && (!new_scores || !K_new || !V_new)) return fail(KVS_EINVAL, "an input pointer is NULL");
+  if (!aligned16(K_new) || !aligned16(V_new) || !aligned16(K_cache) || !aligned16(V_cache))
+    return fail(KVS_EUNSUPPORTED, "K_new, V_new, K_cache and V_cache must be 16-byte aligned");
+  int cus;
+  if ((st = check_device(&cus))) return st;
+  return hip_status(kvs::launch_stream_append(*d, new_scores, K_new, V_new, K_cache, V_cache, pos_cache, win_scores,
+                                              head_len, static_cast<hipStream_t>(stream)),
+                    "kv_stream_append");
 }
 
 KVS_API int kvscore_max(const kvs_attn_desc* d, const kvs_bf16* Q, const kvs_bf16* K, const float* lse,

@@ -25,7 +25,9 @@
 //     (bf16) and LSE.
 //   Scores are kept in the exp2 domain (q is pre-scaled by scale * log2 e).
 //   Offsets are clamped to [0, capacity] and made monotone, so no offset
-//   can send a read outside the cache.
+//   can send a read outside the cache. With a head stride S (the per-head
+//   regions of the streaming cache) head h's rows are [h*S, h*S + len_h),
+//   len_h clamped to [0, S].
 #include <cmath>
 
 #include "common.hpp"
@@ -49,6 +51,7 @@ struct DecParams {
   float* part;  // [n_wchunks_max][G * n_q][2 + D]: m, l, o
   int64_t q_hs, q_ts;
   int64_t capacity;
+  int64_t S;  // head stride in rows (strided heads), 0 for offsets
   int Hkv, G, n_q, nqg, n_wc_max;
   float c2;  // scale * log2 e
 };
@@ -59,12 +62,23 @@ __device__ __forceinline__ int64_t clamp_off(const DecParams& p, int h, int64_t 
   return o < prev ? prev : o;
 }
 
+// Rows [lo, hi) of head k. Offsets: lo comes in as the previous head's hi.
+__device__ __forceinline__ int64_t head_end(const DecParams& p, int k, int64_t& lo) {
+  if (p.S > 0) {
+    int64_t len = p.offs[k];
+    len = len < 0 ? 0 : (len > p.S ? p.S : len);
+    lo = (int64_t)k * p.S;
+    return lo + len;
+  }
+  return clamp_off(p, k + 1, lo);
+}
+
 // Head and chunk of global wave chunk wc; false past the last chunk.
 __device__ bool find_chunk(const DecParams& p, int wc, int& h, int64_t& r0, int64_t& r1) {
-  int64_t lo = clamp_off(p, 0, 0);
+  int64_t lo = p.S > 0 ? 0 : clamp_off(p, 0, 0);
   int cum = 0;
   for (int k = 0; k < p.Hkv; ++k) {
-    const int64_t hi = clamp_off(p, k + 1, lo);
+    const int64_t hi = head_end(p, k, lo);
     const int nc = (int)((hi - lo + WROWS - 1) / WROWS);
     if (wc < cum + nc) {
       h = k;
@@ -287,10 +301,10 @@ __global__ __launch_bounds__(CB_THREADS) void decode_combine(DecParams p) {
   const int nq_head = p.G * p.n_q;
   const int d = threadIdx.x % D, cg = threadIdx.x / D;
   // this head's wave chunks: [wc0, wc0 + nwc)
-  int64_t lo = clamp_off(p, 0, 0);
+  int64_t lo = p.S > 0 ? 0 : clamp_off(p, 0, 0);
   int wc0 = 0, nwc = 0;
   for (int k = 0; k <= h; ++k) {
-    const int64_t hi = clamp_off(p, k + 1, lo);
+    const int64_t hi = head_end(p, k, lo);
     const int nc = (int)((hi - lo + WROWS - 1) / WROWS);
     if (k < h) wc0 += nc; else nwc = nc;
     lo = hi;
@@ -346,6 +360,7 @@ hipError_t launch_decode(const kvs_decode_desc& d, const uint16_t* Q, const uint
   p.part = static_cast<float*>(workspace);
   p.q_hs = d.q_head_stride; p.q_ts = d.q_tok_stride;
   p.capacity = d.capacity;
+  p.S = d.head_stride_rows;
   p.Hkv = d.n_kvheads; p.G = d.n_qheads / d.n_kvheads; p.n_q = d.n_q;
   const int qg = p.G * p.n_q <= 4 ? 4 : QG_MAX;
   p.nqg = (p.G * p.n_q + qg - 1) / qg;

@@ -30,6 +30,10 @@ size_t decode_workspace_bytes(const kvs_decode_desc& d);
 hipError_t launch_decode(const kvs_decode_desc& d, const uint16_t* Q, const uint16_t* K, const uint16_t* V,
                          const int64_t* offs, uint16_t* O, float* lse, void* workspace, hipStream_t s);
 
+hipError_t launch_stream_append(const kvs_stream_desc& d, const float* new_scores, const uint16_t* K_new,
+                                const uint16_t* V_new, uint16_t* K_cache, uint16_t* V_cache, int32_t* pos_cache,
+                                float* win_scores, int64_t* head_len, hipStream_t s);
+
 size_t evict_workspace_bytes(const kvs_evict_desc& e);
 
 hipError_t launch_evict(const kvs_evict_desc& e, const float* scores, const uint16_t* K, const uint16_t* V,

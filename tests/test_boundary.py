@@ -203,6 +203,8 @@ DECODE_BAD = [
     (dict(scale=float("inf")), kvs.KVS_EINVAL),
     (dict(q_head_stride=100), kvs.KVS_EUNSUPPORTED),
     (dict(n_q=2, q_tok_stride=64), kvs.KVS_EINVAL),
+    (dict(head_stride_rows=-1), kvs.KVS_EINVAL),
+    (dict(head_stride_rows=501), kvs.KVS_EINVAL),  # 2 heads x 501 rows > capacity 1000
 ]
 
 
@@ -225,6 +227,57 @@ def test_decode_workspace_and_pointers(L):
     assert D(ctypes.byref(d), FAKE, FAKE, FAKE, None, FAKE, FAKE, FAKE, need, None) == kvs.KVS_EINVAL
     assert D(ctypes.byref(d), ctypes.c_void_p(0x100008), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, need,
              None) == kvs.KVS_EUNSUPPORTED
+
+
+def test_decode_head_stride_workspace(L):
+    """Per-head regions of S rows with live counts: the workspace bound is the
+    offsets form's (every region's chunks fit in capacity / 128 + heads)."""
+    d = _ddesc(head_stride_rows=500)
+    assert L.kvscore_decode_workspace_bytes(ctypes.byref(d)) == (1000 // 128 + 2) * 4 * 130 * 4
+
+
+def _sdesc(**kw):
+    d = kvs.StreamDesc()
+    d.n_kvheads, d.head_dim, d.n_seen, d.n_new, d.window = 2, 128, 100, 3, 16
+    d.tau, d.reserved, d.capacity = 0.5, 0, 200
+    d.new_head_stride, d.new_tok_stride, d.score_head_stride = 3 * 128, 128, 3
+    for k, v in kw.items():
+        setattr(d, k, v)
+    return d
+
+
+STREAM_BAD = [
+    (dict(reserved=1), kvs.KVS_EINVAL),
+    (dict(n_kvheads=0), kvs.KVS_EINVAL),
+    (dict(head_dim=96), kvs.KVS_EUNSUPPORTED),
+    (dict(n_seen=-1), kvs.KVS_EINVAL),
+    (dict(n_new=-1), kvs.KVS_EINVAL),
+    (dict(window=-1), kvs.KVS_EINVAL),
+    (dict(capacity=102), kvs.KVS_ECAPACITY),            # 103 tokens could all be kept
+    (dict(n_seen=0, n_new=1, window=300, capacity=299), kvs.KVS_ECAPACITY),  # the window ring needs 300 rows
+    (dict(n_seen=1 << 30, capacity=(1 << 30) + 8), kvs.KVS_EUNSUPPORTED),
+    (dict(new_tok_stride=100), kvs.KVS_EUNSUPPORTED),
+    (dict(new_tok_stride=64), kvs.KVS_EINVAL),
+    (dict(score_head_stride=2), kvs.KVS_EINVAL),
+    (dict(new_head_stride=-8), kvs.KVS_EINVAL),
+]
+
+
+@pytest.mark.parametrize("kw,code", STREAM_BAD)
+def test_stream_rejects(L, kw, code):
+    d = _sdesc(**kw)
+    assert L.kv_stream_append(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None) == code
+
+
+def test_stream_pointers(L):
+    d = _sdesc()
+    A = L.kv_stream_append
+    assert A(ctypes.byref(d), None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None) == kvs.KVS_EINVAL
+    assert A(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, None) == kvs.KVS_EINVAL
+    assert A(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, None) == kvs.KVS_EINVAL
+    assert A(ctypes.byref(d), FAKE, FAKE, FAKE, ctypes.c_void_p(0x100008), FAKE, FAKE, FAKE, FAKE,
+             None) == kvs.KVS_EUNSUPPORTED
+    assert A(None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None) == kvs.KVS_EINVAL
 
 
 def test_max_and_futuremass_reject(L):
@@ -294,6 +347,8 @@ def test_valid_calls_without_gpu_return_enodev(L):
     e = _edesc()
     ws = L.kv_evict_workspace_bytes(ctypes.byref(e))
     assert L.kv_evict(ctypes.byref(e), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, ws, None) == kvs.KVS_ENODEV
+    assert L.kv_stream_append(ctypes.byref(_sdesc()), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                              None) == kvs.KVS_ENODEV
     assert "device" in L.kvs_last_error().decode()
 
 
