@@ -265,6 +265,45 @@ def main():
                                         outputs=lay_outs), reps=20)
         lay_total = int(lay_outs[1][-1].item())
         del lay_outs, lws
+        # threshold pruning as tokens arrive (threshold workloads): the layer's
+        # context goes into a stream cache in one call, then decoding steps of
+        # one token per head, then decode attention over the stream cache
+        if wl.tau >= 0:
+            n_steps = 32
+            cap = r.n_ctx + n_steps
+            sc = kvs.StreamCache(r.Hkv, r.D, cap, window=wl.window, tau=wl.tau)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            sc.append(S, K, V)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            t_bulk = e0.elapsed_time(e1)
+            live_bulk = int(sc.head_len.sum().item())
+            s_new, K_new, V_new = S[:, :n_steps].contiguous(), K[:, :n_steps], V[:, :n_steps]
+            steps_in = [(s_new[:, i:i + 1], K_new[:, i:i + 1], V_new[:, i:i + 1]) for i in range(n_steps)]
+            # queue GPU work first so the appends run back to back at GPU speed
+            # (the host enqueues them while the GPU is busy)
+            torch.cuda._sleep(20_000_000)
+            e0.record(stream)
+            for a in steps_in:
+                sc.append(*a)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            t_step = e0.elapsed_time(e1) / n_steps
+            Qd = Q[:, -1:, :].contiguous()
+            flat = sc.K.view(-1, r.D)
+            sd = kvs.decode_desc(Qd, flat, r.Hkv, scale, head_stride_rows=cap)
+            sws = torch.empty(max(kvs.decode_workspace_bytes(sd), 16), dtype=torch.uint8, device="cuda")
+            Od, Ld = torch.empty_like(Qd), torch.empty((r.Hq, 1), dtype=torch.float32, device="cuda")
+            t_sdec = timed(lambda: sc.decode(Qd, scale=scale, workspace=sws, out=Od, lse_out=Ld), reps=20)
+            live = int(sc.head_len.sum().item())
+            adjacent["stream"] = {"entry": "kv_stream_append, kvscore_decode over its head regions",
+                                  "bulk_tokens_per_head": r.n_ctx, "bulk_ms": t_bulk,
+                                  "live_rows_after_bulk": live_bulk, "equals_evict_kept_rows": live_bulk == kept_now,
+                                  "step_tokens_per_head": 1, "step_us": t_step * 1e3,
+                                  "decode_ms": t_sdec, "decode_rows": live,
+                                  "decode_gbs": live * 4 * r.D / (t_sdec * 1e-3) / 1e9}
+            del sc, s_new, steps_in, Qd, sws, Od, Ld
     offs = outs[1].cpu().numpy()
     kept = np.diff(offs)
     kept_total = int(offs[-1])

@@ -7,9 +7,9 @@ decode over the same live rows.
 
 Cases cover one token per call across the window edge, bulk calls longer
 than the window (tokens that enter and leave in one call), more leaving
-tokens than one pass of the kernel decides, w = 0 and w = 1, a stream that
-never fills its window, many heads, D = 64 and 128, and scores that are NaN,
-+inf or exactly tau.
+tokens than one pass of the kernel decides, bulk calls split over several
+workgroups per head, w = 0 and w = 1, a stream that never fills its window,
+many heads, D = 64 and 128, and scores that are NaN, +inf or exactly tau.
 """
 import numpy as np
 import pytest
@@ -68,6 +68,10 @@ CASES = [
     ("window-one", 4, 64, 1, [1, 2, 1, 7]),
     ("window-never-filled", 2, 128, 64, [5, 10, 1]),
     ("many-heads", 40, 64, 4, [3, 1, 20, 1]),
+    # bulk calls split over workgroups of 4096 leaving tokens (ring tokens
+    # leave in the first chunk)
+    ("bulk-multi-block-after-a-partial-ring", 2, 128, 16, [5, 10000, 1, 3]),
+    ("bulk-multi-block-full-ring-d64", 3, 64, 128, [300, 9000, 2]),
 ]
 
 
