@@ -9,7 +9,7 @@
 //
 // The work is HBM-bound (each kept K and V row is read once per call), so it
 // is split by rows, flash-decoding style:
-//   * decode_partial: a wave owns a chunk of WROWS consecutive rows of one
+//   * decode_partial: a wave owns a chunk of WR consecutive rows of one
 //     head and 4 or 8 of the head's query vectors (G heads x n_q tokens;
 //     4 when the head has at most 4). A row is read by D/8 lanes, 16 bytes
 //     each (coalesced); the lanes' fp32 partial dot products are
@@ -38,7 +38,10 @@ namespace {
 
 constexpr int DC_WAVES = 4;
 constexpr int DC_THREADS = DC_WAVES * WAVE;
-constexpr int WROWS = 128;  // rows per wave chunk
+// Rows per wave chunk: 128 for large caches; smaller caches take 64 or 32 so
+// that enough waves are in flight (each wave's batches of loads run one after
+// another), at the price of more partials to merge.
+constexpr int wrows_for(int64_t capacity) { return capacity >= 65536 ? 128 : (capacity >= 8192 ? 64 : 32); }
 constexpr int QG_MAX = 8;   // query vectors per wave (4 when a head has at most 4)
 
 struct DecParams {
@@ -52,6 +55,7 @@ struct DecParams {
   int64_t q_hs, q_ts;
   int64_t capacity;
   int64_t S;  // head stride in rows (strided heads), 0 for offsets
+  int wr;     // rows per wave chunk
   int Hkv, G, n_q, nqg, n_wc_max;
   float c2;  // scale * log2 e
 };
@@ -79,11 +83,11 @@ __device__ bool find_chunk(const DecParams& p, int wc, int& h, int64_t& r0, int6
   int cum = 0;
   for (int k = 0; k < p.Hkv; ++k) {
     const int64_t hi = head_end(p, k, lo);
-    const int nc = (int)((hi - lo + WROWS - 1) / WROWS);
+    const int nc = (int)((hi - lo + p.wr - 1) / p.wr);
     if (wc < cum + nc) {
       h = k;
-      r0 = lo + (int64_t)(wc - cum) * WROWS;
-      r1 = min(r0 + WROWS, hi);
+      r0 = lo + (int64_t)(wc - cum) * p.wr;
+      r1 = min(r0 + p.wr, hi);
       return true;
     }
     cum += nc;
@@ -120,13 +124,13 @@ __device__ __forceinline__ float reduce_scatter(float (&v)[NV], int li) {
   return s;
 }
 
-template <int D, int QG>
+template <int D, int QG, int WR>
 __global__ __launch_bounds__(DC_THREADS) void decode_partial(DecParams p) {
   constexpr int LPR = D / 8;            // lanes per row
   constexpr int GPW = WAVE / LPR;       // row groups per wave
   constexpr int UNROLL = 8;             // rows per group in flight per batch
   constexpr int LPQ = WAVE / QG;        // lanes per query in the softmax phase
-  __shared__ __attribute__((aligned(16))) float s_score[DC_WAVES][WROWS][QG];
+  __shared__ __attribute__((aligned(16))) float s_score[DC_WAVES][WR][QG];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -305,7 +309,7 @@ __global__ __launch_bounds__(CB_THREADS) void decode_combine(DecParams p) {
   int wc0 = 0, nwc = 0;
   for (int k = 0; k <= h; ++k) {
     const int64_t hi = head_end(p, k, lo);
-    const int nc = (int)((hi - lo + WROWS - 1) / WROWS);
+    const int nc = (int)((hi - lo + p.wr - 1) / p.wr);
     if (k < h) wc0 += nc; else nwc = nc;
     lo = hi;
   }
@@ -346,11 +350,21 @@ __global__ __launch_bounds__(CB_THREADS) void decode_combine(DecParams p) {
 
 }  // namespace
 
-int64_t decode_wave_chunks_max(const kvs_decode_desc& d) { return d.capacity / WROWS + d.n_kvheads; }
+int64_t decode_wave_chunks_max(const kvs_decode_desc& d) { return d.capacity / wrows_for(d.capacity) + d.n_kvheads; }
 
 size_t decode_workspace_bytes(const kvs_decode_desc& d) {
   const int64_t nq_head = (int64_t)(d.n_qheads / d.n_kvheads) * d.n_q;
   return (size_t)decode_wave_chunks_max(d) * (size_t)nq_head * (size_t)(2 + d.head_dim) * sizeof(float);
+}
+
+template <int D, int QG>
+void launch_partial(const DecParams& p, dim3 grid, hipStream_t s) {
+  if (p.wr == 128)
+    hipLaunchKernelGGL((decode_partial<D, QG, 128>), grid, dim3(DC_THREADS), 0, s, p);
+  else if (p.wr == 64)
+    hipLaunchKernelGGL((decode_partial<D, QG, 64>), grid, dim3(DC_THREADS), 0, s, p);
+  else
+    hipLaunchKernelGGL((decode_partial<D, QG, 32>), grid, dim3(DC_THREADS), 0, s, p);
 }
 
 hipError_t launch_decode(const kvs_decode_desc& d, const uint16_t* Q, const uint16_t* K, const uint16_t* V,
@@ -361,6 +375,7 @@ hipError_t launch_decode(const kvs_decode_desc& d, const uint16_t* Q, const uint
   p.q_hs = d.q_head_stride; p.q_ts = d.q_tok_stride;
   p.capacity = d.capacity;
   p.S = d.head_stride_rows;
+  p.wr = wrows_for(d.capacity);
   p.Hkv = d.n_kvheads; p.G = d.n_qheads / d.n_kvheads; p.n_q = d.n_q;
   const int qg = p.G * p.n_q <= 4 ? 4 : QG_MAX;
   p.nqg = (p.G * p.n_q + qg - 1) / qg;
@@ -369,16 +384,12 @@ hipError_t launch_decode(const kvs_decode_desc& d, const uint16_t* Q, const uint
   const dim3 grid1((unsigned)((p.n_wc_max + DC_WAVES - 1) / DC_WAVES), (unsigned)p.nqg);
   const dim3 grid2((unsigned)(d.n_qheads * d.n_q));
   if (d.head_dim == 128) {
-    if (qg == 4)
-      hipLaunchKernelGGL((decode_partial<128, 4>), grid1, dim3(DC_THREADS), 0, s, p);
-    else
-      hipLaunchKernelGGL((decode_partial<128, 8>), grid1, dim3(DC_THREADS), 0, s, p);
+    if (qg == 4) launch_partial<128, 4>(p, grid1, s);
+    else launch_partial<128, 8>(p, grid1, s);
     hipLaunchKernelGGL(decode_combine<128>, grid2, dim3(CB_THREADS), 0, s, p);
   } else {
-    if (qg == 4)
-      hipLaunchKernelGGL((decode_partial<64, 4>), grid1, dim3(DC_THREADS), 0, s, p);
-    else
-      hipLaunchKernelGGL((decode_partial<64, 8>), grid1, dim3(DC_THREADS), 0, s, p);
+    if (qg == 4) launch_partial<64, 4>(p, grid1, s);
+    else launch_partial<64, 8>(p, grid1, s);
     hipLaunchKernelGGL(decode_combine<64>, grid2, dim3(CB_THREADS), 0, s, p);
   }
   return hipGetLastError();
