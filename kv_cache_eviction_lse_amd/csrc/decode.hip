@@ -20,7 +20,7 @@
 //     each). The row groups of a wave are added with shuffles and the wave
 //     writes one partial (m, l, o) per query to the workspace.
 //   * decode_combine: one workgroup per decode query merges its head's
-//     partials (max, rescaled sums; 1024 threads = chunk groups x
+//     partials (max, rescaled sums; 1024 threads = chunk groups x lanes of 8
 //     dimensions, groups merged through LDS in a fixed order) and writes O
 //     (bf16) and LSE.
 //   Scores are kept in the exp2 domain (q is pre-scaled by scale * log2 e).
@@ -44,6 +44,9 @@ constexpr int DC_THREADS = DC_WAVES * WAVE;
 constexpr int wrows_for(int64_t capacity) { return capacity >= 65536 ? 128 : (capacity >= 8192 ? 64 : 32); }
 constexpr int QG_MAX = 8;   // query vectors per wave (4 when a head has at most 4)
 
+// Floats per partial record: m, l, two pad words, then o[D] at a 16-byte offset.
+constexpr int REC(int D) { return D + 4; }
+
 struct DecParams {
   const uint16_t* Q;
   const uint16_t* K;
@@ -51,7 +54,7 @@ struct DecParams {
   const int64_t* offs;
   uint16_t* O;
   float* lse;
-  float* part;  // [n_wchunks_max][G * n_q][2 + D]: m, l, o
+  float* part;  // [n_wchunks_max][G * n_q][REC(D)]: m, l, two pad words, o (16-byte aligned)
   int64_t q_hs, q_ts;
   int64_t capacity;
   int64_t S;  // head stride in rows (strided heads), 0 for offsets
@@ -278,32 +281,35 @@ __global__ __launch_bounds__(DC_THREADS) void decode_partial(DecParams p) {
     for (int t = 0; t < QG; ++t) {
       const int f = qg * QG + t;
       if (f < nq_head) {
-        float* rec = p.part + ((int64_t)wc * nq_head + f) * (2 + D);
+        float* rec = p.part + ((int64_t)wc * nq_head + f) * REC(D);
         if (li == 0) {
           rec[0] = mq[t];
           rec[1] = l[t];
         }
-#pragma unroll
-        for (int e = 0; e < 8; ++e) rec[2 + 8 * li + e] = o[t][e];
+        *reinterpret_cast<float4*>(rec + 4 + 8 * li) = make_float4(o[t][0], o[t][1], o[t][2], o[t][3]);
+        *reinterpret_cast<float4*>(rec + 8 + 8 * li) = make_float4(o[t][4], o[t][5], o[t][6], o[t][7]);
       }
     }
   }
 }
 
 // One workgroup of 1024 threads per decode query merges the head's partials:
-// NG = 1024 / D chunk groups (thread = group x dimension) each merge every
-// NG-th chunk, then the groups are merged through LDS, in a fixed order.
+// NG = 1024 / (D/8) groups of D/8 lanes, each lane owning 8 dimensions (two
+// 16-byte loads per record); group k merges chunks k, k + NG, ... online,
+// then the groups are merged through LDS, in a fixed order.
 constexpr int CB_THREADS = 1024;
 
 template <int D>
 __global__ __launch_bounds__(CB_THREADS) void decode_combine(DecParams p) {
-  constexpr int NG = CB_THREADS / D;
-  __shared__ float s_m[NG], s_l[NG], s_o[NG][D];
+  constexpr int LPG = D / 8;             // lanes per group
+  constexpr int NG = CB_THREADS / LPG;   // groups
+  __shared__ float s_m[NG], s_l[NG];
+  __shared__ __attribute__((aligned(16))) float s_o[NG][D];
   const int g = blockIdx.x / p.n_q, tok = blockIdx.x % p.n_q;
   const int h = g / p.G;
   const int f = (g % p.G) * p.n_q + tok;
   const int nq_head = p.G * p.n_q;
-  const int d = threadIdx.x % D, cg = threadIdx.x / D;
+  const int li = threadIdx.x % LPG, cg = threadIdx.x / LPG;
   // this head's wave chunks: [wc0, wc0 + nwc)
   int64_t lo = p.S > 0 ? 0 : clamp_off(p, 0, 0);
   int wc0 = 0, nwc = 0;
@@ -313,29 +319,37 @@ __global__ __launch_bounds__(CB_THREADS) void decode_combine(DecParams p) {
     if (k < h) wc0 += nc; else nwc = nc;
     lo = hi;
   }
-  float M = -INFINITY, L = 0.f, acc = 0.f;
+  float M = -INFINITY, L = 0.f, acc[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) acc[e] = 0.f;
 #pragma unroll 4
   for (int c = cg; c < nwc; c += NG) {
-    const float* rec = p.part + ((int64_t)(wc0 + c) * nq_head + f) * (2 + D);
-    const float mc = rec[0], lc = rec[1], oc = rec[2 + d];
+    const float* rec = p.part + ((int64_t)(wc0 + c) * nq_head + f) * REC(D);
+    const float mc = rec[0], lc = rec[1];
+    const float4 o0 = *reinterpret_cast<const float4*>(rec + 4 + 8 * li);
+    const float4 o1 = *reinterpret_cast<const float4*>(rec + 8 + 8 * li);
     const float Mn = fmaxf(M, mc);
-    const float a = fast_exp2(M - Mn), b = fast_exp2(mc - Mn);  // M = -inf on a group's first chunk: a = 0
-    L = L * a + lc * b;
-    acc = acc * a + oc * b;
+    const float a = fast_exp2(M - Mn), bw = fast_exp2(mc - Mn);  // M = -inf on a group's first chunk: a = 0
+    L = L * a + lc * bw;
+    const float oc[8] = {o0.x, o0.y, o0.z, o0.w, o1.x, o1.y, o1.z, o1.w};
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[e] = acc[e] * a + oc[e] * bw;
     M = Mn;
   }
-  if (d == 0) {
+  if (li == 0) {
     s_m[cg] = M;
     s_l[cg] = L;
   }
-  s_o[cg][d] = acc;
+  *reinterpret_cast<float4*>(&s_o[cg][8 * li]) = make_float4(acc[0], acc[1], acc[2], acc[3]);
+  *reinterpret_cast<float4*>(&s_o[cg][8 * li + 4]) = make_float4(acc[4], acc[5], acc[6], acc[7]);
   __syncthreads();
-  if (cg == 0) {
+  const int d = threadIdx.x;
+  if (d < D) {
     float Mt = -INFINITY;
-#pragma unroll
+#pragma unroll 8
     for (int k = 0; k < NG; ++k) Mt = fmaxf(Mt, s_m[k]);
     float Lt = 0.f, ot = 0.f;
-#pragma unroll
+#pragma unroll 8
     for (int k = 0; k < NG; ++k) {
       const float w = s_m[k] == -INFINITY ? 0.f : fast_exp2(s_m[k] - Mt);  // groups with no chunk count 0
       Lt += s_l[k] * w;
@@ -354,7 +368,7 @@ int64_t decode_wave_chunks_max(const kvs_decode_desc& d) { return d.capacity / w
 
 size_t decode_workspace_bytes(const kvs_decode_desc& d) {
   const int64_t nq_head = (int64_t)(d.n_qheads / d.n_kvheads) * d.n_q;
-  return (size_t)decode_wave_chunks_max(d) * (size_t)nq_head * (size_t)(2 + d.head_dim) * sizeof(float);
+  return (size_t)decode_wave_chunks_max(d) * (size_t)nq_head * (size_t)REC(d.head_dim) * sizeof(float);
 }
 
 template <int D, int QG>

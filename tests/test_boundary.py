@@ -219,10 +219,10 @@ def test_decode_workspace_and_pointers(L):
     d = _ddesc()
     need = L.kvscore_decode_workspace_bytes(ctypes.byref(d))
     # wave chunks of 32 rows under 8192 rows of cache, 64 under 65536, else 128:
-    # (capacity // rows + heads) chunks x 4 queries per KV head x (2 + 128) floats
-    assert need == (1000 // 32 + 2) * 4 * 130 * 4
+    # (capacity // rows + heads) chunks x 4 queries per KV head x (4 + 128) floats
+    assert need == (1000 // 32 + 2) * 4 * 132 * 4
     for cap, rows in ((8191, 32), (8192, 64), (65535, 64), (65536, 128), (244110, 128)):
-        assert L.kvscore_decode_workspace_bytes(ctypes.byref(_ddesc(capacity=cap))) == (cap // rows + 2) * 4 * 130 * 4
+        assert L.kvscore_decode_workspace_bytes(ctypes.byref(_ddesc(capacity=cap))) == (cap // rows + 2) * 4 * 132 * 4
     D = L.kvscore_decode
     assert D(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, need - 1, None) == kvs.KVS_EWORKSPACE
     assert D(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, need, None) == kvs.KVS_EWORKSPACE
@@ -236,7 +236,7 @@ def test_decode_head_stride_workspace(L):
     """Per-head regions of S rows with live counts: the workspace bound is the
     offsets form's (every region's chunks fit in capacity / 128 + heads)."""
     d = _ddesc(head_stride_rows=500)
-    assert L.kvscore_decode_workspace_bytes(ctypes.byref(d)) == (1000 // 32 + 2) * 4 * 130 * 4
+    assert L.kvscore_decode_workspace_bytes(ctypes.byref(d)) == (1000 // 32 + 2) * 4 * 132 * 4
 
 
 def _sdesc(**kw):
