@@ -202,6 +202,14 @@ __global__ __launch_bounds__(DC_THREADS) void decode_partial(DecParams p) {
       if (rr < nr && (li & ((1 << SH) - 1)) == 0) s_score[wave][rr][li >> SH] = s;
     }
   }
+  // the first batch of value rows does not depend on the scores: issue it now
+  const uint16_t* Vb = p.V + r0 * D + 8 * li;
+  u32x4 vpre[UNROLL];
+#pragma unroll
+  for (int u = 0; u < UNROLL; ++u) {
+    const int rr = u * GPW + grp;
+    vpre[u] = rr < nr ? __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(Vb + (int64_t)rr * D)) : u32x4{};
+  }
   __syncthreads();  // scores visible (each wave reads only its own region)
 
   // ---- softmax of the chunk, once per (row, query): lane handles query
@@ -237,13 +245,17 @@ __global__ __launch_bounds__(DC_THREADS) void decode_partial(DecParams p) {
   for (int t = 0; t < QG; ++t)
 #pragma unroll
     for (int e = 0; e < 8; ++e) o[t][e] = 0.f;
-  const uint16_t* Vb = p.V + r0 * D + 8 * li;
   for (int k0 = 0; k0 * GPW < nr; k0 += UNROLL) {
     u32x4 vv[UNROLL];
+    if (k0 == 0) {
 #pragma unroll
-    for (int u = 0; u < UNROLL; ++u) {
-      const int rr = (k0 + u) * GPW + grp;
-      vv[u] = rr < nr ? __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(Vb + (int64_t)rr * D)) : u32x4{};
+      for (int u = 0; u < UNROLL; ++u) vv[u] = vpre[u];
+    } else {
+#pragma unroll
+      for (int u = 0; u < UNROLL; ++u) {
+        const int rr = (k0 + u) * GPW + grp;
+        vv[u] = rr < nr ? __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(Vb + (int64_t)rr * D)) : u32x4{};
+      }
     }
 #pragma unroll
     for (int u = 0; u < UNROLL; ++u) {
