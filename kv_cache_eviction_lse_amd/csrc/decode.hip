@@ -38,15 +38,21 @@ namespace {
 
 constexpr int DC_WAVES = 4;
 constexpr int DC_THREADS = DC_WAVES * WAVE;
-// Rows per wave chunk: 64 from 65536 rows of cache, else 32. Each wave's
-// batches of loads run one after another, so the rows in flight are the
-// number of waves times a batch: short chunks keep enough waves in flight,
-// at the price of more partials to merge (measured: the 16752-row cache of
-// the 16k KVpop layer decodes in 23 us with 32-row chunks, 28 with 64, 35
-// with 128; the 244110-row cache of the 32k layer in 44.6 us with 64-row
-// chunks, 45.5 with 128, 51 with 32).
-constexpr int wrows_for(int64_t capacity) { return capacity >= 65536 ? 64 : 32; }
-constexpr int QG_MAX = 8;   // query vectors per wave (4 when a head has at most 4)
+// Rows per wave chunk. Each wave's batches of loads run one after another, so
+// the rows in flight are the number of waves times a batch: short chunks keep
+// enough waves in flight, at the price of more partials to merge, as long as
+// the waves fit on the chip at once. With 4 queries per wave: 64 rows from
+// 65536 rows of cache, else 32 (measured: the 16752-row cache of the 16k
+// KVpop layer decodes in 23 us with 32-row chunks, 28 with 64, 35 with 128;
+// the 244110-row cache of the 32k layer in 44.6 us with 64, 45.5 with 128,
+// 51 with 32). With 8 queries per wave (about 180 registers, 2 waves per
+// SIMD) 64-row chunks of a large cache no longer fit in one round: 128 rows
+// from 65536 rows of cache (the 241024-row cache of the 120k layer: 67 us,
+// against 73 with 64), 64 from 8192, else 32.
+constexpr int queries_per_wave(int G, int n_q) { return G * n_q <= 4 ? 4 : 8; }
+constexpr int wrows_for(int64_t capacity, int qg) {
+  return qg == 4 ? (capacity >= 65536 ? 64 : 32) : (capacity >= 65536 ? 128 : (capacity >= 8192 ? 64 : 32));
+}
 
 // Floats per partial record: m, l, two pad words, then o[D] at a 16-byte offset.
 constexpr int REC(int D) { return D + 4; }
@@ -380,7 +386,11 @@ __global__ __launch_bounds__(CB_THREADS) void decode_combine(DecParams p) {
 
 }  // namespace
 
-int64_t decode_wave_chunks_max(const kvs_decode_desc& d) { return d.capacity / wrows_for(d.capacity) + d.n_kvheads; }
+int wrows_of(const kvs_decode_desc& d) {
+  return wrows_for(d.capacity, queries_per_wave(d.n_qheads / d.n_kvheads, d.n_q));
+}
+
+int64_t decode_wave_chunks_max(const kvs_decode_desc& d) { return d.capacity / wrows_of(d) + d.n_kvheads; }
 
 size_t decode_workspace_bytes(const kvs_decode_desc& d) {
   const int64_t nq_head = (int64_t)(d.n_qheads / d.n_kvheads) * d.n_q;
@@ -389,7 +399,9 @@ size_t decode_workspace_bytes(const kvs_decode_desc& d) {
 
 template <int D, int QG>
 void launch_partial(const DecParams& p, dim3 grid, hipStream_t s) {
-  if (p.wr == 64)
+  if (p.wr == 128)
+    hipLaunchKernelGGL((decode_partial<D, QG, 128>), grid, dim3(DC_THREADS), 0, s, p);
+  else if (p.wr == 64)
     hipLaunchKernelGGL((decode_partial<D, QG, 64>), grid, dim3(DC_THREADS), 0, s, p);
   else
     hipLaunchKernelGGL((decode_partial<D, QG, 32>), grid, dim3(DC_THREADS), 0, s, p);
@@ -403,9 +415,9 @@ hipError_t launch_decode(const kvs_decode_desc& d, const uint16_t* Q, const uint
   p.q_hs = d.q_head_stride; p.q_ts = d.q_tok_stride;
   p.capacity = d.capacity;
   p.S = d.head_stride_rows;
-  p.wr = wrows_for(d.capacity);
+  p.wr = wrows_of(d);
   p.Hkv = d.n_kvheads; p.G = d.n_qheads / d.n_kvheads; p.n_q = d.n_q;
-  const int qg = p.G * p.n_q <= 4 ? 4 : QG_MAX;
+  const int qg = queries_per_wave(p.G, p.n_q);
   p.nqg = (p.G * p.n_q + qg - 1) / qg;
   p.n_wc_max = (int)decode_wave_chunks_max(d);
   p.c2 = d.scale * LOG2E;

@@ -218,11 +218,15 @@ def test_decode_rejects(L, kw, code):
 def test_decode_workspace_and_pointers(L):
     d = _ddesc()
     need = L.kvscore_decode_workspace_bytes(ctypes.byref(d))
-    # wave chunks of 32 rows under 65536 rows of cache, else 64:
-    # (capacity // rows + heads) chunks x 4 queries per KV head x (4 + 128) floats
+    # 4 queries per wave: chunks of 32 rows under 65536 rows of cache, else 64;
+    # 8 queries per wave: 32 under 8192, 64 under 65536, else 128:
+    # (capacity // rows + heads) chunks x queries per KV head x (4 + 128) floats
     assert need == (1000 // 32 + 2) * 4 * 132 * 4
     for cap, rows in ((8192, 32), (65535, 32), (65536, 64), (244110, 64)):
         assert L.kvscore_decode_workspace_bytes(ctypes.byref(_ddesc(capacity=cap))) == (cap // rows + 2) * 4 * 132 * 4
+    for cap, rows in ((8191, 32), (8192, 64), (65535, 64), (65536, 128)):  # G = 5: 8 queries per wave
+        d5 = _ddesc(capacity=cap, n_qheads=10)
+        assert L.kvscore_decode_workspace_bytes(ctypes.byref(d5)) == (cap // rows + 2) * 5 * 132 * 4
     D = L.kvscore_decode
     assert D(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, need - 1, None) == kvs.KVS_EWORKSPACE
     assert D(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, need, None) == kvs.KVS_EWORKSPACE

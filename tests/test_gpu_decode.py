@@ -1,7 +1,8 @@
 """Decode attention over the compacted per-head cache (kvscore_decode) against
 the CPU oracle through the C ABI: ragged and empty heads, D = 64 and 128,
-several query groups per head, wave chunks of 32 and 64 rows (chosen by
-the cache's size), clamped offsets, and the full pipeline
+several query groups per head, wave chunks of 32, 64 and 128 rows (chosen
+by the cache's size and the queries per wave), clamped offsets, and the
+full pipeline
 kv_evict -> kvscore_decode against oracle select -> compact -> decode.
 
 Tolerance: scores, exponentials and sums are fp32 (chunks of 128 rows, then a
@@ -52,9 +53,12 @@ CASES = [
     ("d128-g4-chunk-edges", 16, 4, 128, [1, 128, 129, 3000], 1),
     ("g5-three-tokens-two-query-groups", 10, 2, 128, [700, 45], 3),
     ("mha-one-row", 4, 4, 128, [1, 2, 3, 4], 1),
-    # the wave-chunk size follows the cache: 32 rows up to here, 64 in the last
+    # the wave-chunk size follows the cache and the queries per wave: 32 rows
+    # up to here, then 32, 64 (4 queries), 64 and 128 (8 queries)
     ("d128-32-row-chunks-many", 16, 4, 128, [9000, 33, 32, 7000], 1),
-    ("d64-64-row-chunks", 8, 2, 64, [40000, 30001], 2),
+    ("d128-4q-64-row-chunks", 8, 2, 128, [40000, 30001], 1),
+    ("g5-8q-64-row-chunks", 10, 2, 128, [6000, 4001], 1),
+    ("d64-8q-128-row-chunks", 8, 2, 64, [40000, 30001], 2),
 ]
 
 
