@@ -80,7 +80,7 @@ enum { KVS_SCOPE_HEAD = 0, KVS_SCOPE_LAYER = 1 };
  *          (REPEAT only: the keys of the repeated copy; row j is query j's)
  * Requirements: n_qheads % n_kvheads == 0; head_dim is 64 or 128; every
  * pointer and every stride keeps rows 16-byte aligned (strides multiple of 8);
- * token strides are at least head_dim and at most 2^23 (KVS_EUNSUPPORTED).
+ * token strides are at least head_dim and at most 2^22 (KVS_EUNSUPPORTED).
  * chunk > 0 for REPEAT (the last chunk may be shorter); ignored for CAUSAL. */
 typedef struct kvs_attn_desc {
   int32_t n_qheads;
@@ -159,7 +159,7 @@ int kvscore_futuremass(const kvs_attn_desc* d, const kvs_bf16* Q,
  * V      [n_kvheads, n_tok, head_dim] bf16, strides v_head_stride,
  *        v_tok_stride (elements, multiples of 8, v_tok_stride >= head_dim);
  * W_O    [d_model, n_kvheads * head_dim] bf16, row stride wo_row_stride
- *        (elements, multiple of 8, >= n_kvheads * head_dim, <= 2^23);
+ *        (elements, multiple of 8, >= n_kvheads * head_dim, <= 2^22);
  * vnorm  [n_kvheads, n_tok] fp32, dense, overwritten (0 when d_model == 0).
  * Products of bf16 values are exact; sums are fp32. */
 typedef struct kvs_vnorm_desc {

@@ -80,9 +80,9 @@ int hip_status(hipError_t e, const char* what) {
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 constexpr int64_t MAX_TOKENS = (int64_t)1 << 30;
-// Tiles are read through buffer resources with 32-bit offsets: 64 rows of
-// 2^23 elements span 2^30 bytes.
-constexpr int64_t MAX_TOK_STRIDE = (int64_t)1 << 23;
+// Tiles are read through buffer resources with 32-bit offsets: the score
+// pass's 128-row tiles of rows 2^22 elements apart span 2^30 bytes.
+constexpr int64_t MAX_TOK_STRIDE = (int64_t)1 << 22;
 
 // Checks shared by the three scoring calls. `need_self` for REPEAT LSE.
 int check_attn(const kvs_attn_desc* d, const kvs_bf16* Q, const kvs_bf16* K, const kvs_bf16* Kself,
@@ -110,7 +110,7 @@ int check_attn(const kvs_attn_desc* d, const kvs_bf16* Q, const kvs_bf16* K, con
     if (st[i] % 8) return fail(KVS_EUNSUPPORTED, "strides must be multiples of 8 elements (16 bytes)");
   }
   if (d->q_tok_stride > MAX_TOK_STRIDE || d->k_tok_stride > MAX_TOK_STRIDE || d->ks_tok_stride > MAX_TOK_STRIDE)
-    return fail(KVS_EUNSUPPORTED, "token strides above 2^23 elements");
+    return fail(KVS_EUNSUPPORTED, "token strides above 2^22 elements");
   if (d->n_q > 0 && d->q_tok_stride < d->head_dim)
     return fail(KVS_EINVAL, "q_tok_stride is smaller than head_dim");
   if (d->n_ctx > 0 && d->k_tok_stride < d->head_dim)
@@ -189,7 +189,7 @@ KVS_API int kvscore_vnorm(const kvs_vnorm_desc* d, const kvs_bf16* V, const kvs_
   }
   if (d->n_tok > 0 && d->v_tok_stride < d->head_dim) return fail(KVS_EINVAL, "v_tok_stride is smaller than head_dim");
   if (d->v_tok_stride > MAX_TOK_STRIDE || d->wo_row_stride > MAX_TOK_STRIDE)
-    return fail(KVS_EUNSUPPORTED, "row strides above 2^23 elements");
+    return fail(KVS_EUNSUPPORTED, "row strides above 2^22 elements");
   if (d->d_model > 0 && d->wo_row_stride < (int64_t)d->n_kvheads * d->head_dim)
     return fail(KVS_EINVAL, "wo_row_stride is smaller than n_kvheads * head_dim");
   if (d->n_tok > 0 && (!V || !vnorm)) return fail(KVS_EINVAL, "V or vnorm is NULL");

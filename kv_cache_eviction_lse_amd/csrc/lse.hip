@@ -126,7 +126,7 @@ __global__ __launch_bounds__(LSE_WAVES * WAVE, 3) void lse_kernel(LseParams p) {
   // read as zero; every such row is masked (ctx: key >= n_ctx; self/causal:
   // key > j), so its value never counts. A thread's byte offsets within a
   // tile are fixed, so a tile costs no per-thread address arithmetic. Token
-  // strides are at most 2^23 elements, so 32 rows span at most 2^29 bytes.
+  // strides are at most 2^22 elements, so 32 rows span at most 2^28 bytes.
   int voff_ctx[CPT], voff_self[CPT];
 #pragma unroll
   for (int c = 0; c < CPT; ++c) {

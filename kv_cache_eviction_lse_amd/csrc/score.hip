@@ -159,7 +159,7 @@ __global__ __launch_bounds__(NW * WAVE) void score_kernel(ScoreParams p) {
     // lse and hnorm of one row. A tile is read through buffer resources that
     // start at its first row and cover only the rows that exist, so rows past
     // the end read as zero and a thread's byte offsets are fixed (token
-    // strides are at most 2^23 elements: a tile spans at most 2^30 bytes).
+    // strides are at most 2^22 elements: a 128-row tile spans at most 2^30 bytes).
     // Loads are unconditional and the bias arithmetic waits until the store,
     // so issuing a prefetch never stalls the wave. Rows past the end get bias
     // -inf: they never win a max and add exp2(-inf) = 0 to a sum.
@@ -283,13 +283,16 @@ __global__ __launch_bounds__(NW * WAVE) void score_kernel(ScoreParams p) {
       jt = njt;
     }
 
-    // ---- combine the two half-waves and write one value per key
+    // ---- combine the two half-waves and write one value per key. The lane
+    // index is taken afresh here, so no per-lane key index computed before the
+    // loop has to stay in registers across it.
+    const int lane_e = (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
 #pragma unroll
     for (int st = 0; st < NT; ++st) {
       const float other = __shfl_xor(red[st], 32);
       const float v = SUM ? red[st] + other : fmaxf(red[st], other);
-      const int64_t key = wave_key0 + 32 * st + col;
-      if (half == 0 && key < p.n_keys) {
+      const int64_t key = wave_key0 + 32 * st + (lane_e & 31);
+      if (lane_e < 32 && key < p.n_keys) {
         const float vn = p.vnorm ? p.vnorm[(int64_t)h * p.n_keys + key] : 1.0f;
         float* dst = p.out + (int64_t)h * p.n_keys + key;
         if (SUM) {
@@ -318,9 +321,9 @@ __global__ void fill_zero(float* p, int64_t n) {
 }
 
 // max mode: 8 waves x 2 key subtiles = 512 keys per workgroup, 64-row query tiles
-constexpr int MAX_NW = 8, MAX_NT = 2, MAX_RT = 2;
+constexpr int MAX_NW = 8, MAX_NT = 2, MAX_RT = 4;
 // sum mode: 8 waves x 2 key subtiles = 512 keys per workgroup, 64-row query tiles
-constexpr int SUM_NW = 8, SUM_NT = 2, SUM_RT = 2;
+constexpr int SUM_NW = 8, SUM_NT = 2, SUM_RT = 4;
 
 template <int D, int NW, int NT, int RT, bool SUM>
 hipError_t run(const ScoreParams& p, int nblocks, hipStream_t s) {

@@ -104,7 +104,7 @@ ATTN_BAD = [
     (dict(scale=float("nan")), kvs.KVS_EINVAL),
     (dict(q_tok_stride=100), kvs.KVS_EUNSUPPORTED),
     (dict(k_tok_stride=64), kvs.KVS_EINVAL),
-    (dict(k_tok_stride=(1 << 23) + 8), kvs.KVS_EUNSUPPORTED),  # tile offsets are 32-bit
+    (dict(k_tok_stride=(1 << 22) + 8), kvs.KVS_EUNSUPPORTED),  # tile offsets are 32-bit
     (dict(reserved=1), kvs.KVS_EINVAL),
     (dict(mask=kvs.MASK_CAUSAL), kvs.KVS_EINVAL),  # CAUSAL needs n_q == n_ctx
     (dict(n_ctx=1 << 31), kvs.KVS_EUNSUPPORTED),
@@ -164,7 +164,7 @@ VNORM_BAD = [
     (dict(v_tok_stride=64), kvs.KVS_EINVAL),
     (dict(v_tok_stride=132), kvs.KVS_EUNSUPPORTED),
     (dict(wo_row_stride=248), kvs.KVS_EINVAL),
-    (dict(wo_row_stride=(1 << 23) + 8), kvs.KVS_EUNSUPPORTED),
+    (dict(wo_row_stride=(1 << 22) + 8), kvs.KVS_EUNSUPPORTED),
     (dict(n_tok=(1 << 30) + 1), kvs.KVS_EUNSUPPORTED),
 ]
 
