@@ -8,7 +8,7 @@
 // exact; accumulation is fp32):
 //   * a workgroup owns NW * NT * 32 keys of one KV head; each wave keeps its
 //     NT * 32 value rows in VGPRs as B operands for the whole kernel;
-//   * W_h streams past in tiles of 64 output features through a
+//   * W_h streams past in tiles of 128 output features through a
 //     double-buffered LDS stage shared by the waves;
 //   * a lane holds one key column and 16 feature rows of each 32 x 32 block,
 //     so the sum of squares is in-register; the two half-waves are added once
@@ -33,7 +33,7 @@ struct VnParams {
   int Hkv;
 };
 
-constexpr int VN_NW = 8, VN_NT = 2, VN_RT = 2;
+constexpr int VN_NW = 8, VN_NT = 2, VN_RT = 4;
 
 template <int D>
 __global__ __launch_bounds__(VN_NW * WAVE) void vnorm_kernel(VnParams p) {

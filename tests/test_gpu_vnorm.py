@@ -42,6 +42,7 @@ CASES = [
     ("d64-ragged-features", 3, 33, 64, 100),
     ("one-key", 1, 1, 128, 64),
     ("features-below-one-tile", 2, 600, 128, 40),
+    ("ragged-last-feature-tile", 2, 700, 128, 200),  # tiles of 128 features: 128 + 72
 ]
 
 
