@@ -53,6 +53,7 @@ struct AttnParams {
 };
 
 constexpr int AT_WAVES = 8;
+constexpr int NSTAGE = 3;  // LDS ring: tile t's values, tile t+1's keys, tile t+2 being stored
 constexpr int AT_THREADS = AT_WAVES * WAVE;
 constexpr float AT_LAZY = 1048576.0f;  // 2^20: raise the offset when a lane's tile sum exceeds this
 
@@ -86,7 +87,7 @@ template <int D, bool CAUSAL>
 __global__ __launch_bounds__(AT_THREADS, 1) void attn_kernel(AttnParams p) {
   using T = ATile<D>;
   static_assert(T::CHUNKS % (AT_THREADS / 2) == 0, "K pieces must split evenly over half the workgroup");
-  __shared__ __attribute__((aligned(16))) char s_tile[2][T::STAGE];
+  __shared__ __attribute__((aligned(16))) char s_tile[NSTAGE][T::STAGE];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -219,16 +220,22 @@ __global__ __launch_bounds__(AT_THREADS, 1) void attn_kernel(AttnParams p) {
     return s;
   };
 
-  // One tile for this wave's subtile: S, P, lazy offset, O^T += V^T P^T.
-  auto tile = [&](int tt, int buf, bool masked, int k0, int kend, bool is_ctx) {
-    const char* st = s_tile[buf];
+  // S = K Q^T of one tile (keys from LDS stage buf), raw dot products.
+  auto qk = [&](int buf) {
+    const char* krow = s_tile[buf] + col * T::K_STRIDE + half * D;
     bf16x8 a[T::STEPS];
-    const char* krow = st + col * T::K_STRIDE + half * D;
 #pragma unroll
     for (int s = 0; s < T::STEPS; ++s) a[s] = as_bf16x8(*reinterpret_cast<const u32x4*>(krow + 16 * s));
     f32x16 x = mfma32(a[0], qreg[0], f32x16{});
 #pragma unroll
     for (int s = 1; s < T::STEPS; ++s) x = mfma32(a[s], qreg[s], x);
+    return x;
+  };
+
+  // Mask, exponentiate against the lazy offset, and O^T += V^T P^T for one
+  // tile whose S is x (values from LDS stage buf).
+  auto softmax_pv = [&](f32x16 x, int buf, bool masked, int k0, int kend, bool is_ctx) {
+    const char* st = s_tile[buf];
     if (masked) {
       const int kb = k0 + 4 * half;
 #pragma unroll
@@ -276,38 +283,59 @@ __global__ __launch_bounds__(AT_THREADS, 1) void attn_kernel(AttnParams p) {
       oacc[db] = mfma32(v0, pb0, oacc[db]);
       oacc[db] = mfma32(v1, pb1, oacc[db]);
     }
-    (void)tt;
   };
 
-  if (n_tiles > 0) {
-    load_tile(0);
-    store_tile(0);
+  // What this wave does with tile tt: skip it, or run it masked or not.
+  struct TileInfo {
+    int k0, kend;
+    bool is_ctx, run, masked;
+  };
+  auto tile_info = [&](int tt) {
+    TileInfo ti;
+    ti.is_ctx = tt < n_ctx_tiles;
+    ti.k0 = ti.is_ctx ? tt * 32 : self_lo_s + (tt - n_ctx_tiles) * 32;
+    ti.kend = ti.is_ctx ? n_ctx_s : pos_end_s;
+    if (tt < n_ctx_full_tiles) {
+      ti.run = true;
+      ti.masked = false;
+    } else if (ti.is_ctx) {
+      ti.run = true;
+      ti.masked = !(ti.k0 + 31 < ti.kend);
+    } else {
+      ti.run = !((ti.k0 > pj + 31) || (ti.k0 + 31 < sub_cs_first));
+      ti.masked = !((ti.k0 + 31 <= pj) && (ti.k0 >= sub_cs_last) && (ti.k0 + 31 < ti.kend));
+    }
+    ti.run = ti.run && sub_ok;
+    return ti;
+  };
+
+  // Software pipeline: while the softmax and PV of tile tt run on the VALU
+  // and the matrix core, S of tile tt+1 is already in flight, so a wave's
+  // matrix work overlaps its own exponentials even though the tile barrier
+  // keeps the waves in step. Tile tt lives in stage tt % NSTAGE from its
+  // store (two iterations ahead) until the barrier after its PV.
+  for (int t = 0; t < 2 && t < n_tiles; ++t) {
+    load_tile(t);
+    store_tile(t);
   }
   __syncthreads();
-
+  f32x16 x_cur = f32x16{};
+  {
+    const TileInfo ti = tile_info(0);
+    if (n_tiles > 0 && ti.run) x_cur = qk(0);
+  }
   for (int tt = 0; tt < n_tiles; ++tt) {
-    const int cur = tt & 1;
-    if (tt + 1 < n_tiles) load_tile(tt + 1);
-    if (sub_ok) {
-      const bool is_ctx = tt < n_ctx_tiles;
-      const int k0 = is_ctx ? tt * 32 : self_lo_s + (tt - n_ctx_tiles) * 32;
-      const int kend = is_ctx ? n_ctx_s : pos_end_s;
-      if (tt < n_ctx_full_tiles) {
-        tile(tt, cur, false, k0, kend, true);
-      } else {
-        bool run, full;
-        if (is_ctx) {
-          run = true;
-          full = k0 + 31 < kend;
-        } else {
-          run = !((k0 > pj + 31) || (k0 + 31 < sub_cs_first));
-          full = (k0 + 31 <= pj) && (k0 >= sub_cs_last) && (k0 + 31 < kend);
-        }
-        if (run) tile(tt, cur, !full, k0, kend, is_ctx);
-      }
+    if (tt + 2 < n_tiles) load_tile(tt + 2);
+    const TileInfo cur = tile_info(tt);
+    f32x16 x_next = f32x16{};
+    if (tt + 1 < n_tiles) {
+      const TileInfo nxt = tile_info(tt + 1);
+      if (nxt.run) x_next = qk((tt + 1) % NSTAGE);
     }
-    if (tt + 1 < n_tiles) store_tile(cur ^ 1);
+    if (cur.run) softmax_pv(x_cur, tt % NSTAGE, cur.masked, cur.k0, cur.kend, cur.is_ctx);
+    if (tt + 2 < n_tiles) store_tile((tt + 2) % NSTAGE);
     __syncthreads();
+    x_cur = x_next;
   }
 
   // ---- finish: merge the halves' partial sums, write LSE and O = O^T / l
