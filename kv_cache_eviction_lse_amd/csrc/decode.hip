@@ -19,15 +19,16 @@
 //     are read and o += p v in fp32 (the lanes of a row own 8 dimensions
 //     each). The row groups of a wave are added with shuffles and the wave
 //     writes one partial (m, l, o) per query to the workspace.
-//   * decode_combine: one workgroup per decode query merges its head's
-//     partials (max, rescaled sums; 1024 threads = chunk groups x lanes of 8
-//     dimensions, groups merged through LDS in a fixed order) and writes O
-//     (bf16) and LSE.
+//   * decode_combine: one workgroup per decode query and slice of 16 output
+//     dimensions merges its head's partials (one chunk per thread at a time,
+//     then a block reduction of the max and the rescaled sums, in a fixed
+//     order) and writes that slice of O (bf16), and the LSE.
 //   Scores are kept in the exp2 domain (q is pre-scaled by scale * log2 e).
 //   Offsets are clamped to [0, capacity] and made monotone, so no offset
 //   can send a read outside the cache. With a head stride S (the per-head
 //   regions of the streaming cache) head h's rows are [h*S, h*S + len_h),
-//   len_h clamped to [0, S].
+//   len_h clamped to [0, S]. Both kernels find their heads' rows with one
+//   offset load per lane, 64 heads at a time.
 #include <cmath>
 
 #include "common.hpp"
@@ -73,40 +74,90 @@ struct DecParams {
   float c2;  // scale * log2 e
 };
 
-__device__ __forceinline__ int64_t clamp_off(const DecParams& p, int h, int64_t prev) {
-  int64_t o = p.offs[h];
-  o = o < 0 ? 0 : (o > p.capacity ? p.capacity : o);
-  return o < prev ? prev : o;
-}
+// Row ranges and chunk numbering of the heads, 64 heads at a time across the
+// lanes of a wave (every lane loads one head's offset at once, instead of a
+// chain of dependent loads per head). Lane l describes head k0 + l: its rows
+// [lo, hi) and its chunks [c0, c0 + nc) in the global chunk numbering.
+// Offsets are clamped to [0, capacity] and made non-decreasing (a running
+// max), so no offset can send a read outside the cache; with a head stride S
+// head k's rows are [k*S, k*S + len_k), len_k clamped to [0, S]. `carry` is
+// the running max so far (start: head 0's clamped first offset) and `cum` the
+// chunks of the heads before k0; both are advanced past the 64 heads.
+struct HeadLane {
+  int64_t lo, hi;
+  int c0, nc;
+};
 
-// Rows [lo, hi) of head k. Offsets: lo comes in as the previous head's hi.
-__device__ __forceinline__ int64_t head_end(const DecParams& p, int k, int64_t& lo) {
+__device__ __forceinline__ int64_t clamp_to(int64_t v, int64_t hi) { return v < 0 ? 0 : (v > hi ? hi : v); }
+
+__device__ __forceinline__ HeadLane head_lanes(const DecParams& p, int k0, int64_t& carry, int& cum) {
+  const int lane = threadIdx.x & 63;
+  const int k = k0 + lane;
+  const bool valid = k < p.Hkv;
+  HeadLane r;
   if (p.S > 0) {
-    int64_t len = p.offs[k];
-    len = len < 0 ? 0 : (len > p.S ? p.S : len);
-    lo = (int64_t)k * p.S;
-    return lo + len;
+    r.lo = (int64_t)k * p.S;
+    r.hi = r.lo + (valid ? clamp_to(p.offs[k], p.S) : 0);
+  } else {
+    int64_t e = valid ? clamp_to(p.offs[k + 1], p.capacity) : 0;  // this head's end before the running max
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int64_t y = __shfl_up(e, o);
+      if (lane >= o) e = e > y ? e : y;
+    }
+    r.hi = e > carry ? e : carry;
+    const int64_t prev = __shfl_up(r.hi, 1);
+    r.lo = lane == 0 ? carry : prev;
   }
-  return clamp_off(p, k + 1, lo);
+  r.nc = valid ? (int)((r.hi - r.lo + p.wr - 1) / p.wr) : 0;
+  int incl = r.nc;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(incl, o);
+    if (lane >= o) incl += y;
+  }
+  r.c0 = cum + incl - r.nc;
+  cum += __shfl(incl, 63);
+  carry = __shfl(r.hi, 63);
+  return r;
 }
 
-// Head and chunk of global wave chunk wc; false past the last chunk.
+__device__ __forceinline__ int64_t first_offset(const DecParams& p) {
+  return p.S > 0 ? 0 : clamp_to(p.offs[0], p.capacity);
+}
+
+// Head and rows of global wave chunk wc (wave-uniform; all lanes call it);
+// false past the last chunk.
 __device__ bool find_chunk(const DecParams& p, int wc, int& h, int64_t& r0, int64_t& r1) {
-  int64_t lo = p.S > 0 ? 0 : clamp_off(p, 0, 0);
+  int64_t carry = first_offset(p);
   int cum = 0;
-  for (int k = 0; k < p.Hkv; ++k) {
-    const int64_t hi = head_end(p, k, lo);
-    const int nc = (int)((hi - lo + p.wr - 1) / p.wr);
-    if (wc < cum + nc) {
-      h = k;
-      r0 = lo + (int64_t)(wc - cum) * p.wr;
+  for (int k0 = 0; k0 < p.Hkv; k0 += WAVE) {
+    const HeadLane r = head_lanes(p, k0, carry, cum);
+    const uint64_t hit = __ballot(k0 + (int)(threadIdx.x & 63) < p.Hkv && wc >= r.c0 && wc < r.c0 + r.nc);
+    if (hit) {
+      const int src = __builtin_ctzll(hit);
+      h = k0 + src;
+      const int64_t lo = __shfl(r.lo, src), hi = __shfl(r.hi, src);
+      r0 = lo + (int64_t)(wc - __shfl(r.c0, src)) * p.wr;
       r1 = min(r0 + p.wr, hi);
       return true;
     }
-    cum += nc;
-    lo = hi;
   }
   return false;
+}
+
+// Chunks [wc0, wc0 + nwc) of head h (wave-uniform; all lanes call it).
+__device__ void head_chunks(const DecParams& p, int h, int& wc0, int& nwc) {
+  int64_t carry = first_offset(p);
+  int cum = 0;
+  for (int k0 = 0; k0 <= h; k0 += WAVE) {
+    const HeadLane r = head_lanes(p, k0, carry, cum);
+    if (h < k0 + WAVE) {
+      wc0 = __shfl(r.c0, h - k0);
+      nwc = __shfl(r.nc, h - k0);
+      return;
+    }
+  }
 }
 
 // Reduce-scatter of v[0..NV) over the LPR lanes of a row group (xor masks
@@ -315,72 +366,89 @@ __global__ __launch_bounds__(DC_THREADS) void decode_partial(DecParams p) {
   }
 }
 
-// One workgroup of 1024 threads per decode query merges the head's partials:
-// NG = 1024 / (D/8) groups of D/8 lanes, each lane owning 8 dimensions (two
-// 16-byte loads per record); group k merges chunks k, k + NG, ... online,
-// then the groups are merged through LDS, in a fixed order.
-constexpr int CB_THREADS = 1024;
+// Merge of a head's partials: one workgroup per (decode query, slice of
+// CB_DIMS output dimensions), so a layer's few decode queries still spread
+// over many CUs. Thread t takes chunks t, t + CB_THREADS, ... (every load of
+// a record issued at once: m, l and the slice of o), merges them online, and
+// the block then reduces (max, then rescaled sums of l and the slice) with
+// wave shuffles and one LDS step, in a fixed order. Every slice reads the
+// records' m and l itself and derives the same maxima and sums, so the
+// slices agree on the LSE, which the first writes.
+constexpr int CB_THREADS = 256;
+constexpr int CB_DIMS = 16;
 
 template <int D>
 __global__ __launch_bounds__(CB_THREADS) void decode_combine(DecParams p) {
-  constexpr int LPG = D / 8;             // lanes per group
-  constexpr int NG = CB_THREADS / LPG;   // groups
-  __shared__ float s_m[NG], s_l[NG];
-  __shared__ __attribute__((aligned(16))) float s_o[NG][D];
+  static_assert(D % CB_DIMS == 0, "whole slices");
+  constexpr int NWV = CB_THREADS / WAVE;
+  constexpr int NV = CB_DIMS + 1;  // l, then the slice of o
+  __shared__ float s_m[NWV];
+  __shared__ float s_v[NWV][NV];
   const int g = blockIdx.x / p.n_q, tok = blockIdx.x % p.n_q;
+  const int d0 = blockIdx.y * CB_DIMS;
   const int h = g / p.G;
   const int f = (g % p.G) * p.n_q + tok;
   const int nq_head = p.G * p.n_q;
-  const int li = threadIdx.x % LPG, cg = threadIdx.x / LPG;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   // this head's wave chunks: [wc0, wc0 + nwc)
-  int64_t lo = p.S > 0 ? 0 : clamp_off(p, 0, 0);
   int wc0 = 0, nwc = 0;
-  for (int k = 0; k <= h; ++k) {
-    const int64_t hi = head_end(p, k, lo);
-    const int nc = (int)((hi - lo + p.wr - 1) / p.wr);
-    if (k < h) wc0 += nc; else nwc = nc;
-    lo = hi;
-  }
-  float M = -INFINITY, L = 0.f, acc[8];
+  head_chunks(p, h, wc0, nwc);
+  float M = -INFINITY, v[NV];
 #pragma unroll
-  for (int e = 0; e < 8; ++e) acc[e] = 0.f;
-#pragma unroll 4
-  for (int c = cg; c < nwc; c += NG) {
+  for (int e = 0; e < NV; ++e) v[e] = 0.f;
+  for (int c = tid; c < nwc; c += CB_THREADS) {
     const float* rec = p.part + ((int64_t)(wc0 + c) * nq_head + f) * REC(D);
     const float mc = rec[0], lc = rec[1];
-    const float4 o0 = *reinterpret_cast<const float4*>(rec + 4 + 8 * li);
-    const float4 o1 = *reinterpret_cast<const float4*>(rec + 8 + 8 * li);
-    const float Mn = fmaxf(M, mc);
-    const float a = fast_exp2(M - Mn), bw = fast_exp2(mc - Mn);  // M = -inf on a group's first chunk: a = 0
-    L = L * a + lc * bw;
-    const float oc[8] = {o0.x, o0.y, o0.z, o0.w, o1.x, o1.y, o1.z, o1.w};
+    float oc[CB_DIMS];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) acc[e] = acc[e] * a + oc[e] * bw;
+    for (int e = 0; e < CB_DIMS; e += 4) {
+      const float4 x = *reinterpret_cast<const float4*>(rec + 4 + d0 + e);
+      oc[e] = x.x;
+      oc[e + 1] = x.y;
+      oc[e + 2] = x.z;
+      oc[e + 3] = x.w;
+    }
+    const float Mn = fmaxf(M, mc);
+    const float a = fast_exp2(M - Mn), bw = fast_exp2(mc - Mn);  // M = -inf on a thread's first chunk: a = 0
+    v[0] = v[0] * a + lc * bw;
+#pragma unroll
+    for (int e = 0; e < CB_DIMS; ++e) v[e + 1] = v[e + 1] * a + oc[e] * bw;
     M = Mn;
   }
-  if (li == 0) {
-    s_m[cg] = M;
-    s_l[cg] = L;
-  }
-  *reinterpret_cast<float4*>(&s_o[cg][8 * li]) = make_float4(acc[0], acc[1], acc[2], acc[3]);
-  *reinterpret_cast<float4*>(&s_o[cg][8 * li + 4]) = make_float4(acc[4], acc[5], acc[6], acc[7]);
+  // block max of the offsets
+  float Mt = M;
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) Mt = fmaxf(Mt, __shfl_xor(Mt, o));
+  if (lane == 0) s_m[wave] = Mt;
   __syncthreads();
-  const int d = threadIdx.x;
-  if (d < D) {
-    float Mt = -INFINITY;
-#pragma unroll 8
-    for (int k = 0; k < NG; ++k) Mt = fmaxf(Mt, s_m[k]);
-    float Lt = 0.f, ot = 0.f;
-#pragma unroll 8
-    for (int k = 0; k < NG; ++k) {
-      const float w = s_m[k] == -INFINITY ? 0.f : fast_exp2(s_m[k] - Mt);  // groups with no chunk count 0
-      Lt += s_l[k] * w;
-      ot += s_o[k][d] * w;
+  Mt = s_m[0];
+#pragma unroll
+  for (int w = 1; w < NWV; ++w) Mt = fmaxf(Mt, s_m[w]);
+  // rescale to Mt (threads with no chunk count 0), then sum over the block
+  const float wgt = M == -INFINITY ? 0.f : fast_exp2(M - Mt);
+#pragma unroll
+  for (int e = 0; e < NV; ++e) {
+    float x = v[e] * wgt;
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o);
+    v[e] = x;
+  }
+  if (lane == 0) {
+#pragma unroll
+    for (int e = 0; e < NV; ++e) s_v[wave][e] = v[e];
+  }
+  __syncthreads();
+  if (tid < CB_DIMS) {
+    float Lt = s_v[0][0], ot = s_v[0][tid + 1];
+#pragma unroll
+    for (int w = 1; w < NWV; ++w) {
+      Lt += s_v[w][0];
+      ot += s_v[w][tid + 1];
     }
     uint16_t* orow = p.O + (int64_t)g * p.q_hs + (int64_t)tok * p.q_ts;
     const float out = nwc > 0 ? ot / Lt : 0.f;
-    orow[d] = __builtin_bit_cast(uint16_t, (__bf16)out);
-    if (d == 0) p.lse[(int64_t)g * p.n_q + tok] = nwc > 0 ? (Mt + __log2f(Lt)) * LN2 : -INFINITY;
+    orow[d0 + tid] = __builtin_bit_cast(uint16_t, (__bf16)out);
+    if (d0 == 0 && tid == 0) p.lse[(int64_t)g * p.n_q + tok] = nwc > 0 ? (Mt + __log2f(Lt)) * LN2 : -INFINITY;
   }
 }
 
@@ -422,7 +490,7 @@ hipError_t launch_decode(const kvs_decode_desc& d, const uint16_t* Q, const uint
   p.n_wc_max = (int)decode_wave_chunks_max(d);
   p.c2 = d.scale * LOG2E;
   const dim3 grid1((unsigned)((p.n_wc_max + DC_WAVES - 1) / DC_WAVES), (unsigned)p.nqg);
-  const dim3 grid2((unsigned)(d.n_qheads * d.n_q));
+  const dim3 grid2((unsigned)(d.n_qheads * d.n_q), (unsigned)(d.head_dim / CB_DIMS));
   if (d.head_dim == 128) {
     if (qg == 4) launch_partial<128, 4>(p, grid1, s);
     else launch_partial<128, 8>(p, grid1, s);

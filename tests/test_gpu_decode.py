@@ -59,6 +59,10 @@ CASES = [
     ("d128-4q-64-row-chunks", 8, 2, 128, [40000, 30001], 1),
     ("g5-8q-64-row-chunks", 10, 2, 128, [6000, 4001], 1),
     ("d64-8q-128-row-chunks", 8, 2, 64, [40000, 30001], 2),
+    # heads are located 64 at a time (one per lane): 70 heads span two such
+    # groups, with empty heads on both sides of the group edge
+    ("d64-70-heads-two-lane-groups", 140, 70, 64,
+     [(37 * k) % 211 if k not in (0, 5, 63, 64, 69) else 0 for k in range(70)], 1),
 ]
 
 
@@ -79,6 +83,24 @@ def test_decode_clamps_offsets():
     O, L = kvs.decode(dev_bf16(Q), dev_bf16(Kc), dev_bf16(Vc), torch.from_numpy(bad).cuda(), scale=0.09)
     torch.cuda.synchronize()
     _check(host_bits(O), host(L), Q, Kc, Vc, offs, 0.09, "clamped")
+
+
+def test_decode_clamps_offsets_across_lane_groups():
+    """Negative, decreasing and too-large offsets over 70 heads (two groups of
+    64 heads): clamped to [0, capacity], then a running max, as one sequence."""
+    counts = [(53 * k) % 97 for k in range(70)]
+    Q, Kc, Vc, offs = _case(117, 70, 70, 128, counts, 1)
+    cap = int(offs[-1])
+    bad = offs.copy()
+    bad[3] = -50                 # negative: clamped to 0, then the running max
+    bad[40] = bad[38]            # decreasing into head 39's range
+    bad[64] = bad[60] - 7        # across the lane-group edge
+    bad[66] = cap + 10 ** 6      # past the cache: clamped to capacity, later heads empty
+    eff = np.maximum.accumulate(np.clip(bad, 0, cap))
+    say("[decode] clamped offsets across lane groups")
+    O, L = kvs.decode(dev_bf16(Q), dev_bf16(Kc), dev_bf16(Vc), torch.from_numpy(bad).cuda(), scale=0.09)
+    torch.cuda.synchronize()
+    _check(host_bits(O), host(L), Q, Kc, Vc, eff, 0.09, "clamped across lane groups")
 
 
 def test_evict_then_decode_pipeline():
