@@ -12,9 +12,10 @@
 //   * decode_partial: a wave owns a chunk of WR consecutive rows of one
 //     head and 4 or 8 of the head's query vectors (G heads x n_q tokens;
 //     4 when the head has at most 4). A row is read by D/8 lanes, 16 bytes
-//     each (coalesced); the lanes' fp32 partial dot products are
-//     reduce-scattered in shuffle steps so one lane ends with each query's
-//     score, which goes to LDS. The chunk max and p = exp2(s - m) are then
+//     each (coalesced); 32 rows at a time are staged in LDS and multiplied
+//     with the queries on the matrix cores (S = K Q^T, 32 keys x 32 query
+//     columns, of which the wave's queries are used); the scores go to
+//     LDS. The chunk max and p = exp2(s - m) are then
 //     computed once per (row, query) in LDS, with l = sum p; the value rows
 //     are read and o += p v in fp32 (the lanes of a row own 8 dimensions
 //     each). The row groups of a wave are added with shuffles and the wave
@@ -23,7 +24,7 @@
 //     dimensions merges its head's partials (one chunk per thread at a time,
 //     then a block reduction of the max and the rescaled sums, in a fixed
 //     order) and writes that slice of O (bf16), and the LSE.
-//   Scores are kept in the exp2 domain (q is pre-scaled by scale * log2 e).
+//   Scores are kept in the exp2 domain (scaled by scale * log2 e after the product).
 //   Offsets are clamped to [0, capacity] and made monotone, so no offset
 //   can send a read outside the cache. With a head stride S (the per-head
 //   regions of the streaming cache) head h's rows are [h*S, h*S + len_h),
@@ -160,41 +161,19 @@ __device__ void head_chunks(const DecParams& p, int h, int& wc0, int& nwc) {
   }
 }
 
-// Reduce-scatter of v[0..NV) over the LPR lanes of a row group (xor masks
-// LPR/2, LPR/4, ...): each step hands the partner the half of the values it
-// keeps and adds the half it receives, so after log2(NV) steps lane li holds
-// the partial sum of query (li >> (log2 LPR - log2 NV)); the remaining masks
-// complete the sum. Returned in v[0].
-template <int LPR, int NV>
-__device__ __forceinline__ float reduce_scatter(float (&v)[NV], int li) {
-  static_assert(LPR >= NV && (NV == 4 || NV == 8), "4 or 8 values, at least one lane per value");
-  int mask = LPR / 2;
-#pragma unroll
-  for (int n = NV; n > 1; n /= 2) {
-    const int hf = n / 2;
-    const bool upper = (li & mask) != 0;
-#pragma unroll
-    for (int j = 0; j < NV / 2; ++j) {
-      if (j < hf) {
-        const float send = upper ? v[j] : v[hf + j];
-        const float keep = upper ? v[hf + j] : v[j];
-        v[j] = keep + __shfl_xor(send, mask);
-      }
-    }
-    mask >>= 1;
-  }
-  float s = v[0];
-  for (; mask >= 1; mask >>= 1) s += __shfl_xor(s, mask);
-  return s;
-}
-
 template <int D, int QG, int WR>
 __global__ __launch_bounds__(DC_THREADS) void decode_partial(DecParams p) {
   constexpr int LPR = D / 8;            // lanes per row
   constexpr int GPW = WAVE / LPR;       // row groups per wave
-  constexpr int UNROLL = 8;             // rows per group in flight per batch
+  constexpr int UNROLL = 8;             // value rows per group in flight per batch
+  constexpr int BATCH = 32;             // key rows per batch: one MFMA row block
+  constexpr int KUNROLL = BATCH / GPW;  // key rows per group per batch
   constexpr int LPQ = WAVE / QG;        // lanes per query in the softmax phase
+  constexpr int STEPS = D / 16;         // k-steps of the score MFMA chain
+  constexpr int KSTRIDE = D * 2 + 16;   // padded rows of the key staging area, bytes
+  static_assert(KUNROLL * GPW == BATCH, "whole row groups per key batch");
   __shared__ __attribute__((aligned(16))) float s_score[DC_WAVES][WR][QG];
+  __shared__ __attribute__((aligned(16))) char s_k[DC_WAVES][BATCH * KSTRIDE];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -209,55 +188,57 @@ __global__ __launch_bounds__(DC_THREADS) void decode_partial(DecParams p) {
   const int nr = active ? (int)(r1 - r0) : 0;
   const int nq_head = p.G * p.n_q;
 
-  // this wave's queries (f = qg*8 + t < G*n_q), 8 dims per lane, pre-scaled; absent ones are 0
-  float q[QG][8];
+  // this wave's queries as MFMA B operands: lane l holds query f = qg*QG +
+  // (l % 32) (zero when absent, or when l % 32 >= QG), head dimensions in the
+  // permuted order [half*D/2 + 8s, +8) of step s (the key rows use the same)
+  const int col = lane & 31, half = lane >> 5;
+  bf16x8 qb[STEPS];
+  {
+    const int f = qg * QG + col;
+    const bool has = col < QG && f < nq_head;
+    const int g = h * p.G + (has ? f / p.n_q : 0), tok = has ? f % p.n_q : 0;
+    const uint16_t* qp = p.Q + (int64_t)g * p.q_hs + (int64_t)tok * p.q_ts + half * (D / 2);
 #pragma unroll
-  for (int t = 0; t < QG; ++t) {
-    const int f = qg * QG + t;
-    if (f < nq_head) {
-      const int g = h * p.G + f / p.n_q, tok = f % p.n_q;
-      const u32x4 w = ld16(p.Q + (int64_t)g * p.q_hs + (int64_t)tok * p.q_ts + 8 * li);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        q[t][2 * e] = __uint_as_float(w[e] << 16) * p.c2;
-        q[t][2 * e + 1] = __uint_as_float(w[e] & 0xffff0000u) * p.c2;
-      }
-    } else {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) q[t][e] = 0.f;
+    for (int s = 0; s < STEPS; ++s) {
+      u32x4 w = has ? ld16(qp + 8 * s) : u32x4{};
+      qb[s] = as_bf16x8(w);
     }
   }
 
-  // ---- scores: rows r0 + grp + GPW*k
+  // ---- scores, 32 rows per batch: coalesced row loads (D/8 lanes per row,
+  // 16 bytes each) are staged in this wave's LDS area, read back as the A
+  // operands of S = K_batch Q^T (keys as rows, queries as columns), and each
+  // lane's 16 scores (query col, rows acc_row(r, half)) go to s_score,
+  // scaled to the exp2 domain. The wave's own LDS accesses are in order, so
+  // staging needs no barrier.
+  char* const stage = s_k[wave];
   const uint16_t* Kb = p.K + r0 * D + 8 * li;
-  for (int k0 = 0; k0 * GPW < nr; k0 += UNROLL) {
-    u32x4 kv[UNROLL];
+  for (int b0 = 0; b0 < nr; b0 += BATCH) {
+    u32x4 kv[KUNROLL];
 #pragma unroll
-    for (int u = 0; u < UNROLL; ++u) {
-      const int rr = (k0 + u) * GPW + grp;
+    for (int u = 0; u < KUNROLL; ++u) {
+      const int rr = b0 + u * GPW + grp;
       kv[u] = rr < nr ? __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(Kb + (int64_t)rr * D)) : u32x4{};
     }
 #pragma unroll
-    for (int u = 0; u < UNROLL; ++u) {
-      const int rr = (k0 + u) * GPW + grp;
-      float kf[8];
+    for (int u = 0; u < KUNROLL; ++u)
+      *reinterpret_cast<u32x4*>(stage + (u * GPW + grp) * KSTRIDE + li * 16) = kv[u];
+    __builtin_amdgcn_wave_barrier();
+    bf16x8 a[STEPS];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        kf[2 * e] = __uint_as_float(kv[u][e] << 16);
-        kf[2 * e + 1] = __uint_as_float(kv[u][e] & 0xffff0000u);
+    for (int s = 0; s < STEPS; ++s)
+      a[s] = as_bf16x8(*reinterpret_cast<const u32x4*>(stage + col * KSTRIDE + half * D + 16 * s));
+    f32x16 acc = mfma32(a[0], qb[0], f32x16{});
+#pragma unroll
+    for (int s = 1; s < STEPS; ++s) acc = mfma32(a[s], qb[s], acc);
+    if (col < QG) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int rr = b0 + acc_row(r, half);
+        if (rr < nr) s_score[wave][rr][col] = acc[r] * p.c2;
       }
-      float v[QG];
-#pragma unroll
-      for (int t = 0; t < QG; ++t) {
-        float a = 0.f;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) a = __builtin_fmaf(q[t][e], kf[e], a);
-        v[t] = a;
-      }
-      const float s = reduce_scatter<LPR, QG>(v, li);
-      constexpr int SH = (LPR / QG == 4) ? 2 : ((LPR / QG == 2) ? 1 : 0);  // log2 lanes per query after the scatter
-      if (rr < nr && (li & ((1 << SH) - 1)) == 0) s_score[wave][rr][li >> SH] = s;
     }
+    __builtin_amdgcn_wave_barrier();
   }
   // the first batch of value rows does not depend on the scores: issue it now
   const uint16_t* Vb = p.V + r0 * D + 8 * li;
