@@ -40,20 +40,18 @@ namespace {
 
 constexpr int DC_WAVES = 4;
 constexpr int DC_THREADS = DC_WAVES * WAVE;
-// Rows per wave chunk. Each wave's batches of loads run one after another, so
-// the rows in flight are the number of waves times a batch: short chunks keep
-// enough waves in flight, at the price of more partials to merge, as long as
-// the waves fit on the chip at once. With 4 queries per wave: 64 rows from
-// 65536 rows of cache, else 32 (measured: the 16752-row cache of the 16k
-// KVpop layer decodes in 23 us with 32-row chunks, 28 with 64, 35 with 128;
-// the 244110-row cache of the 32k layer in 44.6 us with 64, 45.5 with 128,
-// 51 with 32). With 8 queries per wave (about 180 registers, 2 waves per
-// SIMD) 64-row chunks of a large cache no longer fit in one round: 128 rows
-// from 65536 rows of cache (the 241024-row cache of the 120k layer: 67 us,
-// against 73 with 64), 64 from 8192, else 32.
+// Rows per wave chunk: the longest of 128, 64 and 32 that still gives at
+// least WAVES_WANTED chunks for a cache of `capacity` rows (about 1.5 waves
+// per SIMD). Longer chunks mean fewer partials to merge and fewer waves
+// paying the per-wave start-up; enough waves keep the rows in flight.
+// Measured with the scores on the matrix cores (us, 4 / 8 queries per
+// wave): 244,110 rows 31.4 with 128-row chunks, 35.0 with 64, 42.1 with 32;
+// 241,024 rows (8 queries) 36.0 / 44.4 / 51.8; 65,536 rows 24.7 / 20.5 /
+// 20.4 (8 queries: 29.5 / 23.4 / 22.7); 16,752 rows 24.5 / 20.7 / 20.7.
+constexpr int64_t WAVES_WANTED = 1536;
 constexpr int queries_per_wave(int G, int n_q) { return G * n_q <= 4 ? 4 : 8; }
-constexpr int wrows_for(int64_t capacity, int qg) {
-  return qg == 4 ? (capacity >= 65536 ? 64 : 32) : (capacity >= 65536 ? 128 : (capacity >= 8192 ? 64 : 32));
+constexpr int wrows_for(int64_t capacity) {
+  return capacity >= 128 * WAVES_WANTED ? 128 : (capacity >= 64 * WAVES_WANTED ? 64 : 32);
 }
 
 // Floats per partial record: m, l, two pad words, then o[D] at a 16-byte offset.
@@ -436,7 +434,7 @@ __global__ __launch_bounds__(CB_THREADS) void decode_combine(DecParams p) {
 }  // namespace
 
 int wrows_of(const kvs_decode_desc& d) {
-  return wrows_for(d.capacity, queries_per_wave(d.n_qheads / d.n_kvheads, d.n_q));
+  return wrows_for(d.capacity);
 }
 
 int64_t decode_wave_chunks_max(const kvs_decode_desc& d) { return d.capacity / wrows_of(d) + d.n_kvheads; }

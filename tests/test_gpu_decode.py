@@ -1,12 +1,13 @@
 """Decode attention over the compacted per-head cache (kvscore_decode) against
 the CPU oracle through the C ABI: ragged and empty heads, D = 64 and 128,
 several query groups per head, wave chunks of 32, 64 and 128 rows (chosen
-by the cache's size and the queries per wave), clamped offsets, and the
+by the cache's size), 4 and 8 queries per wave, clamped offsets, and the
 full pipeline
 kv_evict -> kvscore_decode against oracle select -> compact -> decode.
 
-Tolerance: scores, exponentials and sums are fp32 (chunks of 128 rows, then a
-merge over chunks), so the summation error stays far below 2^-12 of
+Tolerance: scores (bf16 products summed in fp32 on the matrix cores),
+exponentials and sums are fp32 (chunks of at most 128 rows, then a merge
+over chunks), so the summation error stays far below 2^-12 of
 sum_r a_r |v_r|; O is rounded once to bf16 (2^-8 |O|):
     |O_gpu - O_ref| <= 2^-8 |O_ref| + 2^-12 sum_r a_r |v_r|,  |LSE err| <= 1e-3,
 and a head with no rows gives exactly O = 0, LSE = -inf.
@@ -53,12 +54,14 @@ CASES = [
     ("d128-g4-chunk-edges", 16, 4, 128, [1, 128, 129, 3000], 1),
     ("g5-three-tokens-two-query-groups", 10, 2, 128, [700, 45], 3),
     ("mha-one-row", 4, 4, 128, [1, 2, 3, 4], 1),
-    # the wave-chunk size follows the cache and the queries per wave: 32 rows
-    # up to here, then 32, 64 (4 queries), 64 and 128 (8 queries)
+    # the wave-chunk size follows the cache: 32 rows below 98,304 rows of
+    # cache, 64 below 196,608, else 128; 4 or 8 queries per wave
     ("d128-32-row-chunks-many", 16, 4, 128, [9000, 33, 32, 7000], 1),
-    ("d128-4q-64-row-chunks", 8, 2, 128, [40000, 30001], 1),
-    ("g5-8q-64-row-chunks", 10, 2, 128, [6000, 4001], 1),
-    ("d64-8q-128-row-chunks", 8, 2, 64, [40000, 30001], 2),
+    ("g5-8q-32-row-chunks", 10, 2, 128, [6000, 4001], 1),
+    ("d128-4q-64-row-chunks", 8, 2, 128, [60000, 40001], 1),
+    ("d64-8q-64-row-chunks", 8, 2, 64, [50000, 48305], 2),
+    ("d128-8q-128-row-chunks", 10, 2, 128, [120000, 76609], 1),
+    ("d64-4q-128-row-chunks", 4, 2, 64, [100000, 100001], 1),
     # heads are located 64 at a time (one per lane): 70 heads span two such
     # groups, with empty heads on both sides of the group edge
     ("d64-70-heads-two-lane-groups", 140, 70, 64,
