@@ -218,13 +218,13 @@ def test_decode_rejects(L, kw, code):
 def test_decode_workspace_and_pointers(L):
     d = _ddesc()
     need = L.kvscore_decode_workspace_bytes(ctypes.byref(d))
-    # 4 queries per wave: chunks of 32 rows under 65536 rows of cache, else 64;
-    # 8 queries per wave: 32 under 8192, 64 under 65536, else 128:
+    # chunks of 32 rows under 98,304 rows of cache, 64 under 196,608, else 128
+    # (with 4 or 8 queries per wave alike):
     # (capacity // rows + heads) chunks x queries per KV head x (4 + 128) floats
     assert need == (1000 // 32 + 2) * 4 * 132 * 4
-    for cap, rows in ((8192, 32), (65535, 32), (65536, 64), (244110, 64)):
+    for cap, rows in ((8192, 32), (98303, 32), (98304, 64), (196607, 64), (196608, 128), (244110, 128)):
         assert L.kvscore_decode_workspace_bytes(ctypes.byref(_ddesc(capacity=cap))) == (cap // rows + 2) * 4 * 132 * 4
-    for cap, rows in ((8191, 32), (8192, 64), (65535, 64), (65536, 128)):  # G = 5: 8 queries per wave
+    for cap, rows in ((65536, 32), (98304, 64), (241024, 128)):  # G = 5: 8 queries per wave
         d5 = _ddesc(capacity=cap, n_qheads=10)
         assert L.kvscore_decode_workspace_bytes(ctypes.byref(d5)) == (cap // rows + 2) * 5 * 132 * 4
     D = L.kvscore_decode
