@@ -54,6 +54,16 @@ constexpr int wrows_for(int64_t capacity) {
   return capacity >= 128 * WAVES_WANTED ? 128 : (capacity >= 64 * WAVES_WANTED ? 64 : 32);
 }
 
+// Orders this wave's LDS writes before its later LDS reads by other lanes:
+// wait until the wave's LDS operations have completed (lgkmcnt 0), and keep
+// the compiler from moving LDS accesses across the point. Each wave of
+// decode_partial works in an LDS area of its own, so no workgroup barrier is
+// needed (and none would be safe where the waves' loop counts differ).
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_s_waitcnt(0xc07f);  // vmcnt and expcnt unconstrained, lgkmcnt(0)
+  __builtin_amdgcn_wave_barrier();
+}
+
 // Floats per partial record: m, l, two pad words, then o[D] at a 16-byte offset.
 constexpr int REC(int D) { return D + 4; }
 
@@ -181,7 +191,7 @@ __global__ __launch_bounds__(DC_THREADS) void decode_partial(DecParams p) {
   const int qg = blockIdx.y;
   int h = 0;
   int64_t r0 = 0, r1 = 0;
-  // waves past the last chunk do no work (nr = 0) but still reach the barrier
+  // waves past the last chunk do no work (nr = 0)
   const bool active = find_chunk(p, wc, h, r0, r1);
   const int nr = active ? (int)(r1 - r0) : 0;
   const int nq_head = p.G * p.n_q;
@@ -207,8 +217,8 @@ __global__ __launch_bounds__(DC_THREADS) void decode_partial(DecParams p) {
   // 16 bytes each) are staged in this wave's LDS area, read back as the A
   // operands of S = K_batch Q^T (keys as rows, queries as columns), and each
   // lane's 16 scores (query col, rows acc_row(r, half)) go to s_score,
-  // scaled to the exp2 domain. The wave's own LDS accesses are in order, so
-  // staging needs no barrier.
+  // scaled to the exp2 domain. Staging is ordered within the wave (no
+  // workgroup barrier: each wave has its own area).
   char* const stage = s_k[wave];
   const uint16_t* Kb = p.K + r0 * D + 8 * li;
   for (int b0 = 0; b0 < nr; b0 += BATCH) {
@@ -221,7 +231,7 @@ __global__ __launch_bounds__(DC_THREADS) void decode_partial(DecParams p) {
 #pragma unroll
     for (int u = 0; u < KUNROLL; ++u)
       *reinterpret_cast<u32x4*>(stage + (u * GPW + grp) * KSTRIDE + li * 16) = kv[u];
-    __builtin_amdgcn_wave_barrier();
+    wave_lds_sync();
     bf16x8 a[STEPS];
 #pragma unroll
     for (int s = 0; s < STEPS; ++s)
@@ -246,7 +256,7 @@ __global__ __launch_bounds__(DC_THREADS) void decode_partial(DecParams p) {
     const int rr = u * GPW + grp;
     vpre[u] = rr < nr ? __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(Vb + (int64_t)rr * D)) : u32x4{};
   }
-  __syncthreads();  // scores visible (each wave reads only its own region)
+  wave_lds_sync();  // scores visible to the wave's other lanes
 
   // ---- softmax of the chunk, once per (row, query): lane handles query
   // lane / LPQ and rows lane % LPQ + LPQ*k; the scores become p = exp2(s - m)
@@ -267,7 +277,7 @@ __global__ __launch_bounds__(DC_THREADS) void decode_partial(DecParams p) {
 #pragma unroll
     for (int msk = 1; msk < LPQ; msk <<= 1) lsum += __shfl_xor(lsum, msk);
   }
-  __syncthreads();  // probabilities visible
+  wave_lds_sync();  // probabilities visible
   float mq[QG], l[QG];
 #pragma unroll
   for (int t = 0; t < QG; ++t) {
