@@ -112,6 +112,25 @@ def test_max_score_given_lse_input():
     check_scores(host(s), ref, "given-lse")
 
 
+@pytest.mark.parametrize("D", [128, 64])
+def test_max_score_long_context_form(D):
+    """Enough 768-key blocks (>= 4 rounds of workgroups) for the score pass's
+    long-context form (3 resident key subtiles per wave, 64-row query tiles),
+    with a ragged last key block and a ragged query tile, on a stand-in
+    normaliser."""
+    r = synth.Recipe(Hq=64, Hkv=64, D=D, n_ctx=12289, n_q=100, chunk=100)
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    assert -(-r.n_ctx // 768) * r.Hkv >= 4 * cus, "sized for the long-context form on this GPU"
+    d = synth.draw(r, 305)
+    lse_in = synth.lse_values(305, r.Hq, r.n_q, 6.0, 9.0)
+    hn = synth.lse_values(306, 1, r.n_q, 1.0, 3.0)[0].astype(np.float32)
+    say(f"[max] long-context form D={D}")
+    s = kvs.max_scores(dev_bf16(d["Q"]), dev_bf16(d["Kctx"]), dev_f32(lse_in), scale=d["scale"], hnorm=dev_f32(hn))
+    torch.cuda.synchronize()
+    ref = oracle.max_scores(d["Q"], d["Kctx"], lse_in, d["scale"], r.Hkv, hnorm=hn)
+    check_scores(host(s), ref, f"long-context D={D}")
+
+
 def test_max_score_accumulate_over_chunks_equals_one_call():
     r = synth.Recipe(Hq=8, Hkv=2, D=128, n_ctx=600, n_q=1000, chunk=400, value_norms=True)
     d = synth.draw(r, 404)
