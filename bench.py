@@ -208,9 +208,25 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_start
     ms_per_step = wall * 1e3 / args.steps
-    t_lse = float(np.mean([a[0].elapsed_time(a[1]) for a in evs]))
-    t_score = float(np.mean([a[1].elapsed_time(a[2]) for a in evs]))
-    t_evict = float(np.mean([a[2].elapsed_time(a[3]) for a in evs]))
+    per_step = {k: [a[i].elapsed_time(a[i + 1]) for a in evs] for i, k in enumerate(("lse", "score", "evict"))}
+    t_lse = float(np.mean(per_step["lse"]))
+    t_score = float(np.mean(per_step["score"]))
+    t_evict = float(np.mean(per_step["evict"]))
+
+    # Eviction with cold caches (not part of the step): before each
+    # repetition a 512 MiB write pushes the scores and K/V out of L2 and the
+    # Infinity Cache.
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+    cold = []
+    for i in range(10):
+        flush.fill_(i & 0xFF)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        kvs.evict(S, K, V, window=wl.window, workspace=ws, outputs=outs, **sel)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        cold.append(e0.elapsed_time(e1))
+    del flush
 
     # Adjacent kernels, timed after the step (not part of it): the attention
     # forward that returns O with the same LSE.
@@ -347,11 +363,15 @@ def main():
                      "frac": score_tflops / PEAK_BF16_TFLOPS, "traffic": traffic,
                      "kernel": "score pass (" + ("kvscore_futuremass" if sum_mode else "kvscore_max") + ")"},
         "kernels_ms": {"lse": t_lse, "score": t_score, "evict": t_evict},
+        "kernels_ms_median": {k: float(np.median(v)) for k, v in per_step.items()},
+        "kernels_ms_min": {k: float(np.min(v)) for k, v in per_step.items()},
         "lse_pass": {"tflops": lse_tflops, "frac_of_bf16_peak": lse_tflops / PEAK_BF16_TFLOPS},
         "score_pass": {"tflops": score_tflops, "flops": score_flops},
         "evict": {"gbs": evict_gbs, "frac_of_hbm_peak": evict_gbs / PEAK_HBM_GBS, "bytes": ev_bytes,
                   "kept_per_head": kept.tolist(),
-                  "compression_per_head": [round(acc.compression_ratio(int(x), r.n_ctx), 4) for x in kept]},
+                  "compression_per_head": [round(acc.compression_ratio(int(x), r.n_ctx), 4) for x in kept],
+                  "cold_caches": {"median_ms": float(np.median(cold)), "min_ms": float(np.min(cold)), "reps": len(cold),
+                                  "gbs_median": ev_bytes / (float(np.median(cold)) * 1e-3) / 1e9}},
     }
     if not args.no_cpu_baseline and not sum_mode:
         _log("[bench] timing the CPU oracle on a sample")
