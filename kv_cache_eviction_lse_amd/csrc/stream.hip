@@ -32,7 +32,7 @@ namespace {
 constexpr int ST_THREADS = 512;
 constexpr int TILE = ST_THREADS;  // leaving tokens decided per pass
 constexpr int UNR = 4;            // rows per thread in flight in a copy
-constexpr int CHUNK = 4096;       // leaving tokens per workgroup in a bulk call
+constexpr int CHUNK = 1024;       // leaving tokens per workgroup in a bulk call
 
 struct StreamParams {
   const float* new_scores;
@@ -116,10 +116,21 @@ __device__ int block_sum(int v, int* s_wave) {
 }
 
 // Kept tokens among leaving tokens t0 .. t1-1 (block-wide, every thread).
+// CU_UNR score loads per thread are issued before any is tested, so a long
+// count is not a chain of one load round trip per pass.
+constexpr int CU_UNR = 8;
 template <int D>
 __device__ int64_t count_kept(const HeadCall<D>& c, int64_t t0, int64_t t1, int* s_wave) {
   int k = 0;
-  for (int64_t t = t0 + threadIdx.x; t < t1; t += ST_THREADS) k += c.keeps(c.L0 + t);
+  int64_t t = t0 + threadIdx.x;
+  for (; t + (CU_UNR - 1) * ST_THREADS < t1; t += CU_UNR * ST_THREADS) {
+    bool kk[CU_UNR];
+#pragma unroll
+    for (int u = 0; u < CU_UNR; ++u) kk[u] = c.keeps(c.L0 + t + u * ST_THREADS);
+#pragma unroll
+    for (int u = 0; u < CU_UNR; ++u) k += kk[u];
+  }
+  for (; t < t1; t += ST_THREADS) k += c.keeps(c.L0 + t);
   return block_sum(k, s_wave);
 }
 

@@ -68,10 +68,13 @@ CASES = [
     ("window-one", 4, 64, 1, [1, 2, 1, 7]),
     ("window-never-filled", 2, 128, 64, [5, 10, 1]),
     ("many-heads", 40, 64, 4, [3, 1, 20, 1]),
-    # bulk calls split over workgroups of 4096 leaving tokens (ring tokens
+    # bulk calls split over workgroups of 1024 leaving tokens (ring tokens
     # leave in the first chunk)
     ("bulk-multi-block-after-a-partial-ring", 2, 128, 16, [5, 10000, 1, 3]),
     ("bulk-multi-block-full-ring-d64", 3, 64, 128, [300, 9000, 2]),
+    # the widest window a split bulk call allows (w = 1024): its 1024 ring
+    # tokens are exactly the first chunk, the call's 1100 leaving tokens two chunks
+    ("bulk-two-chunks-widest-window", 2, 128, 1024, [1500, 1100, 1]),
 ]
 
 
