@@ -78,6 +78,17 @@ def test_decode_parity(name, Hq, Hkv, D, counts, n_q):
     _check(host_bits(O), host(L), Q, Kc, Vc, offs, 0.09, name)
 
 
+def test_decode_is_deterministic():
+    """Two calls give bit-identical O and LSE (fixed-order merges, no atomics)."""
+    Q, Kc, Vc, offs = _case(119, 10, 2, 128, [60000, 40001], 1)
+    args = (dev_bf16(Q), dev_bf16(Kc), dev_bf16(Vc), torch.from_numpy(offs).cuda())
+    say("[decode] determinism")
+    O1, L1 = kvs.decode(*args, scale=0.09)
+    O2, L2 = kvs.decode(*args, scale=0.09)
+    torch.cuda.synchronize()
+    assert torch.equal(O1.view(torch.int16), O2.view(torch.int16)) and torch.equal(L1, L2)
+
+
 def test_decode_clamps_offsets():
     """Offsets past the cache or decreasing are clamped to [0, capacity] and made monotone."""
     Q, Kc, Vc, offs = _case(113, 4, 2, 128, [200, 300], 1)
