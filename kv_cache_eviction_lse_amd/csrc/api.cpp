@@ -152,7 +152,7 @@ KVS_API int kvscore_lse(const kvs_attn_desc* d, const kvs_bf16* Q, const kvs_bf1
   if (d->n_q > 0 && !lse) return fail(KVS_EINVAL, "lse is NULL");
   int cus;
   if ((st = check_device(&cus))) return st;
-  return hip_status(kvs::launch_lse(*d, Q, K, Kself, lse, static_cast<hipStream_t>(stream)), "kvscore_lse");
+  return hip_status(kvs::launch_lse(*d, Q, K, Kself, lse, cus, static_cast<hipStream_t>(stream)), "kvscore_lse");
 }
 
 KVS_API int kvscore_attention(const kvs_attn_desc* d, const kvs_bf16* Q, const kvs_bf16* K, const kvs_bf16* Kself,

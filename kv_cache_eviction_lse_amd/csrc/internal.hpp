@@ -9,7 +9,7 @@
 namespace kvs {
 
 hipError_t launch_lse(const kvs_attn_desc& d, const uint16_t* Q, const uint16_t* K, const uint16_t* Kself,
-                      float* lse, hipStream_t s);
+                      float* lse, int num_cus, hipStream_t s);
 
 hipError_t launch_score_max(const kvs_attn_desc& d, const uint16_t* Q, const uint16_t* K, const float* lse,
                             const float* vnorm, const float* hnorm, float* scores, int accumulate,

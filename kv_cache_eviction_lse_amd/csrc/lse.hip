@@ -312,16 +312,201 @@ __global__ __launch_bounds__(LSE_WAVES * WAVE, 3) void lse_kernel(LseParams p) {
   }
 }
 
+// Small layers (fewer workgroups of the kernel above than CUs): the pass is
+// then as long as one wave's walk over the keys, so the keys are split
+// instead. A workgroup serves LSE_NQ subtiles (one 32-position block of one
+// query head each); all LSE_WAVES waves hold both as B operands and walk
+// every LSE_WAVES-th key tile, reading each tile's A operands straight from
+// memory (buffer loads in the operand layout, one tile ahead), with no LDS
+// staging and no barrier in the loop. The waves' running (offset, sum)
+// pairs are merged through LDS at the end. Same softmax arithmetic and
+// visibility rules as lse_kernel.
 template <int D, bool CAUSAL>
-hipError_t run(const LseParams& p, int nblocks, hipStream_t s) {
-  hipLaunchKernelGGL((lse_kernel<D, CAUSAL>), dim3(nblocks), dim3(LSE_WAVES * WAVE), 0, s, p);
+__global__ __launch_bounds__(LSE_WAVES * WAVE, 2) void lse_split_kernel(LseParams p) {
+  using T = KTile<D>;
+  __shared__ float s_o[LSE_WAVES][LSE_NQ][WAVE], s_l[LSE_WAVES][LSE_NQ][WAVE];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int half = lane >> 5;
+  const int col = lane & 31;
+
+  const int b = blockIdx.x;
+  const int h = b % p.Hkv;
+  const int nbx = (p.n_sub + LSE_NQ - 1) / LSE_NQ;
+  const int bx = CAUSAL ? nbx - 1 - b / p.Hkv : b / p.Hkv;
+  const int u_lo = bx * LSE_NQ;
+  const int u_hi = min(u_lo + LSE_NQ, p.n_sub) - 1;
+
+  const int64_t pos_lo = (int64_t)(u_lo / p.G) * 32;
+  const int64_t pos_end = min((int64_t)(u_hi / p.G) * 32 + 32, p.n_q);
+  const int64_t chunk = CAUSAL ? 1 : p.chunk;
+  const int64_t self_lo = CAUSAL ? 0 : (pos_lo / chunk) * chunk;
+  const int64_t n_ctx_tiles = CAUSAL ? 0 : (p.n_ctx + 31) / 32;
+  const int64_t n_tiles = n_ctx_tiles + (pos_end - self_lo + 31) / 32;
+
+  int sub_g[LSE_NQ];
+  int64_t sub_pos[LSE_NQ];
+  bool sub_ok[LSE_NQ];
+  bf16x8 qreg[LSE_NQ][T::STEPS];
+#pragma unroll
+  for (int q = 0; q < LSE_NQ; ++q) {
+    const int u = u_lo + q;
+    sub_ok[q] = u < p.n_sub;
+    sub_g[q] = h * p.G + (sub_ok[q] ? u % p.G : 0);
+    sub_pos[q] = sub_ok[q] ? (int64_t)(u / p.G) * 32 : 0;
+    const int64_t j = min(sub_pos[q] + col, p.n_q - 1);
+    const uint16_t* qp = p.Q + (int64_t)sub_g[q] * p.q_hs + j * p.q_ts + half * (D / 2);
+#pragma unroll
+    for (int s = 0; s < T::STEPS; ++s) {
+      u32x4 v = ld16(qp + 8 * s);
+      pin(v);
+      qreg[q][s] = as_bf16x8(v);
+    }
+  }
+
+  // A operands of tile tt (lane: key row col of the tile, elements
+  // [half*D/2 + 8s, +8) of step s) through a buffer resource over the rows
+  // the segment has; rows past the end read as zero and are masked.
+  const int n_ctx_tiles_s = (int)n_ctx_tiles, n_ctx_s = (int)p.n_ctx, pos_end_s = (int)pos_end;
+  const int self_lo_s = (int)self_lo, k_ts_s = (int)p.k_ts;
+  const int ks_ts_s = CAUSAL ? k_ts_s : (int)p.ks_ts;
+  const uint16_t* const ctx_base = p.K + (int64_t)h * p.k_hs;
+  const uint16_t* const self_base = CAUSAL ? ctx_base : p.Kself + (int64_t)h * p.ks_hs;
+  auto load_a = [&](int tt, bf16x8 (&a)[T::STEPS]) {
+    const bool ctx = tt < n_ctx_tiles_s;
+    const int k0 = ctx ? tt * 32 : self_lo_s + (tt - n_ctx_tiles_s) * 32;
+    const int kend = ctx ? n_ctx_s : pos_end_s;
+    const int ts = ctx ? k_ts_s : ks_ts_s;
+    const int rows = min(kend - k0, 32);
+    const __amdgpu_buffer_rsrc_t r = tile_rsrc((ctx ? ctx_base : self_base) + (int64_t)k0 * ts, rows * ts * 2);
+    const int off = col * ts * 2 + half * D;
+#pragma unroll
+    for (int s = 0; s < T::STEPS; ++s) a[s] = as_bf16x8(buf_ld16(r, off + 16 * s));
+  };
+
+  const float c2 = p.scale * LOG2E;
+  float o_run[LSE_NQ], l_run[LSE_NQ];
+  int lane_j[LSE_NQ], lane_cs[LSE_NQ], sub_pj[LSE_NQ], sub_cs_first[LSE_NQ], sub_cs_last[LSE_NQ];
+#pragma unroll
+  for (int q = 0; q < LSE_NQ; ++q) {
+    o_run[q] = -3.402823466e38f;
+    l_run[q] = 0.f;
+    sub_pj[q] = (int)sub_pos[q];
+    lane_j[q] = sub_pj[q] + col;
+    lane_cs[q] = CAUSAL ? 0 : (int)((lane_j[q] / chunk) * chunk);
+    sub_cs_first[q] = CAUSAL ? 0 : (int)((sub_pj[q] / chunk) * chunk);
+    sub_cs_last[q] = CAUSAL ? 0 : (int)(((sub_pj[q] + 31) / chunk) * chunk);
+  }
+  auto exp_sum = [&](const f32x16& x, float o) {
+    float e[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) e[r] = fast_exp2(__builtin_fmaf(x[r], c2, -o));
+#pragma unroll
+    for (int w = 8; w >= 1; w >>= 1)
+#pragma unroll
+      for (int r = 0; r < w; ++r) e[r] += e[r + w];
+    return e[0];
+  };
+  auto softmax_update = [&](int q, const f32x16& x) {
+    float sum = exp_sum(x, o_run[q]);
+    if (sum > LAZY_LIMIT) {
+      float tm = max3(x[0], x[1], x[2]);
+#pragma unroll
+      for (int r = 3; r < 15; r += 2) tm = max3(tm, x[r], x[r + 1]);
+      tm = fmaxf(tm, x[15]);
+      const float o_new = fmaxf(o_run[q], tm * c2);
+      l_run[q] *= fast_exp2(o_run[q] - o_new);
+      o_run[q] = o_new;
+      sum = exp_sum(x, o_new);
+    }
+    l_run[q] += sum;
+  };
+
+  // this wave's tiles: wave, wave + LSE_WAVES, ...; the next one's operands
+  // are in flight while the current one is processed
+  const int n_tiles_i = (int)n_tiles;
+  bf16x8 a_cur[T::STEPS], a_nxt[T::STEPS];
+  if (wave < n_tiles_i) load_a(wave, a_cur);
+  for (int tt = wave; tt < n_tiles_i; tt += LSE_WAVES) {
+    if (tt + LSE_WAVES < n_tiles_i) load_a(tt + LSE_WAVES, a_nxt);
+    const bool is_ctx = tt < n_ctx_tiles_s;
+    const int k0 = is_ctx ? tt * 32 : self_lo_s + (tt - n_ctx_tiles_s) * 32;
+    const int kend = is_ctx ? n_ctx_s : pos_end_s;
+#pragma unroll
+    for (int q = 0; q < LSE_NQ; ++q) {
+      const int pj = sub_pj[q];
+      bool run, full;
+      if (is_ctx) {
+        run = sub_ok[q];
+        full = k0 + 31 < kend;
+      } else {
+        run = sub_ok[q] && !((k0 > pj + 31) || (k0 + 31 < sub_cs_first[q]));
+        full = (k0 + 31 <= pj) && (k0 >= sub_cs_last[q]) && (k0 + 31 < kend);
+      }
+      if (!run) continue;
+      f32x16 x = mfma32(a_cur[0], qreg[q][0], f32x16{});
+#pragma unroll
+      for (int s = 1; s < T::STEPS; ++s) x = mfma32(a_cur[s], qreg[q][s], x);
+      if (!full) {
+        const int kb = k0 + 4 * half;
+        const int j = lane_j[q], cs = lane_cs[q];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = kb + 8 * (r >> 2) + (r & 3);
+          const bool vis = is_ctx ? (key < kend) : (key <= j && key >= cs);
+          x[r] = vis ? x[r] : -INFINITY;
+        }
+      }
+      softmax_update(q, x);
+    }
+#pragma unroll
+    for (int s = 0; s < T::STEPS; ++s) a_cur[s] = a_nxt[s];
+  }
+
+  // ---- merge the waves' and half-waves' (offset, sum) pairs, write natural-log LSE
+#pragma unroll
+  for (int q = 0; q < LSE_NQ; ++q) {
+    s_o[wave][q][lane] = o_run[q];
+    s_l[wave][q][lane] = l_run[q];
+  }
+  __syncthreads();
+  if (wave == 0 && half == 0) {
+#pragma unroll
+    for (int q = 0; q < LSE_NQ; ++q) {
+      float Mc = -3.402823466e38f;
+#pragma unroll
+      for (int w = 0; w < LSE_WAVES; ++w)
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf) Mc = fmaxf(Mc, s_o[w][q][col + 32 * hf]);
+      float L = 0.f;
+#pragma unroll
+      for (int w = 0; w < LSE_WAVES; ++w)
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf) {
+          const float l = s_l[w][q][col + 32 * hf];
+          L += l > 0.f ? l * fast_exp2(s_o[w][q][col + 32 * hf] - Mc) : 0.f;
+        }
+      const int64_t j = sub_pos[q] + col;
+      if (sub_ok[q] && j < p.n_q) p.lse[(int64_t)sub_g[q] * p.n_q + j] = (Mc + __log2f(L)) * LN2;
+    }
+  }
+}
+
+template <int D, bool CAUSAL>
+hipError_t run(const LseParams& p, int nblocks, bool split, hipStream_t s) {
+  if (split)
+    hipLaunchKernelGGL((lse_split_kernel<D, CAUSAL>), dim3(nblocks), dim3(LSE_WAVES * WAVE), 0, s, p);
+  else
+    hipLaunchKernelGGL((lse_kernel<D, CAUSAL>), dim3(nblocks), dim3(LSE_WAVES * WAVE), 0, s, p);
   return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_lse(const kvs_attn_desc& d, const uint16_t* Q, const uint16_t* K, const uint16_t* Kself,
-                      float* lse, hipStream_t s) {
+                      float* lse, int num_cus, hipStream_t s) {
   if (d.n_q == 0) return hipSuccess;
   LseParams p{};
   p.Q = Q; p.K = K; p.Kself = Kself; p.lse = lse;
@@ -332,10 +517,14 @@ hipError_t launch_lse(const kvs_attn_desc& d, const uint16_t* Q, const uint16_t*
   p.Hkv = d.n_kvheads; p.G = d.n_qheads / d.n_kvheads; p.scale = d.scale;
   const int64_t n_sub = ((d.n_q + 31) / 32) * p.G;
   p.n_sub = (int)n_sub;
-  const int64_t nblocks = ((n_sub + SUB_PER_BLOCK - 1) / SUB_PER_BLOCK) * p.Hkv;
+  // fewer workgroups than CUs: split the keys over the waves instead
+  const bool split = ((n_sub + SUB_PER_BLOCK - 1) / SUB_PER_BLOCK) * p.Hkv < num_cus;
+  const int64_t per_block = split ? LSE_NQ : SUB_PER_BLOCK;
+  const int64_t nblocks = ((n_sub + per_block - 1) / per_block) * p.Hkv;
   const bool causal = d.mask == KVS_MASK_CAUSAL;
-  if (d.head_dim == 128) return causal ? run<128, true>(p, (int)nblocks, s) : run<128, false>(p, (int)nblocks, s);
-  return causal ? run<64, true>(p, (int)nblocks, s) : run<64, false>(p, (int)nblocks, s);
+  if (d.head_dim == 128)
+    return causal ? run<128, true>(p, (int)nblocks, split, s) : run<128, false>(p, (int)nblocks, split, s);
+  return causal ? run<64, true>(p, (int)nblocks, split, s) : run<64, false>(p, (int)nblocks, split, s);
 }
 
 }  // namespace kvs

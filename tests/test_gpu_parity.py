@@ -43,6 +43,12 @@ LSE_CASES = [
     ("causal-g6-ragged", dict(Hq=6, Hkv=1, D=128, n_ctx=777, n_q=777, mask="causal"), "causal", 0),
     ("causal-g4-sinks-d64", dict(Hq=8, Hkv=2, D=64, n_ctx=1000, n_q=1000, mask="causal", sinks=4), "causal", 0),
     ("causal-tiny", dict(Hq=2, Hkv=1, D=128, n_ctx=3, n_q=3, mask="causal"), "causal", 0),
+    # the cases above have fewer workgroups than CUs, so they take the pass's
+    # key-split form; these two are large enough (256 workgroups of 8
+    # subtiles) for the form that shares key tiles through LDS
+    ("repeat-lds-form-ragged", dict(Hq=32, Hkv=8, D=128, n_ctx=700, n_q=2048, lowrank_rank=8,
+                                    lowrank_scale=2.0), "repeat", 1000),
+    ("causal-lds-form", dict(Hq=32, Hkv=8, D=128, n_ctx=2048, n_q=2048, mask="causal", sinks=4), "causal", 0),
 ]
 
 
