@@ -8,7 +8,10 @@
 // values[indices]).
 //
 // Kernels (one grid of blocks of EPB keys per head, unless noted):
-//   top-k only: evict_zero, then three radix-digit histogram passes over the
+//   top-k with at most SEL_MAX candidates per head (per-head budget):
+//     evict_select_small, one workgroup per head, does the three passes below
+//     on an LDS histogram and leaves T and the quota in the head's state.
+//   other top-k: evict_zero, then three radix-digit histogram passes over the
 //     order-preserving 32-bit keys of the candidate scores (bits 31..21,
 //     20..10, 9..0). Each pass re-derives, from the previous passes'
 //     histograms, the prefix of the k-th largest key, so no separate "find"
@@ -54,6 +57,7 @@ struct EvictParams {
   int64_t n, n_cand, kprime;  // kprime: per head, or for the whole layer when layer != 0
   int Hkv, D, nb, mode;
   int layer;  // top-k over all heads' candidates together (one histogram, one quota)
+  int small_sel;  // top-k found by evict_select_small (T and quota already in state)
   float tau;
 };
 
@@ -69,9 +73,10 @@ __device__ __forceinline__ uint32_t order_key(float s) {
 __device__ __forceinline__ int digit_shift(int pass) { return pass == 0 ? 21 : (pass == 1 ? 10 : 0); }
 __device__ __forceinline__ uint32_t digit_mask(int pass) { return pass == 2 ? 1023u : 2047u; }
 
-// Exclusive prefix sum over the block's threads (tid order); *total gets the sum.
+// Exclusive prefix sum over the block's NT threads (tid order); *total gets the sum.
+template <int NT = EV_THREADS>
 __device__ int block_exclusive_scan(int v, int* total) {
-  __shared__ int s_wave[EV_THREADS / WAVE];
+  __shared__ int s_wave[NT / WAVE];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   int x = v;
 #pragma unroll
@@ -83,7 +88,7 @@ __device__ int block_exclusive_scan(int v, int* total) {
   __syncthreads();
   int before = 0, tot = 0;
 #pragma unroll
-  for (int w = 0; w < EV_THREADS / WAVE; ++w) {
+  for (int w = 0; w < NT / WAVE; ++w) {
     const int t = s_wave[w];
     if (w < wave) before += t;
     tot += t;
@@ -93,41 +98,104 @@ __device__ int block_exclusive_scan(int v, int* total) {
   return before + x - v;
 }
 
+// Radix-digit pass `pass` over a finished histogram: the digit (counted from
+// the top) that holds the rank-th largest key, and the number of keys in
+// the higher digits. Block-wide over NT threads; every thread returns the
+// same values.
+template <int NT = EV_THREADS>
+__device__ void find_digit(const uint32_t* bins, int pass, int rank, int& digit, int& cum_out) {
+  __shared__ int s_digit, s_cum;
+  const int nbins = pass == 2 ? 1024 : 2048;
+  const int per = nbins / NT;  // bins per thread
+  const int rt = NT - 1 - (int)threadIdx.x;  // reversed: high digits first
+  int mine = 0;
+  for (int k = 0; k < per; ++k) mine += (int)bins[rt * per + k];
+  int tot;
+  const int higher = block_exclusive_scan<NT>(mine, &tot);  // keys in higher digit bins
+  if (higher < rank && rank <= higher + mine) {
+    int cum = higher;
+    for (int k = per - 1; k >= 0; --k) {
+      const int c = (int)bins[rt * per + k];
+      if (cum + c >= rank) {
+        s_digit = rt * per + k;
+        s_cum = cum;
+        break;
+      }
+      cum += c;
+    }
+  }
+  __syncthreads();
+  digit = s_digit;
+  cum_out = s_cum;
+  __syncthreads();
+}
+
 // Walk the finished histogram passes of head h and return the prefix of the
 // k-th largest candidate key, the number of candidates above that prefix's
 // range, and the rank still to find inside it. Block-wide; every thread
 // returns the same values.
 __device__ void radix_state(const EvictParams& p, int h, int passes, uint32_t& prefix, int& above, int& rank) {
-  __shared__ int s_digit, s_cum;
   prefix = 0;
   above = 0;
   rank = (int)p.kprime;
   for (int pass = 0; pass < passes; ++pass) {
-    const uint32_t* bins = p.hist + ((int64_t)pass * p.Hkv + h) * NBINS;
-    const int nbins = pass == 2 ? 1024 : 2048;
-    const int per = nbins / EV_THREADS;  // 8 or 4 bins per thread
-    const int rt = EV_THREADS - 1 - (int)threadIdx.x;  // reversed: high digits first
-    int mine = 0;
-    for (int k = 0; k < per; ++k) mine += (int)bins[rt * per + k];
-    int tot;
-    const int higher = block_exclusive_scan(mine, &tot);  // keys in higher digit bins
-    if (higher < rank && rank <= higher + mine) {
-      int cum = higher;
-      for (int k = per - 1; k >= 0; --k) {
-        const int c = (int)bins[rt * per + k];
-        if (cum + c >= rank) {
-          s_digit = rt * per + k;
-          s_cum = cum;
-          break;
-        }
-        cum += c;
-      }
+    int digit, cum;
+    find_digit(p.hist + ((int64_t)pass * p.Hkv + h) * NBINS, pass, rank, digit, cum);
+    prefix |= (uint32_t)digit << digit_shift(pass);
+    above += cum;
+    rank -= cum;
+  }
+}
+
+// Per-head top-k when a head has at most SEL_MAX candidates: one workgroup
+// of SEL_THREADS per head keeps the candidates' order keys in LDS and runs
+// the three radix-digit passes on an LDS histogram, then stores the k-th key
+// T and the tie quota in the head's state, as the histogram kernels and the
+// count pass would (one launch instead of four).
+constexpr int SEL_MAX = 16384;
+constexpr int SEL_THREADS = 1024;
+constexpr int SEL_UNROLL = 4;  // global loads in flight per thread
+
+__global__ __launch_bounds__(SEL_THREADS) void evict_select_small(EvictParams p) {
+  __shared__ uint32_t s_key[SEL_MAX];
+  __shared__ uint32_t s_hist[NBINS];
+  const int h = blockIdx.x;
+  const int n = (int)p.n_cand;
+  const float* sc = p.scores + (int64_t)h * p.s_hs;
+  for (int i0 = threadIdx.x; i0 < n; i0 += SEL_THREADS * SEL_UNROLL) {
+    float v[SEL_UNROLL];
+#pragma unroll
+    for (int u = 0; u < SEL_UNROLL; ++u) {
+      const int i = i0 + u * SEL_THREADS;
+      v[u] = i < n ? sc[i] : 0.f;
+    }
+#pragma unroll
+    for (int u = 0; u < SEL_UNROLL; ++u) {
+      const int i = i0 + u * SEL_THREADS;
+      if (i < n) s_key[i] = order_key(v[u]);
+    }
+  }
+  uint32_t prefix = 0;
+  int above = 0, rank = (int)p.kprime;
+  for (int pass = 0; pass < 3; ++pass) {
+    for (int i = threadIdx.x; i < NBINS; i += SEL_THREADS) s_hist[i] = 0u;
+    __syncthreads();  // (pass 0: also the key stores)
+    const int hs = pass > 0 ? digit_shift(pass - 1) : 32;
+    for (int i = threadIdx.x; i < n; i += SEL_THREADS) {
+      const uint32_t u = s_key[i];
+      if (pass == 0 || (u >> hs) == (prefix >> hs))
+        atomicAdd(&s_hist[(u >> digit_shift(pass)) & digit_mask(pass)], 1u);
     }
     __syncthreads();
-    prefix |= (uint32_t)s_digit << digit_shift(pass);
-    above += s_cum;
-    rank -= s_cum;
-    __syncthreads();
+    int digit, cum;
+    find_digit<SEL_THREADS>(s_hist, pass, rank, digit, cum);
+    prefix |= (uint32_t)digit << digit_shift(pass);
+    above += cum;
+    rank -= cum;
+  }
+  if (threadIdx.x == 0) {
+    p.state[h * 4 + 0] = (int32_t)prefix;
+    p.state[h * 4 + 1] = (int)p.kprime - above;
   }
 }
 
@@ -182,16 +250,20 @@ __global__ __launch_bounds__(EV_THREADS) void evict_count(EvictParams p) {
   const int h = blockIdx.y, b = blockIdx.x;
   uint32_t T = 0;
   int quota = 0;
-  if (p.mode == MODE_TOPK) {
-    uint32_t prefix;
-    int above, rank;
-    radix_state(p, p.layer ? 0 : h, 3, prefix, above, rank);
-    T = prefix;
-    quota = (int)p.kprime - above;  // ties kept: per head, or for the layer (split by evict_scan)
-  }
-  if (b == 0 && threadIdx.x == 0) {
-    p.state[h * 4 + 0] = (int32_t)T;
-    p.state[h * 4 + 1] = quota;
+  if (p.mode == MODE_TOPK && p.small_sel) {
+    T = (uint32_t)p.state[h * 4 + 0];  // from evict_select_small
+  } else {
+    if (p.mode == MODE_TOPK) {
+      uint32_t prefix;
+      int above, rank;
+      radix_state(p, p.layer ? 0 : h, 3, prefix, above, rank);
+      T = prefix;
+      quota = (int)p.kprime - above;  // ties kept: per head, or for the layer (split by evict_scan)
+    }
+    if (b == 0 && threadIdx.x == 0) {
+      p.state[h * 4 + 0] = (int32_t)T;
+      p.state[h * 4 + 1] = quota;
+    }
   }
   const int64_t i0 = (int64_t)b * EPB + threadIdx.x * EV_PER_THREAD;
   const float* sc = p.scores + (int64_t)h * p.s_hs;
@@ -500,10 +572,15 @@ hipError_t launch_evict(const kvs_evict_desc& e, const float* scores, const uint
   const dim3 grid(p.nb > 0 ? p.nb : 1, p.Hkv);
   hipError_t err;
   if (p.mode == MODE_TOPK) {
-    hipLaunchKernelGGL(evict_zero, dim3(64), dim3(256), 0, s, p.hist, (int64_t)3 * p.Hkv * NBINS);
-    hipLaunchKernelGGL(evict_hist<0>, grid, dim3(EV_THREADS), 0, s, p);
-    hipLaunchKernelGGL(evict_hist<1>, grid, dim3(EV_THREADS), 0, s, p);
-    hipLaunchKernelGGL(evict_hist<2>, grid, dim3(EV_THREADS), 0, s, p);
+    p.small_sel = !p.layer && p.n_cand <= SEL_MAX;
+    if (p.small_sel) {
+      hipLaunchKernelGGL(evict_select_small, dim3(p.Hkv), dim3(SEL_THREADS), 0, s, p);
+    } else {
+      hipLaunchKernelGGL(evict_zero, dim3(64), dim3(256), 0, s, p.hist, (int64_t)3 * p.Hkv * NBINS);
+      hipLaunchKernelGGL(evict_hist<0>, grid, dim3(EV_THREADS), 0, s, p);
+      hipLaunchKernelGGL(evict_hist<1>, grid, dim3(EV_THREADS), 0, s, p);
+      hipLaunchKernelGGL(evict_hist<2>, grid, dim3(EV_THREADS), 0, s, p);
+    }
   }
   if (p.nb > 0) hipLaunchKernelGGL(evict_count, grid, dim3(EV_THREADS), 0, s, p);
   if ((err = hipGetLastError()) != hipSuccess) return err;

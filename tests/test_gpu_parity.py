@@ -245,6 +245,11 @@ EVICT_CASES = [
     ("many-heads-topk", 4097, 100, 64, 10, 30, None),
     ("many-heads-tau", 300, 700, 64, 16, None, float(np.exp(-6.0))),
     ("long-heads-topk", 2, 140000, 64, 128, 35000, None),
+    # per-head top-k is selected in one workgroup's LDS up to 16384 candidates
+    # per head, through the grid histograms above that
+    ("topk-lds-select-largest", 3, 16384 + 64, 128, 64, 4000, None),
+    ("topk-grid-select-smallest", 3, 16385 + 64, 64, 64, 4000, None),
+    ("topk-lds-select-top1", 2, 16384, 128, 0, 1, None),
     ("long-heads-tau", 2, 140000, 64, 128, None, float(np.exp(-6.0))),
 ]
 
