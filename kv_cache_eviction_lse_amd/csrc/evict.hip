@@ -9,8 +9,8 @@
 //
 // Kernels (one grid of blocks of EPB keys per head, unless noted):
 //   top-k with at most SEL_MAX candidates per head (per-head budget):
-//     evict_select_small, one workgroup per head, does the three passes below
-//     on an LDS histogram and leaves T and the quota in the head's state.
+//     evict_select_small, one workgroup per head, does the three passes and
+//     the count pass below from LDS (T, the quota and the block counts).
 //   other top-k: evict_zero, then three radix-digit histogram passes over the
 //     order-preserving 32-bit keys of the candidate scores (bits 31..21,
 //     20..10, 9..0). Each pass re-derives, from the previous passes'
@@ -57,7 +57,6 @@ struct EvictParams {
   int64_t n, n_cand, kprime;  // kprime: per head, or for the whole layer when layer != 0
   int Hkv, D, nb, mode;
   int layer;  // top-k over all heads' candidates together (one histogram, one quota)
-  int small_sel;  // top-k found by evict_select_small (T and quota already in state)
   float tau;
 };
 
@@ -150,8 +149,9 @@ __device__ void radix_state(const EvictParams& p, int h, int passes, uint32_t& p
 // Per-head top-k when a head has at most SEL_MAX candidates: one workgroup
 // of SEL_THREADS per head keeps the candidates' order keys in LDS and runs
 // the three radix-digit passes on an LDS histogram, then stores the k-th key
-// T and the tie quota in the head's state, as the histogram kernels and the
-// count pass would (one launch instead of four).
+// T and the tie quota in the head's state and the kept / tied counts of each
+// of the head's key blocks, as the histogram kernels and the count pass
+// would (one launch instead of five).
 constexpr int SEL_MAX = 16384;
 constexpr int SEL_THREADS = 1024;
 constexpr int SEL_UNROLL = 4;  // global loads in flight per thread
@@ -196,6 +196,33 @@ __global__ __launch_bounds__(SEL_THREADS) void evict_select_small(EvictParams p)
   if (threadIdx.x == 0) {
     p.state[h * 4 + 0] = (int32_t)prefix;
     p.state[h * 4 + 1] = (int)p.kprime - above;
+  }
+  // Count pass: candidates above T (kept for sure) and at T (tied) per key
+  // block. One sweep of SEL_THREADS keys lies inside one block (EPB is a
+  // multiple of SEL_THREADS), so each wave adds its ballot counts once per
+  // sweep; window keys are all kept and are added per block from the ranges.
+  static_assert(EPB % SEL_THREADS == 0, "a sweep must lie inside one key block");
+  __shared__ int s_cnt[SEL_MAX / EPB][2];
+  if (threadIdx.x < 2 * (SEL_MAX / EPB)) (&s_cnt[0][0])[threadIdx.x] = 0;
+  __syncthreads();
+  for (int i0 = 0; i0 < n; i0 += SEL_THREADS) {
+    const int i = i0 + (int)threadIdx.x;
+    const uint32_t u = i < n ? s_key[i] : 0u;
+    const uint64_t above_t = __ballot(i < n && u > prefix);
+    const uint64_t at_t = __ballot(i < n && u == prefix);
+    if ((threadIdx.x & (WAVE - 1)) == 0) {
+      atomicAdd(&s_cnt[i0 / EPB][0], (int)__popcll(above_t));
+      atomicAdd(&s_cnt[i0 / EPB][1], (int)__popcll(at_t));
+    }
+  }
+  __syncthreads();
+  for (int b = threadIdx.x; b < p.nb; b += SEL_THREADS) {
+    const int64_t lo = max((int64_t)b * EPB, p.n_cand), hi = min((int64_t)(b + 1) * EPB, p.n);
+    const int in_window = hi > lo ? (int)(hi - lo) : 0;
+    const bool has_cand = (int64_t)b * EPB < p.n_cand;
+    int32_t* e = p.blk + ((int64_t)h * p.nb + b) * 4;
+    e[0] = (has_cand ? s_cnt[b][0] : 0) + in_window;
+    e[1] = has_cand ? s_cnt[b][1] : 0;
   }
 }
 
@@ -250,20 +277,16 @@ __global__ __launch_bounds__(EV_THREADS) void evict_count(EvictParams p) {
   const int h = blockIdx.y, b = blockIdx.x;
   uint32_t T = 0;
   int quota = 0;
-  if (p.mode == MODE_TOPK && p.small_sel) {
-    T = (uint32_t)p.state[h * 4 + 0];  // from evict_select_small
-  } else {
-    if (p.mode == MODE_TOPK) {
-      uint32_t prefix;
-      int above, rank;
-      radix_state(p, p.layer ? 0 : h, 3, prefix, above, rank);
-      T = prefix;
-      quota = (int)p.kprime - above;  // ties kept: per head, or for the layer (split by evict_scan)
-    }
-    if (b == 0 && threadIdx.x == 0) {
-      p.state[h * 4 + 0] = (int32_t)T;
-      p.state[h * 4 + 1] = quota;
-    }
+  if (p.mode == MODE_TOPK) {
+    uint32_t prefix;
+    int above, rank;
+    radix_state(p, p.layer ? 0 : h, 3, prefix, above, rank);
+    T = prefix;
+    quota = (int)p.kprime - above;  // ties kept: per head, or for the layer (split by evict_scan)
+  }
+  if (b == 0 && threadIdx.x == 0) {
+    p.state[h * 4 + 0] = (int32_t)T;
+    p.state[h * 4 + 1] = quota;
   }
   const int64_t i0 = (int64_t)b * EPB + threadIdx.x * EV_PER_THREAD;
   const float* sc = p.scores + (int64_t)h * p.s_hs;
@@ -571,18 +594,18 @@ hipError_t launch_evict(const kvs_evict_desc& e, const float* scores, const uint
 
   const dim3 grid(p.nb > 0 ? p.nb : 1, p.Hkv);
   hipError_t err;
-  if (p.mode == MODE_TOPK) {
-    p.small_sel = !p.layer && p.n_cand <= SEL_MAX;
-    if (p.small_sel) {
-      hipLaunchKernelGGL(evict_select_small, dim3(p.Hkv), dim3(SEL_THREADS), 0, s, p);
-    } else {
+  const bool small_sel = p.mode == MODE_TOPK && !p.layer && p.n_cand <= SEL_MAX;
+  if (small_sel) {
+    hipLaunchKernelGGL(evict_select_small, dim3(p.Hkv), dim3(SEL_THREADS), 0, s, p);
+  } else {
+    if (p.mode == MODE_TOPK) {
       hipLaunchKernelGGL(evict_zero, dim3(64), dim3(256), 0, s, p.hist, (int64_t)3 * p.Hkv * NBINS);
       hipLaunchKernelGGL(evict_hist<0>, grid, dim3(EV_THREADS), 0, s, p);
       hipLaunchKernelGGL(evict_hist<1>, grid, dim3(EV_THREADS), 0, s, p);
       hipLaunchKernelGGL(evict_hist<2>, grid, dim3(EV_THREADS), 0, s, p);
     }
+    if (p.nb > 0) hipLaunchKernelGGL(evict_count, grid, dim3(EV_THREADS), 0, s, p);
   }
-  if (p.nb > 0) hipLaunchKernelGGL(evict_count, grid, dim3(EV_THREADS), 0, s, p);
   if ((err = hipGetLastError()) != hipSuccess) return err;
   const bool fused = p.Hkv <= FUSED_HEADS && (int64_t)p.Hkv * p.nb <= FUSED_ENTRIES;
   const dim3 wgrid = p.nb > 0 ? grid : dim3(1, 1);  // no keys: one block writes the (zero) offsets

@@ -250,6 +250,10 @@ EVICT_CASES = [
     ("topk-lds-select-largest", 3, 16384 + 64, 128, 64, 4000, None),
     ("topk-grid-select-smallest", 3, 16385 + 64, 64, 64, 4000, None),
     ("topk-lds-select-top1", 2, 16384, 128, 0, 1, None),
+    # the LDS selection also counts each key block: window keys spanning
+    # whole blocks, and candidates ending on a block edge
+    ("topk-lds-select-wide-window", 2, 10000, 64, 9000, 300, None),
+    ("topk-lds-select-block-edge", 2, 4096 + 100, 128, 100, 1000, None),
     ("long-heads-tau", 2, 140000, 64, 128, None, float(np.exp(-6.0))),
 ]
 
