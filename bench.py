@@ -122,7 +122,7 @@ def main():
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the scoring path shards by KV head "
-              "with no communication, and multi-GPU runs are not part of this build.", file=sys.stderr)
+              "with no communication, and this benchmark measures one GPU.", file=sys.stderr)
         sys.exit(2)
 
     import torch
