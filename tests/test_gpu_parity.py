@@ -254,6 +254,10 @@ EVICT_CASES = [
     # whole blocks, and candidates ending on a block edge
     ("topk-lds-select-wide-window", 2, 10000, 64, 9000, 300, None),
     ("topk-lds-select-block-edge", 2, 4096 + 100, 128, 100, 1000, None),
+    # small outputs: several key blocks per head with few kept rows, and
+    # threshold mode on a short layer (its capacity is every token)
+    ("topk-write-copies-rows", 4, 5000, 64, 8, 20, None),
+    ("tau-write-copies-rows", 2, 100, 64, 4, None, float(np.exp(-6.0))),
     ("long-heads-tau", 2, 140000, 64, 128, None, float(np.exp(-6.0))),
 ]
 
