@@ -164,13 +164,15 @@ def _stream(stream):
 
 
 def _bf16(name, t, ndim=3):
+    """dtype and layout of a bf16 operand (the device is checked by _on_gpu,
+    after the shape checks, so that those also run on a host without a GPU)."""
     torch = _torch()
+    if t is None or not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a tensor")
     if t.dtype != torch.bfloat16:
         raise TypeError(f"{name} must be bfloat16, got {t.dtype}")
     if t.dim() != ndim or t.stride(-1) != 1:
         raise ValueError(f"{name} must be [heads, tokens, head_dim] with a contiguous last dimension")
-    if not t.is_cuda:
-        raise ValueError(f"{name} must be a GPU tensor")
     return t
 
 
@@ -178,9 +180,22 @@ def _f32(name, t, shape):
     torch = _torch()
     if t is None:
         return None
-    if t.dtype != torch.float32 or not t.is_contiguous() or tuple(t.shape) != tuple(shape) or not t.is_cuda:
-        raise ValueError(f"{name} must be a contiguous float32 GPU tensor of shape {tuple(shape)}")
+    if t.dtype != torch.float32 or not t.is_contiguous() or tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must be a contiguous float32 tensor of shape {tuple(shape)}")
     return t
+
+
+def _on_gpu(**tensors):
+    """Every given tensor (None skipped) must be on the GPU."""
+    for name, t in tensors.items():
+        if t is not None and not t.is_cuda:
+            raise ValueError(f"{name} must be a GPU tensor")
+
+
+def _check_kself(K, Kself, n_q):
+    """REPEAT self keys: [Hkv, n_q, D] with K's head count and head_dim."""
+    if tuple(Kself.shape) != (K.shape[0], n_q, K.shape[2]):
+        raise ValueError(f"Kself must be [Hkv, n_q, D] = {(K.shape[0], n_q, K.shape[2])}, got {tuple(Kself.shape)}")
 
 
 def attn_desc(Q, K, Kself, scale, mask, chunk) -> AttnDesc:
@@ -188,6 +203,8 @@ def attn_desc(Q, K, Kself, scale, mask, chunk) -> AttnDesc:
     Hkv, n_ctx, Dk = K.shape
     if Dk != D:
         raise ValueError("Q and K head_dim differ")
+    if Kself is not None:
+        _check_kself(K, Kself, n_q)
     d = AttnDesc()
     d.n_qheads, d.n_kvheads, d.head_dim = Hq, Hkv, D
     d.mask = MASK_REPEAT if mask == "repeat" else MASK_CAUSAL
@@ -214,6 +231,7 @@ def lse(Q, K, Kself=None, *, scale: float, mask: str = "repeat", chunk: int = 0,
     if out is None:
         out = torch.empty((d.n_qheads, d.n_q), dtype=torch.float32, device=Q.device)
     _f32("out", out, (d.n_qheads, d.n_q))
+    _on_gpu(Q=Q, K=K, Kself=Kself, out=out)
     check(lib().kvscore_lse(ctypes.byref(d), _ptr(Q), _ptr(K), _ptr(Kself), _ptr(out), _stream(stream)))
     return out
 
@@ -239,6 +257,7 @@ def attention(Q, K, V, Kself=None, Vself=None, *, scale: float, mask: str = "rep
     if lse_out is None:
         lse_out = torch.empty((d.n_qheads, d.n_q), dtype=torch.float32, device=Q.device)
     _f32("lse_out", lse_out, (d.n_qheads, d.n_q))
+    _on_gpu(Q=Q, K=K, V=V, Kself=Kself, Vself=Vself, out=out, lse_out=lse_out)
     check(lib().kvscore_attention(ctypes.byref(d), _ptr(Q), _ptr(K), _ptr(Kself), _ptr(V), _ptr(Vself),
                                   _ptr(out), _ptr(lse_out), _stream(stream)))
     return out, lse_out
@@ -249,8 +268,8 @@ def value_norms(V, W_O, *, out=None, stream=None):
     V bf16 [Hkv, n, D]; W_O bf16 [d_model, Hkv * D] with a contiguous last dimension."""
     torch = _torch()
     _bf16("V", V)
-    if W_O.dtype != torch.bfloat16 or W_O.dim() != 2 or W_O.stride(-1) != 1 or not W_O.is_cuda:
-        raise ValueError("W_O must be a bfloat16 GPU matrix [d_model, Hkv * D] with a contiguous last dimension")
+    if W_O.dtype != torch.bfloat16 or W_O.dim() != 2 or W_O.stride(-1) != 1:
+        raise ValueError("W_O must be a bfloat16 matrix [d_model, Hkv * D] with a contiguous last dimension")
     Hkv, n, D = V.shape
     if W_O.shape[1] != Hkv * D:
         raise ValueError("W_O must have Hkv * D columns")
@@ -260,6 +279,7 @@ def value_norms(V, W_O, *, out=None, stream=None):
     if out is None:
         out = torch.empty((Hkv, n), dtype=torch.float32, device=V.device)
     _f32("out", out, (Hkv, n))
+    _on_gpu(V=V, W_O=W_O, out=out)
     check(lib().kvscore_vnorm(ctypes.byref(d), _ptr(V), _ptr(W_O), _ptr(out), _stream(stream)))
     return out
 
@@ -289,12 +309,12 @@ def decode(Q, K_cache, V_cache, head_offsets, *, scale: float, workspace=None, o
     torch = _torch()
     _bf16("Q", Q)
     for name, t in (("K_cache", K_cache), ("V_cache", V_cache)):
-        if t.dtype != torch.bfloat16 or t.dim() != 2 or not t.is_contiguous() or not t.is_cuda:
-            raise ValueError(f"{name} must be a contiguous bfloat16 GPU matrix [capacity, D]")
+        if t.dtype != torch.bfloat16 or t.dim() != 2 or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous bfloat16 matrix [capacity, D]")
     if K_cache.shape != V_cache.shape or K_cache.shape[1] != Q.shape[2]:
         raise ValueError("K_cache and V_cache must be [capacity, D] with Q's D")
-    if head_offsets.dtype != torch.int64 or head_offsets.dim() != 1 or not head_offsets.is_cuda:
-        raise ValueError("head_offsets must be a GPU int64 vector ([Hkv + 1], or [Hkv] with head_stride_rows)")
+    if head_offsets.dtype != torch.int64 or head_offsets.dim() != 1:
+        raise ValueError("head_offsets must be an int64 vector ([Hkv + 1], or [Hkv] with head_stride_rows)")
     n_kv = head_offsets.numel() - (0 if head_stride_rows else 1)
     d = decode_desc(Q, K_cache, n_kv, scale, head_stride_rows)
     need = decode_workspace_bytes(d)
@@ -308,6 +328,8 @@ def decode(Q, K_cache, V_cache, head_offsets, *, scale: float, workspace=None, o
     if lse_out is None:
         lse_out = torch.empty((d.n_qheads, d.n_q), dtype=torch.float32, device=Q.device)
     _f32("lse_out", lse_out, (d.n_qheads, d.n_q))
+    _on_gpu(Q=Q, K_cache=K_cache, V_cache=V_cache, head_offsets=head_offsets, workspace=workspace, out=out,
+            lse_out=lse_out)
     check(lib().kvscore_decode(ctypes.byref(d), _ptr(Q), _ptr(K_cache), _ptr(V_cache), _ptr(head_offsets),
                                _ptr(out), _ptr(lse_out), _ptr(workspace), workspace.numel(), _stream(stream)))
     return out, lse_out
@@ -327,6 +349,7 @@ def max_scores(Q, K, lse_vals, *, scale: float, vnorm=None, hnorm=None, out=None
             raise ValueError("accumulate needs an existing out tensor")
         out = torch.empty((d.n_kvheads, d.n_ctx), dtype=torch.float32, device=Q.device)
     _f32("out", out, (d.n_kvheads, d.n_ctx))
+    _on_gpu(Q=Q, K=K, lse=lse_vals, vnorm=vnorm, hnorm=hnorm, out=out)
     check(lib().kvscore_max(ctypes.byref(d), _ptr(Q), _ptr(K), _ptr(lse_vals), _ptr(vnorm), _ptr(hnorm),
                             _ptr(out), 1 if accumulate else 0, _stream(stream)))
     return out
@@ -343,6 +366,7 @@ def future_mass(Q, K, lse_vals, *, scale: float, window: int, vnorm=None, hnorm=
     if out is None:
         out = torch.empty((d.n_kvheads, d.n_ctx), dtype=torch.float32, device=Q.device)
     _f32("out", out, (d.n_kvheads, d.n_ctx))
+    _on_gpu(Q=Q, K=K, lse=lse_vals, vnorm=vnorm, hnorm=hnorm, out=out)
     check(lib().kvscore_futuremass(ctypes.byref(d), _ptr(Q), _ptr(K), _ptr(lse_vals), int(window), _ptr(vnorm),
                                    _ptr(hnorm), _ptr(out), _stream(stream)))
     return out
@@ -380,18 +404,22 @@ def evict_workspace_bytes(desc: EvictDesc) -> int:
     return int(lib().kv_evict_workspace_bytes(ctypes.byref(desc)))
 
 
-def evict(scores, K, V, *, window: int, k=None, tau=None, capacity=None, workspace=None, outputs=None,
-          scope: str = "head", stream=None):
-    """Keep the window plus top-k / tau-passing keys per KV head and compact K, V
-    (``kv_evict``); ``scope="layer"`` makes k one budget for all heads together.
-    Returns (kept_idx int32 [capacity], head_offsets int64 [Hkv+1],
-    K_out, V_out bf16 [capacity, D]); rows past head_offsets[-1] are unused."""
+def torch_empty_bytes(n: int, device):
+    return _torch().empty(n, dtype=_torch().uint8, device=device)
+
+
+def _evict_prepare(scores, K, V, window, k, tau, capacity, outputs, scope):
+    """Shared argument checks of evict / evict_noalloc; returns the descriptor
+    and the four output tensors (allocated here when not given)."""
     torch = _torch()
     _bf16("K", K), _bf16("V", V)
     if K.shape != V.shape or K.stride() != V.stride():
         raise ValueError("K and V must have the same shape and strides")
+    Hkv, n, D = K.shape
     if scores.dtype != torch.float32 or scores.dim() != 2 or (scores.numel() and scores.stride(1) != 1):
         raise ValueError("scores must be float32 [Hkv, n] with contiguous rows")
+    if tuple(scores.shape) != (Hkv, n):
+        raise ValueError(f"scores must be [Hkv, n] = {(Hkv, n)}, got {tuple(scores.shape)}")
     e = evict_desc(scores, K, window=window, k=k, tau=tau, capacity=capacity, scope=scope)
     dev = K.device
     if outputs is None:
@@ -401,9 +429,31 @@ def evict(scores, K, V, *, window: int, k=None, tau=None, capacity=None, workspa
         Vo = torch.empty((max(e.capacity, 1), e.head_dim), dtype=torch.bfloat16, device=dev)
     else:
         kept, offs, Ko, Vo = outputs
+        if kept.dtype != torch.int32 or kept.dim() != 1 or not kept.is_contiguous() or kept.numel() < e.capacity:
+            raise ValueError(f"kept_idx must be a contiguous int32 vector of at least {e.capacity} entries")
+        if offs.dtype != torch.int64 or offs.dim() != 1 or not offs.is_contiguous() or offs.numel() < Hkv + 1:
+            raise ValueError(f"head_offsets must be a contiguous int64 vector of at least {Hkv + 1} entries")
+        for name, t in (("K_out", Ko), ("V_out", Vo)):
+            if (t.dtype != torch.bfloat16 or t.dim() != 2 or not t.is_contiguous() or t.shape[1] != D
+                    or t.shape[0] < e.capacity):
+                raise ValueError(f"{name} must be a contiguous bfloat16 [>= {e.capacity}, {D}] matrix")
+    _on_gpu(kept_idx=kept, head_offsets=offs, K_out=Ko, V_out=Vo)
+    return e, (kept, offs, Ko, Vo)
+
+
+def evict(scores, K, V, *, window: int, k=None, tau=None, capacity=None, workspace=None, outputs=None,
+          scope: str = "head", stream=None):
+    """Keep the window plus top-k / tau-passing keys per KV head and compact K, V
+    (``kv_evict``); ``scope="layer"`` makes k one budget for all heads together.
+    Returns (kept_idx int32 [capacity], head_offsets int64 [Hkv+1],
+    K_out, V_out bf16 [capacity, D]); rows past head_offsets[-1] are unused."""
+    e, (kept, offs, Ko, Vo) = _evict_prepare(scores, K, V, window, k, tau, capacity, outputs, scope)
     nbytes = evict_workspace_bytes(e)
     if workspace is None:
-        workspace = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=dev)
+        workspace = torch_empty_bytes(max(nbytes, 256), K.device)
+    if workspace.dtype != _torch().uint8 or workspace.dim() != 1:
+        raise ValueError("workspace must be a uint8 vector")
+    _on_gpu(scores=scores, K=K, V=V, workspace=workspace)
     check(lib().kv_evict(ctypes.byref(e), _ptr(scores), _ptr(K), _ptr(V), _ptr(kept), _ptr(offs), _ptr(Ko),
                          _ptr(Vo), _ptr(workspace), workspace.numel(), _stream(stream)))
     return kept, offs, Ko, Vo
@@ -451,6 +501,7 @@ class StreamCache:
                 or (new_scores.numel() and new_scores.stride(1) != 1):
             raise ValueError("new_scores must be float32 [n_kvheads, n_new] with contiguous rows")
         d = self.desc(new_scores, K_new)
+        _on_gpu(new_scores=new_scores, K_new=K_new, V_new=V_new)
         check(lib().kv_stream_append(ctypes.byref(d), _ptr(new_scores), _ptr(K_new), _ptr(V_new), _ptr(self.K),
                                      _ptr(self.V), _ptr(self.pos), _ptr(self.win_scores), _ptr(self.head_len),
                                      _stream(stream)))

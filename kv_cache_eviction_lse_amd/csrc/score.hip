@@ -409,7 +409,10 @@ hipError_t launch_score_sum(const kvs_attn_desc& d, const uint16_t* Q, const uin
   ScoreParams p{};
   p.Q = Q; p.K = K; p.lse = lse; p.vnorm = vnorm; p.hnorm = hnorm; p.out = target;
   p.q_hs = d.q_head_stride; p.q_ts = d.q_tok_stride; p.k_hs = d.k_head_stride; p.k_ts = d.k_tok_stride;
-  p.n_keys = T; p.n_q = T; p.window = window;
+  // Keys with i + window >= T get 0 whatever the window, so a window past T
+  // is the same as T; clamping keeps key0 + window (the first row a key block
+  // counts) from overflowing for sentinel windows near INT64_MAX.
+  p.n_keys = T; p.n_q = T; p.window = window < T ? window : T;
   p.Hkv = d.n_kvheads; p.G = d.n_qheads / d.n_kvheads; p.scale = d.scale;
   constexpr int BK = SUM_NW * SUM_NT * 32;
   p.n_kblocks = (int)((T + BK - 1) / BK);

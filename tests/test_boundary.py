@@ -389,3 +389,60 @@ def test_last_error_is_per_thread(L):
     for name, (got, expect) in results.items():
         assert all(expect in msg for _, msg in got), name
 
+
+
+# ---------------------------------------------------------------- binding checks
+# Shapes the C ABI cannot see (it gets pointers and a descriptor) are checked
+# by the Python binding before the device is; these run on host tensors.
+
+def _t(shape, dtype):
+    import torch
+
+    return torch.zeros(shape, dtype=dtype)
+
+
+def test_binding_rejects_scores_of_wrong_shape():
+    import torch
+
+    K = _t((2, 100, 128), torch.bfloat16)
+    for bad in ((1, 100), (2, 99), (3, 100)):
+        with pytest.raises(ValueError, match="scores must be"):
+            kvs.evict(_t(bad, torch.float32), K, K, window=8, k=10)
+
+
+def test_binding_rejects_small_or_mistyped_outputs():
+    import torch
+
+    K = _t((2, 100, 128), torch.bfloat16)
+    s = _t((2, 100), torch.float32)
+    cap = 2 * (8 + 10)
+    good = (_t(cap, torch.int32), _t(3, torch.int64), _t((cap, 128), torch.bfloat16), _t((cap, 128), torch.bfloat16))
+    bad_sets = {
+        "kept_idx": (_t(cap - 1, torch.int32),) + good[1:],
+        "head_offsets": (good[0], _t(2, torch.int64)) + good[2:],
+        "K_out": good[:2] + (_t((cap - 1, 128), torch.bfloat16), good[3]),
+        "V_out": good[:3] + (_t((cap, 64), torch.bfloat16),),
+    }
+    for name, outs in bad_sets.items():
+        with pytest.raises(ValueError, match=name):
+            kvs.evict(s, K, K, window=8, k=10, outputs=outs)
+    with pytest.raises(ValueError, match="kept_idx"):
+        kvs.evict(s, K, K, window=8, k=10, outputs=(_t(cap, torch.int64),) + good[1:])
+    # right shapes on the host: the device check is what fails
+    with pytest.raises(ValueError, match="GPU tensor"):
+        kvs.evict(s, K, K, window=8, k=10, outputs=good)
+
+
+def test_binding_rejects_self_keys_of_wrong_shape():
+    import torch
+
+    Q = _t((8, 64, 128), torch.bfloat16)
+    K = _t((2, 300, 128), torch.bfloat16)
+    for bad in ((2, 63, 128), (1, 64, 128), (2, 64, 64)):
+        with pytest.raises(ValueError, match="Kself must be"):
+            kvs.lse(Q, K, _t(bad, torch.bfloat16), scale=0.1, mask="repeat", chunk=64)
+        with pytest.raises(ValueError, match="Kself must be"):
+            kvs.attention(Q, K, K, _t(bad, torch.bfloat16), _t(bad, torch.bfloat16), scale=0.1, mask="repeat",
+                          chunk=64)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        kvs.lse(Q, K, _t((2, 64, 128), torch.bfloat16), scale=0.1, mask="repeat", chunk=64)

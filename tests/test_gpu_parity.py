@@ -203,6 +203,26 @@ def test_future_mass_conserves_mass_at_window_zero():
     assert np.allclose(tot, 4 * 3000, rtol=1e-4)
 
 
+def test_future_mass_sentinel_window_gives_zero():
+    """A window far past T (a sentinel such as 2**62) is the same as T: every
+    key is still inside it, so every target is 0 (and no row before the
+    first is ever read)."""
+    r = synth.Recipe(Hq=8, Hkv=2, D=128, n_ctx=3000, n_q=3000, mask="causal")
+    d = synth.draw(r, 709)
+    Q, K = dev_bf16(d["Q"]), dev_bf16(d["Kctx"])
+    L = kvs.lse(Q, K, None, scale=d["scale"], mask="causal")
+    for w in (2 ** 62, 2 ** 63 - 1, 3000, 2999):
+        say(f"[sum] window {w}")
+        t = kvs.future_mass(Q, K, L, scale=d["scale"], window=w)
+        torch.cuda.synchronize()
+        ht = host(t)
+        if w >= 3000:
+            assert np.all(ht == 0), w
+        else:
+            # only key 0 leaves the window (query 2999 counts it)
+            assert np.all(ht[:, 1:] == 0) and np.all(ht[:, 0] > 0), w
+
+
 def test_future_mass_is_deterministic():
     """Few key blocks: the query rows of each block pair are split in two and
     added atomically; repeated calls must still give identical bits."""
