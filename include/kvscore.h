@@ -26,7 +26,8 @@
  *
  * Conventions shared by every call
  *   - Tensors are device pointers owned by the caller. The library allocates
- *     nothing and keeps no state between calls.
+ *     nothing and keeps no state between calls (kv_evict_noalloc's fixed
+ *     scratch array, see there, only holds the last call's intermediates).
  *   - bf16 tensors are passed as their 16-bit patterns (kvs_bf16). The head
  *     dimension is contiguous; head and token strides are in elements.
  *   - Logit of query j (query head g) and key i: l = scale * q_j . k_i.
@@ -222,6 +223,27 @@ int kv_evict(const kvs_evict_desc* e, const float* scores, const kvs_bf16* K,
              const kvs_bf16* V, int32_t* kept_idx, int64_t* head_offsets,
              kvs_bf16* K_out, kvs_bf16* V_out, void* workspace,
              size_t workspace_bytes, void* stream);
+
+/* Eviction that allocates nothing and takes no workspace argument, for
+ * callers that cannot allocate device memory: code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc. Same descriptor,
+ * inputs, outputs, checks and results as kv_evict (it runs the same
+ * kernels); the workspace kv_evict would take is instead a fixed device
+ * array inside the library, KVS_EVICT_NOALLOC_MAX_WORKSPACE bytes, one copy
+ * per GPU, held until the process ends. A layer whose
+ * kv_evict_workspace_bytes(e) exceeds that returns KVS_EWORKSPACE (nothing
+ * is launched). The first call on a device looks up that device's copy
+ * (no allocation); no call allocates, frees or synchronises.
+ * Every call on one GPU shares that GPU's array: calls ordered on one
+ * stream are safe, but calls that can overlap in time on the same GPU
+ * (different streams, or threads without ordering between them) race on it
+ * and give wrong results. */
+#define KVS_EVICT_NOALLOC_MAX_WORKSPACE ((size_t)4 << 20)
+
+int kv_evict_noalloc(const kvs_evict_desc* e, const float* scores,
+                     const kvs_bf16* K, const kvs_bf16* V, int32_t* kept_idx,
+                     int64_t* head_offsets, kvs_bf16* K_out, kvs_bf16* V_out,
+                     void* stream);
 
 /* Decode attention over the compacted per-head cache (the cache kv_evict
  * writes: KVzap page Algorithm 1 keys[indices], values[indices], head after

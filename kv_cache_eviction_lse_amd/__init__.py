@@ -12,6 +12,7 @@ the C ABI in ``include/kvscore.h``:
 * :func:`max_scores`   -> ``kvscore_max``
 * :func:`future_mass`  -> ``kvscore_futuremass``
 * :func:`evict`        -> ``kv_evict`` (+ ``kv_evict_workspace_bytes``)
+* :func:`evict_noalloc` -> ``kv_evict_noalloc`` (no workspace argument; allocates nothing)
 * :class:`StreamCache` -> ``kv_stream_append`` (threshold pruning as tokens arrive)
 
 Tensors: bf16 ``[heads, tokens, head_dim]`` with a contiguous last dimension
@@ -34,7 +35,8 @@ MASK_REPEAT, MASK_CAUSAL = 0, 1
 
 EXPORTED_SYMBOLS = (
     "kvscore_lse", "kvscore_attention", "kvscore_vnorm", "kvscore_decode_workspace_bytes", "kvscore_decode",
-    "kvscore_max", "kvscore_futuremass", "kv_evict_workspace_bytes", "kv_evict", "kv_stream_append",
+    "kvscore_max", "kvscore_futuremass", "kv_evict_workspace_bytes", "kv_evict", "kv_evict_noalloc",
+    "kv_stream_append",
     "kvs_strerror", "kvs_last_error", "kvs_version",
 )
 
@@ -126,6 +128,7 @@ def lib() -> ctypes.CDLL:
     L.kv_evict_workspace_bytes.argtypes = [pE]
     L.kv_evict_workspace_bytes.restype = ctypes.c_size_t
     L.kv_evict.argtypes = [pE, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
+    L.kv_evict_noalloc.argtypes = [pE, vp, vp, vp, vp, vp, vp, vp, vp]
     L.kv_stream_append.argtypes = [ctypes.POINTER(StreamDesc), vp, vp, vp, vp, vp, vp, vp, vp, vp]
     L.kvs_strerror.argtypes = [i32]
     L.kvs_strerror.restype = ctypes.c_char_p
@@ -133,7 +136,7 @@ def lib() -> ctypes.CDLL:
     L.kvs_last_error.restype = ctypes.c_char_p
     L.kvs_version.restype = c
     for name in ("kvscore_lse", "kvscore_attention", "kvscore_vnorm", "kvscore_decode", "kvscore_max", "kvscore_futuremass", "kv_evict",
-                 "kv_stream_append"):
+                 "kv_evict_noalloc", "kv_stream_append"):
         getattr(L, name).restype = c
     _lib = L
     return L
@@ -456,6 +459,26 @@ def evict(scores, K, V, *, window: int, k=None, tau=None, capacity=None, workspa
     _on_gpu(scores=scores, K=K, V=V, workspace=workspace)
     check(lib().kv_evict(ctypes.byref(e), _ptr(scores), _ptr(K), _ptr(V), _ptr(kept), _ptr(offs), _ptr(Ko),
                          _ptr(Vo), _ptr(workspace), workspace.numel(), _stream(stream)))
+    return kept, offs, Ko, Vo
+
+
+# kv_evict_noalloc's fixed scratch (KVS_EVICT_NOALLOC_MAX_WORKSPACE in the header)
+EVICT_NOALLOC_MAX_WORKSPACE = 4 << 20
+
+
+def evict_noalloc(scores, K, V, *, window: int, outputs, k=None, tau=None, capacity=None, scope: str = "head",
+                  stream=None):
+    """``kv_evict_noalloc``: :func:`evict` without a workspace argument, for
+    callers that cannot allocate device memory. ``outputs`` (kept_idx,
+    head_offsets, K_out, V_out) must be given: nothing is allocated here or
+    in the library. Calls that can overlap in time on one GPU share the
+    library's scratch and race."""
+    if outputs is None:
+        raise ValueError("evict_noalloc allocates nothing: pass outputs=(kept_idx, head_offsets, K_out, V_out)")
+    e, (kept, offs, Ko, Vo) = _evict_prepare(scores, K, V, window, k, tau, capacity, outputs, scope)
+    _on_gpu(scores=scores, K=K, V=V)
+    check(lib().kv_evict_noalloc(ctypes.byref(e), _ptr(scores), _ptr(K), _ptr(V), _ptr(kept), _ptr(offs), _ptr(Ko),
+                                 _ptr(Vo), _stream(stream)))
     return kept, offs, Ko, Vo
 
 

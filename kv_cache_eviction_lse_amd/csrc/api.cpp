@@ -42,8 +42,9 @@ constexpr int MAX_DEVICES = 64;
 DevInfo g_devs[MAX_DEVICES];
 std::mutex g_dev_mu;
 
-// The current device must be a gfx950 GPU. Fills *num_cus.
-int check_device(int* num_cus) {
+// The current device must be a gfx950 GPU. Fills *num_cus (and *dev_out, the
+// current device's index, when given).
+int check_device(int* num_cus, int* dev_out = nullptr) {
   int count = 0;
   if (hipGetDeviceCount(&count) != hipSuccess || count <= 0) {
     (void)hipGetLastError();
@@ -69,6 +70,7 @@ int check_device(int* num_cus) {
   }
   if (!di.usable) return fail(KVS_ENODEV, "device %d is not gfx950", dev);
   *num_cus = di.num_cus;
+  if (dev_out) *dev_out = dev;
   return KVS_OK;
 }
 
@@ -349,9 +351,11 @@ KVS_API size_t kv_evict_workspace_bytes(const kvs_evict_desc* e) {
   return kvs::evict_workspace_bytes(*e);
 }
 
-KVS_API int kv_evict(const kvs_evict_desc* e, const float* scores, const kvs_bf16* K, const kvs_bf16* V,
-                     int32_t* kept_idx, int64_t* head_offsets, kvs_bf16* K_out, kvs_bf16* V_out, void* workspace,
-                     size_t workspace_bytes, void* stream) {
+namespace {
+// Checks of kv_evict and kv_evict_noalloc other than the workspace.
+int check_evict_call(const kvs_evict_desc* e, const float* scores, const kvs_bf16* K, const kvs_bf16* V,
+                     const int32_t* kept_idx, const int64_t* head_offsets, const kvs_bf16* K_out,
+                     const kvs_bf16* V_out) {
   int st = check_evict(e);
   if (st) return st;
   const int64_t w = e->window < e->n_tok ? e->window : e->n_tok;
@@ -372,6 +376,15 @@ KVS_API int kv_evict(const kvs_evict_desc* e, const float* scores, const kvs_bf1
   if (e->n_tok > 0 && (!scores || !K || !V)) return fail(KVS_EINVAL, "an input pointer is NULL");
   if (!aligned16(K) || !aligned16(V) || !aligned16(K_out) || !aligned16(V_out))
     return fail(KVS_EUNSUPPORTED, "K, V, K_out and V_out must be 16-byte aligned");
+  return KVS_OK;
+}
+}  // namespace
+
+KVS_API int kv_evict(const kvs_evict_desc* e, const float* scores, const kvs_bf16* K, const kvs_bf16* V,
+                     int32_t* kept_idx, int64_t* head_offsets, kvs_bf16* K_out, kvs_bf16* V_out, void* workspace,
+                     size_t workspace_bytes, void* stream) {
+  int st = check_evict_call(e, scores, K, V, kept_idx, head_offsets, K_out, V_out);
+  if (st) return st;
   const size_t ws = kvs::evict_workspace_bytes(*e);
   if (!workspace || workspace_bytes < ws)
     return fail(KVS_EWORKSPACE, "workspace of %zu bytes needed, %zu given", ws, workspace ? workspace_bytes : 0);
@@ -382,4 +395,24 @@ KVS_API int kv_evict(const kvs_evict_desc* e, const float* scores, const kvs_bf1
   return hip_status(kvs::launch_evict(*e, scores, K, V, kept_idx, head_offsets, K_out, V_out, workspace,
                                       static_cast<hipStream_t>(stream)),
                     "kv_evict");
+}
+
+KVS_API int kv_evict_noalloc(const kvs_evict_desc* e, const float* scores, const kvs_bf16* K, const kvs_bf16* V,
+                             int32_t* kept_idx, int64_t* head_offsets, kvs_bf16* K_out, kvs_bf16* V_out,
+                             void* stream) {
+  int st = check_evict_call(e, scores, K, V, kept_idx, head_offsets, K_out, V_out);
+  if (st) return st;
+  const size_t ws = kvs::evict_workspace_bytes(*e);
+  static_assert(kvs::EVICT_SCRATCH_BYTES == KVS_EVICT_NOALLOC_MAX_WORKSPACE, "header and library disagree");
+  if (ws > kvs::EVICT_SCRATCH_BYTES)
+    return fail(KVS_EWORKSPACE, "this layer needs %zu bytes of workspace, above the %zu-byte built-in scratch of "
+                "kv_evict_noalloc (use kv_evict with a workspace)", ws, kvs::EVICT_SCRATCH_BYTES);
+  int cus, dev;
+  if ((st = check_device(&cus, &dev))) return st;
+  void* ws_dev = nullptr;  // this device's copy of the library's scratch array
+  st = hip_status(kvs::evict_scratch(dev, &ws_dev), "kv_evict_noalloc: scratch lookup");
+  if (st) return st;
+  return hip_status(kvs::launch_evict(*e, scores, K, V, kept_idx, head_offsets, K_out, V_out, ws_dev,
+                                      static_cast<hipStream_t>(stream)),
+                    "kv_evict_noalloc");
 }

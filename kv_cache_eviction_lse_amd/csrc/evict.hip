@@ -28,6 +28,8 @@
 //     every block instead (no evict_scan launch).
 //   evict_gather (a grid over output rows): coalesced copy of the kept K and
 //     V rows, 16-byte pieces, non-temporal loads and stores.
+#include <mutex>
+
 #include "common.hpp"
 #include "internal.hpp"
 
@@ -551,6 +553,32 @@ WsLayout ws_layout(int Hkv, int nb) {
 }
 
 }  // namespace
+
+// Workspace of kv_evict_noalloc: a fixed device array of this library, one
+// copy per GPU, held until the process ends. In host code `scratch` names a
+// host-side stand-in, never device memory: the device address comes from
+// hipGetSymbolAddress, taken once per device with that device current, and
+// only that address is passed to kernels.
+static __device__ __align__(256) char scratch[EVICT_SCRATCH_BYTES];
+
+namespace {
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[MAX_SCRATCH_DEVICES] = {};
+}  // namespace
+
+hipError_t evict_scratch(int dev, void** ptr) {
+  if (dev < 0 || dev >= MAX_SCRATCH_DEVICES) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    const hipError_t err = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (err != hipSuccess) return err;
+    if (!p) return hipErrorInvalidSymbol;
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return hipSuccess;
+}
 
 size_t evict_workspace_bytes(const kvs_evict_desc& e) {
   const int64_t nb = (e.n_tok + EPB - 1) / EPB;

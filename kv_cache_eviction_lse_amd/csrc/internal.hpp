@@ -36,6 +36,13 @@ hipError_t launch_stream_append(const kvs_stream_desc& d, const float* new_score
 
 size_t evict_workspace_bytes(const kvs_evict_desc& e);
 
+// kv_evict_noalloc's workspace: a device array of EVICT_SCRATCH_BYTES per
+// GPU. evict_scratch() returns its device address on device `dev`, which
+// must be the current device (looked up on the first call per device).
+constexpr size_t EVICT_SCRATCH_BYTES = (size_t)4 << 20;
+constexpr int MAX_SCRATCH_DEVICES = 64;
+hipError_t evict_scratch(int dev, void** ptr);
+
 hipError_t launch_evict(const kvs_evict_desc& e, const float* scores, const uint16_t* K, const uint16_t* V,
                         int32_t* kept_idx, int64_t* head_offsets, uint16_t* K_out, uint16_t* V_out,
                         void* workspace, hipStream_t s);

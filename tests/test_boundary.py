@@ -344,6 +344,26 @@ def test_evict_workspace_checks(L):
     assert L.kv_evict(ctypes.byref(e), FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE, FAKE, ws, None) == kvs.KVS_EINVAL
 
 
+def test_evict_noalloc_rejects(L):
+    """Host checks of kv_evict_noalloc: kv_evict's argument checks, and the
+    layer's workspace must fit the built-in scratch (KVS_EWORKSPACE)."""
+    for kw, code in EVICT_BAD:
+        e = _edesc(**kw)
+        assert L.kv_evict_noalloc(ctypes.byref(e), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None) == code, kw
+    e = _edesc()
+    assert L.kv_evict_noalloc(ctypes.byref(e), FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE, None) == kvs.KVS_EINVAL
+    big = _edesc(n_kvheads=256, capacity=256 * 132, kv_head_stride=1000 * 128)
+    assert L.kv_evict_workspace_bytes(ctypes.byref(big)) > kvs.EVICT_NOALLOC_MAX_WORKSPACE
+    assert L.kv_evict_noalloc(ctypes.byref(big), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None) == kvs.KVS_EWORKSPACE
+    assert "scratch" in L.kvs_last_error().decode()
+
+
+def test_noalloc_limit_matches_header():
+    src = open(HEADER).read()
+    m = re.search(r"#define KVS_EVICT_NOALLOC_MAX_WORKSPACE \(\(size_t\)(\d+) << (\d+)\)", src)
+    assert m and int(m.group(1)) << int(m.group(2)) == kvs.EVICT_NOALLOC_MAX_WORKSPACE
+
+
 @pytest.mark.skipif(not _no_gpu(), reason="valid calls would launch on a GPU host")
 def test_valid_calls_without_gpu_return_enodev(L):
     d = _desc()
@@ -354,6 +374,7 @@ def test_valid_calls_without_gpu_return_enodev(L):
     e = _edesc()
     ws = L.kv_evict_workspace_bytes(ctypes.byref(e))
     assert L.kv_evict(ctypes.byref(e), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, ws, None) == kvs.KVS_ENODEV
+    assert L.kv_evict_noalloc(ctypes.byref(e), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None) == kvs.KVS_ENODEV
     assert L.kv_stream_append(ctypes.byref(_sdesc()), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
                               None) == kvs.KVS_ENODEV
     assert "device" in L.kvs_last_error().decode()
