@@ -7,11 +7,14 @@
 // written in ascending position, head after head (Algorithm 1's keys[indices],
 // values[indices]).
 //
-// Kernels (one grid of blocks of EPB keys per head, unless noted):
-//   top-k with at most SEL_MAX candidates per head (per-head budget):
-//     evict_select_small, one workgroup per head, does the three passes and
-//     the count pass below from LDS (T, the quota and the block counts).
-//   other top-k: evict_zero, then three radix-digit histogram passes over the
+// Kernels:
+//   per-head top-k (or keep-all / window-only) with at most HD_MAX
+//   candidates per head: evict_head, one workgroup per head, selects in LDS
+//   and writes the head's kept indices and offsets itself; then
+//   evict_gather_head copies the rows. Two launches.
+//   Otherwise (thresholds, layer budgets, longer heads), one grid of blocks
+//   of EPB keys per head, unless noted:
+//   top-k: evict_zero, then three radix-digit histogram passes over the
 //     order-preserving 32-bit keys of the candidate scores (bits 31..21,
 //     20..10, 9..0). Each pass re-derives, from the previous passes'
 //     histograms, the prefix of the k-th largest key, so no separate "find"
@@ -60,6 +63,7 @@ struct EvictParams {
   int Hkv, D, nb, mode;
   int layer;  // top-k over all heads' candidates together (one histogram, one quota)
   float tau;
+  int64_t per_head;  // one-workgroup-per-head path: rows per head (known on the host there)
 };
 
 // Order-preserving key: a > b as floats <=> key(a) > key(b); -0 and +0 share
@@ -145,86 +149,6 @@ __device__ void radix_state(const EvictParams& p, int h, int passes, uint32_t& p
     prefix |= (uint32_t)digit << digit_shift(pass);
     above += cum;
     rank -= cum;
-  }
-}
-
-// Per-head top-k when a head has at most SEL_MAX candidates: one workgroup
-// of SEL_THREADS per head keeps the candidates' order keys in LDS and runs
-// the three radix-digit passes on an LDS histogram, then stores the k-th key
-// T and the tie quota in the head's state and the kept / tied counts of each
-// of the head's key blocks, as the histogram kernels and the count pass
-// would (one launch instead of five).
-constexpr int SEL_MAX = 16384;
-constexpr int SEL_THREADS = 1024;
-constexpr int SEL_UNROLL = 4;  // global loads in flight per thread
-
-__global__ __launch_bounds__(SEL_THREADS) void evict_select_small(EvictParams p) {
-  __shared__ uint32_t s_key[SEL_MAX];
-  __shared__ uint32_t s_hist[NBINS];
-  const int h = blockIdx.x;
-  const int n = (int)p.n_cand;
-  const float* sc = p.scores + (int64_t)h * p.s_hs;
-  for (int i0 = threadIdx.x; i0 < n; i0 += SEL_THREADS * SEL_UNROLL) {
-    float v[SEL_UNROLL];
-#pragma unroll
-    for (int u = 0; u < SEL_UNROLL; ++u) {
-      const int i = i0 + u * SEL_THREADS;
-      v[u] = i < n ? sc[i] : 0.f;
-    }
-#pragma unroll
-    for (int u = 0; u < SEL_UNROLL; ++u) {
-      const int i = i0 + u * SEL_THREADS;
-      if (i < n) s_key[i] = order_key(v[u]);
-    }
-  }
-  uint32_t prefix = 0;
-  int above = 0, rank = (int)p.kprime;
-  for (int pass = 0; pass < 3; ++pass) {
-    for (int i = threadIdx.x; i < NBINS; i += SEL_THREADS) s_hist[i] = 0u;
-    __syncthreads();  // (pass 0: also the key stores)
-    const int hs = pass > 0 ? digit_shift(pass - 1) : 32;
-    for (int i = threadIdx.x; i < n; i += SEL_THREADS) {
-      const uint32_t u = s_key[i];
-      if (pass == 0 || (u >> hs) == (prefix >> hs))
-        atomicAdd(&s_hist[(u >> digit_shift(pass)) & digit_mask(pass)], 1u);
-    }
-    __syncthreads();
-    int digit, cum;
-    find_digit<SEL_THREADS>(s_hist, pass, rank, digit, cum);
-    prefix |= (uint32_t)digit << digit_shift(pass);
-    above += cum;
-    rank -= cum;
-  }
-  if (threadIdx.x == 0) {
-    p.state[h * 4 + 0] = (int32_t)prefix;
-    p.state[h * 4 + 1] = (int)p.kprime - above;
-  }
-  // Count pass: candidates above T (kept for sure) and at T (tied) per key
-  // block. One sweep of SEL_THREADS keys lies inside one block (EPB is a
-  // multiple of SEL_THREADS), so each wave adds its ballot counts once per
-  // sweep; window keys are all kept and are added per block from the ranges.
-  static_assert(EPB % SEL_THREADS == 0, "a sweep must lie inside one key block");
-  __shared__ int s_cnt[SEL_MAX / EPB][2];
-  if (threadIdx.x < 2 * (SEL_MAX / EPB)) (&s_cnt[0][0])[threadIdx.x] = 0;
-  __syncthreads();
-  for (int i0 = 0; i0 < n; i0 += SEL_THREADS) {
-    const int i = i0 + (int)threadIdx.x;
-    const uint32_t u = i < n ? s_key[i] : 0u;
-    const uint64_t above_t = __ballot(i < n && u > prefix);
-    const uint64_t at_t = __ballot(i < n && u == prefix);
-    if ((threadIdx.x & (WAVE - 1)) == 0) {
-      atomicAdd(&s_cnt[i0 / EPB][0], (int)__popcll(above_t));
-      atomicAdd(&s_cnt[i0 / EPB][1], (int)__popcll(at_t));
-    }
-  }
-  __syncthreads();
-  for (int b = threadIdx.x; b < p.nb; b += SEL_THREADS) {
-    const int64_t lo = max((int64_t)b * EPB, p.n_cand), hi = min((int64_t)(b + 1) * EPB, p.n);
-    const int in_window = hi > lo ? (int)(hi - lo) : 0;
-    const bool has_cand = (int64_t)b * EPB < p.n_cand;
-    int32_t* e = p.blk + ((int64_t)h * p.nb + b) * 4;
-    e[0] = (has_cand ? s_cnt[b][0] : 0) + in_window;
-    e[1] = has_cand ? s_cnt[b][1] : 0;
   }
 }
 
@@ -538,13 +462,298 @@ __global__ __launch_bounds__(EV_THREADS) void evict_gather(EvictParams p) {
   }
 }
 
+// ---------------------------------------------------------------- one workgroup per head
+// Per-head top-k (and keep-all / window-only) with at most HD_MAX candidates
+// per head: one workgroup of HD_THREADS per head keeps the head's order keys
+// in LDS, radix-selects the k-th key T and the tie quota there, and writes
+// the head's kept positions itself, so only the gather follows (two
+// launches in all). Per-head row counts are known on the host in these
+// modes, so head h's rows start at h * per_head.
+//
+// Radix digits as in the grid path (bits 31..21, 20..10, 9..0). Scores that
+// cluster in a few bins would serialise the histogram's LDS atomics on a
+// few addresses, so each bin has HD_COPIES counters and lane l adds to copy
+// l % HD_COPIES: at most 64 / HD_COPIES lanes of a wave meet on an address.
+// Copies are stored copy-major with a stride of NBINS + 1 words, so the
+// copies of one bin sit in different LDS banks (for the atomics and for the
+// digit search's reads alike).
+//
+// The kept positions are written in ascending order by wave segments: wave
+// w owns the contiguous positions [w * seg, (w + 1) * seg) and walks them
+// 64 at a time, so a ballot is the keep mask of 64 consecutive positions; a
+// count walk and one pass over the 16 waves' totals give each wave its
+// first output row and first tie rank.
+constexpr int HD_THREADS = 1024;
+constexpr int HD_WAVES = HD_THREADS / WAVE;
+constexpr int HD_MAX = 16384;
+constexpr int HD_COPIES = 8;
+constexpr int HD_UNROLL = 16;  // score loads in flight per thread
+constexpr int HD_CSTRIDE = NBINS + 1;  // words between histogram copies
+
+// Number of set bits of m below this lane.
+__device__ __forceinline__ int below(uint64_t m) {
+  return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+}
+
+// The digit (of nbins, counts summed over the copies) holding the rank-th
+// largest key, and the number of keys in higher digits. Every thread sums
+// its nbins / HD_THREADS digits (top digits first in thread order); wave 0
+// scans the HD_THREADS sums and finds the digit. Block-wide; every thread
+// returns the same values, and every read of hist is done when it returns.
+__device__ void hd_find_digit(const uint32_t* hist, int nbins, int rank, int& digit, int& above) {
+  __shared__ int s_part[HD_THREADS];
+  __shared__ int s_digit, s_above;
+  const int tid = threadIdx.x;
+  const int per = nbins / HD_THREADS;  // 2 (2048 bins) or 1 (1024)
+  auto count = [&](int b) {
+    int c = 0;
+#pragma unroll
+    for (int k = 0; k < HD_COPIES; ++k) c += (int)hist[k * HD_CSTRIDE + b];
+    return c;
+  };
+  const int lo = (HD_THREADS - 1 - tid) * per;  // thread 0 holds the top digits
+  int mine = 0;
+  for (int k = 0; k < per; ++k) mine += count(lo + k);
+  s_part[tid] = mine;
+  __syncthreads();
+  if (tid < WAVE) {
+    // lane l owns the sums of threads 16l .. 16l + 15
+    constexpr int PER_LANE = HD_THREADS / WAVE;
+    int v[PER_LANE], run = 0;
+#pragma unroll
+    for (int j = 0; j < PER_LANE; ++j) {
+      v[j] = s_part[tid * PER_LANE + j];
+      run += v[j];
+    }
+    int x = run;  // inclusive scan over lanes
+#pragma unroll
+    for (int o = 1; o < WAVE; o <<= 1) {
+      const int y = __shfl_up(x, o);
+      if (tid >= o) x += y;
+    }
+    int higher = x - run;  // sums of the lanes before this one
+    if (higher < rank && rank <= x) {
+#pragma unroll
+      for (int j = 0; j < PER_LANE; ++j) {
+        if (higher < rank && rank <= higher + v[j]) {
+          // thread t = 16 * lane + j holds digits lo(t) .. lo(t) + per - 1, top first
+          const int t = tid * PER_LANE + j;
+          int cum = higher;
+          for (int k = per - 1; k >= 0; --k) {
+            const int c = count((HD_THREADS - 1 - t) * per + k);
+            if (cum + c >= rank) {
+              s_digit = (HD_THREADS - 1 - t) * per + k;
+              s_above = cum;
+              break;
+            }
+            cum += c;
+          }
+        }
+        higher += v[j];
+      }
+    }
+  }
+  __syncthreads();
+  digit = s_digit;
+  above = s_above;
+}
+
+__global__ __launch_bounds__(HD_THREADS) void evict_head(EvictParams p) {
+  __shared__ uint32_t s_key[HD_MAX];
+  __shared__ __attribute__((aligned(16))) uint32_t s_hist[HD_CSTRIDE * HD_COPIES];
+  __shared__ int s_cnt[HD_WAVES][2];
+  const int h = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int n_cand = (int)p.n_cand;
+  const int copy = lane % HD_COPIES;
+  const float* sc = p.scores + (int64_t)h * p.s_hs;
+
+  uint32_t T = 0;
+  int quota = 0;
+  const bool topk = p.mode == MODE_TOPK;
+  if (topk) {
+    // order keys of the candidates into LDS (HD_UNROLL loads in flight)
+    for (int i0 = tid; i0 < n_cand; i0 += HD_THREADS * HD_UNROLL) {
+      float v[HD_UNROLL];
+#pragma unroll
+      for (int u = 0; u < HD_UNROLL; ++u) {
+        const int i = i0 + u * HD_THREADS;
+        v[u] = i < n_cand ? sc[i] : 0.f;
+      }
+#pragma unroll
+      for (int u = 0; u < HD_UNROLL; ++u) {
+        const int i = i0 + u * HD_THREADS;
+        if (i < n_cand) s_key[i] = order_key(v[u]);
+      }
+    }
+    uint32_t prefix = 0;
+    int rank = (int)p.kprime;
+#pragma unroll 1
+    for (int pass = 0; pass < 3; ++pass) {
+      const int nbins = pass == 2 ? 1024 : 2048;
+      for (int i = tid; i < HD_CSTRIDE * HD_COPIES; i += HD_THREADS) s_hist[i] = 0u;
+      __syncthreads();  // (pass 0: also the key stores)
+      const int hs = pass > 0 ? digit_shift(pass - 1) : 32;
+      const int ds = digit_shift(pass);
+      const uint32_t dm = digit_mask(pass);
+      constexpr int RU = 4;  // LDS reads of a batch issued before its atomics
+      for (int i0 = tid; i0 < n_cand; i0 += HD_THREADS * RU) {
+        uint32_t u[RU];
+#pragma unroll
+        for (int k = 0; k < RU; ++k) {
+          const int i = i0 + k * HD_THREADS;
+          u[k] = i < n_cand ? s_key[i] : 0u;
+        }
+#pragma unroll
+        for (int k = 0; k < RU; ++k) {
+          const int i = i0 + k * HD_THREADS;
+          if (i < n_cand && (pass == 0 || (u[k] >> hs) == (prefix >> hs)))
+            atomicAdd(&s_hist[copy * HD_CSTRIDE + ((u[k] >> ds) & dm)], 1u);
+        }
+      }
+      __syncthreads();
+      int digit, above;
+      hd_find_digit(s_hist, nbins, rank, digit, above);
+      prefix |= (uint32_t)digit << ds;
+      rank -= above;
+    }
+    T = prefix;
+    quota = rank;  // keys equal to T that are kept, lowest positions first
+  } else {
+    __syncthreads();
+  }
+
+  // keep classes: 1 kept, 2 tied at T (top-k), 0 dropped
+  const int seg = ((n_cand + HD_WAVES * WAVE - 1) / (HD_WAVES * WAVE)) * WAVE;
+  const int seg_lo = wave * seg;
+  const int seg_hi = min(seg_lo + seg, n_cand);
+  const bool keep_all = p.mode == MODE_ALL;
+  auto cls_of = [&](int i) -> int {
+    if (i >= seg_hi) return 0;
+    if (!topk) return keep_all ? 1 : 0;
+    const uint32_t u = s_key[i];
+    return u > T ? 1 : (u == T ? 2 : 0);
+  };
+  constexpr int WU = 2;  // 64-position steps of a walk whose reads are issued together
+  int n_keep = 0, n_tie = 0;
+  for (int i0 = seg_lo; i0 < seg_hi; i0 += WAVE * WU) {
+    int c[WU];
+#pragma unroll
+    for (int k = 0; k < WU; ++k) c[k] = cls_of(i0 + k * WAVE + lane);
+#pragma unroll
+    for (int k = 0; k < WU; ++k) {
+      n_keep += __popcll(__ballot(c[k] == 1));
+      n_tie += __popcll(__ballot(c[k] == 2));
+    }
+  }
+  if (lane == 0) {
+    s_cnt[wave][0] = n_keep;
+    s_cnt[wave][1] = n_tie;
+  }
+  __syncthreads();
+  int out_run = 0, tie_run = 0, total = 0, ties_seen = 0;
+  for (int w = 0; w < HD_WAVES; ++w) {
+    const int kw = s_cnt[w][0], tw = s_cnt[w][1];
+    const int take = min(max(quota - ties_seen, 0), tw);
+    if (w < wave) {
+      out_run += kw + take;
+      tie_run += tw;
+    }
+    total += kw + take;
+    ties_seen += tw;
+  }
+  // kept candidate positions, ascending; the window's rows follow them
+  // (writes are capped to the head's rows whatever the counts say)
+  int32_t* out = p.kept_idx + (int64_t)h * p.per_head;
+  const int w_rows = (int)(p.n - p.n_cand);
+  const int cand_rows = (int)p.per_head - w_rows;
+  for (int i0 = seg_lo; i0 < seg_hi; i0 += WAVE * WU) {
+    int c[WU];
+#pragma unroll
+    for (int k = 0; k < WU; ++k) c[k] = cls_of(i0 + k * WAVE + lane);
+#pragma unroll
+    for (int k = 0; k < WU; ++k) {
+      const int i = i0 + k * WAVE + lane;
+      const uint64_t tm = __ballot(c[k] == 2);
+      bool keep = c[k] == 1;
+      if (tm) keep = keep || (c[k] == 2 && tie_run + below(tm) < quota);  // (steps with no tie skip this)
+      const uint64_t km = __ballot(keep);
+      const int o = out_run + below(km);
+      if (keep && o < cand_rows) out[o] = i;
+      out_run += __popcll(km);
+      tie_run += __popcll(tm);
+    }
+  }
+  for (int i = tid; i < w_rows && total + i < (int)p.per_head; i += HD_THREADS) out[total + i] = n_cand + i;
+  if (tid == 0) {
+    p.head_offsets[h] = (int64_t)h * p.per_head;
+    if (h == 0) p.head_offsets[p.Hkv] = (int64_t)p.Hkv * p.per_head;
+  }
+}
+
+// Copy of the kept rows after evict_head (a grid over output rows, GROWS rows
+// per block, as evict_gather): the head of row r is r / per_head, and its
+// position is the kept index evict_head wrote (clamped into the head, which
+// never moves a correct index).
+template <int D>
+__global__ __launch_bounds__(EV_THREADS) void evict_gather_head(EvictParams p, int64_t total) {
+  const int64_t r0 = (int64_t)blockIdx.x * GROWS;
+  if (r0 >= total) return;
+  constexpr int LPR = D / 8;
+  constexpr int RPP = EV_THREADS / LPR;
+  constexpr int PASSES = GROWS / RPP;
+  const int part = threadIdx.x % LPR;
+  const int rr = threadIdx.x / LPR;
+  u32x4 kv[PASSES], vv[PASSES];
+#pragma unroll
+  for (int i = 0; i < PASSES; ++i) {
+    const int64_t r = r0 + i * RPP + rr;
+    if (r < total) {
+      const int h = (int)(r / p.per_head);
+      int64_t pos = p.kept_idx[r];
+      pos = pos < 0 ? 0 : (pos >= p.n ? p.n - 1 : pos);
+      const int64_t src = (int64_t)h * p.kv_hs + pos * p.kv_ts + part * 8;
+      kv[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p.K + src));
+      vv[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p.V + src));
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < PASSES; ++i) {
+    const int64_t r = r0 + i * RPP + rr;
+    if (r < total) {
+      __builtin_nontemporal_store(kv[i], reinterpret_cast<u32x4*>(p.K_out + r * D + part * 8));
+      __builtin_nontemporal_store(vv[i], reinterpret_cast<u32x4*>(p.V_out + r * D + part * 8));
+    }
+  }
+}
+
+// The one-workgroup-per-head path serves per-head top-k budgets (and their
+// keep-all / window-only ends) with at most HD_MAX candidates per head and
+// Hkv * n < 2^31 (row counts fit 32 bits); thresholds, layer budgets and
+// longer heads take the grid path.
+bool use_head_path(const kvs_evict_desc& e) {
+  const int64_t w = e.window < e.n_tok ? e.window : e.n_tok;
+  return e.k >= 0 && e.scope == KVS_SCOPE_HEAD && e.n_tok - w <= HD_MAX &&
+         (int64_t)e.n_kvheads * e.n_tok < ((int64_t)1 << 31);
+}
+
 struct WsLayout {
   size_t hist, blk, state, total;
 };
 
-WsLayout ws_layout(int Hkv, int nb) {
+// Grid path: histograms, block counts, per-head state. The head path uses no
+// workspace (its state lives in LDS; it writes the kept indices directly).
+WsLayout ws_layout(const kvs_evict_desc& e) {
   auto al = [](size_t x) { return (x + 255) & ~(size_t)255; };
-  WsLayout L;
+  WsLayout L{};
+  const int Hkv = e.n_kvheads;
+  if (use_head_path(e)) {
+    L.total = 256;
+    return L;
+  }
+  const int64_t nb = (e.n_tok + EPB - 1) / EPB;
   L.hist = 0;
   L.blk = al((size_t)3 * Hkv * NBINS * 4);
   L.state = L.blk + al((size_t)Hkv * (nb > 0 ? nb : 1) * 16);
@@ -580,10 +789,7 @@ hipError_t evict_scratch(int dev, void** ptr) {
   return hipSuccess;
 }
 
-size_t evict_workspace_bytes(const kvs_evict_desc& e) {
-  const int64_t nb = (e.n_tok + EPB - 1) / EPB;
-  return ws_layout(e.n_kvheads, (int)nb).total;
-}
+size_t evict_workspace_bytes(const kvs_evict_desc& e) { return ws_layout(e).total; }
 
 hipError_t launch_evict(const kvs_evict_desc& e, const float* scores, const uint16_t* K, const uint16_t* V,
                         int32_t* kept_idx, int64_t* head_offsets, uint16_t* K_out, uint16_t* V_out,
@@ -614,26 +820,39 @@ hipError_t launch_evict(const kvs_evict_desc& e, const float* scores, const uint
     p.kprime = e.k < cand ? e.k : cand;
     p.mode = p.kprime == 0 ? MODE_WINDOW : (p.kprime == cand ? MODE_ALL : MODE_TOPK);
   }
-  const WsLayout L = ws_layout(p.Hkv, p.nb);
+  const WsLayout L = ws_layout(e);
   char* ws = static_cast<char*>(workspace);
+
+  if (use_head_path(e)) {
+    const int64_t kc = p.mode == MODE_TOPK ? p.kprime : (p.mode == MODE_ALL ? p.n_cand : 0);
+    p.per_head = kc + (p.n - p.n_cand);
+    hipLaunchKernelGGL(evict_head, dim3(p.Hkv), dim3(HD_THREADS), 0, s, p);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    const int64_t rows = (int64_t)p.Hkv * p.per_head;  // known here in these modes
+    if (rows > 0) {
+      const int64_t gblocks = (rows + GROWS - 1) / GROWS;
+      if (p.D == 128)
+        hipLaunchKernelGGL(evict_gather_head<128>, dim3((unsigned)gblocks), dim3(EV_THREADS), 0, s, p, rows);
+      else
+        hipLaunchKernelGGL(evict_gather_head<64>, dim3((unsigned)gblocks), dim3(EV_THREADS), 0, s, p, rows);
+    }
+    return hipGetLastError();
+  }
+
   p.hist = reinterpret_cast<uint32_t*>(ws + L.hist);
   p.blk = reinterpret_cast<int32_t*>(ws + L.blk);
   p.state = reinterpret_cast<int32_t*>(ws + L.state);
 
   const dim3 grid(p.nb > 0 ? p.nb : 1, p.Hkv);
   hipError_t err;
-  const bool small_sel = p.mode == MODE_TOPK && !p.layer && p.n_cand <= SEL_MAX;
-  if (small_sel) {
-    hipLaunchKernelGGL(evict_select_small, dim3(p.Hkv), dim3(SEL_THREADS), 0, s, p);
-  } else {
-    if (p.mode == MODE_TOPK) {
-      hipLaunchKernelGGL(evict_zero, dim3(64), dim3(256), 0, s, p.hist, (int64_t)3 * p.Hkv * NBINS);
-      hipLaunchKernelGGL(evict_hist<0>, grid, dim3(EV_THREADS), 0, s, p);
-      hipLaunchKernelGGL(evict_hist<1>, grid, dim3(EV_THREADS), 0, s, p);
-      hipLaunchKernelGGL(evict_hist<2>, grid, dim3(EV_THREADS), 0, s, p);
-    }
-    if (p.nb > 0) hipLaunchKernelGGL(evict_count, grid, dim3(EV_THREADS), 0, s, p);
+  if (p.mode == MODE_TOPK) {
+    hipLaunchKernelGGL(evict_zero, dim3(64), dim3(256), 0, s, p.hist, (int64_t)3 * p.Hkv * NBINS);
+    hipLaunchKernelGGL(evict_hist<0>, grid, dim3(EV_THREADS), 0, s, p);
+    hipLaunchKernelGGL(evict_hist<1>, grid, dim3(EV_THREADS), 0, s, p);
+    hipLaunchKernelGGL(evict_hist<2>, grid, dim3(EV_THREADS), 0, s, p);
   }
+  if (p.nb > 0) hipLaunchKernelGGL(evict_count, grid, dim3(EV_THREADS), 0, s, p);
   if ((err = hipGetLastError()) != hipSuccess) return err;
   const bool fused = p.Hkv <= FUSED_HEADS && (int64_t)p.Hkv * p.nb <= FUSED_ENTRIES;
   const dim3 wgrid = p.nb > 0 ? grid : dim3(1, 1);  // no keys: one block writes the (zero) offsets

@@ -352,7 +352,8 @@ def test_evict_noalloc_rejects(L):
         assert L.kv_evict_noalloc(ctypes.byref(e), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None) == code, kw
     e = _edesc()
     assert L.kv_evict_noalloc(ctypes.byref(e), FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE, None) == kvs.KVS_EINVAL
-    big = _edesc(n_kvheads=256, capacity=256 * 132, kv_head_stride=1000 * 128)
+    # (threshold mode takes the grid path, whose histograms need 24 KiB per head)
+    big = _edesc(n_kvheads=300, k=-1, capacity=300 * 1000, kv_head_stride=1000 * 128)
     assert L.kv_evict_workspace_bytes(ctypes.byref(big)) > kvs.EVICT_NOALLOC_MAX_WORKSPACE
     assert L.kv_evict_noalloc(ctypes.byref(big), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None) == kvs.KVS_EWORKSPACE
     assert "scratch" in L.kvs_last_error().decode()

@@ -260,26 +260,77 @@ EVICT_CASES = [
     ("tau-zero", 2, 3000, 64, 8, None, 0.0),
     ("tau-inf", 2, 3000, 128, 8, None, float("inf")),
     ("empty", 2, 0, 128, 8, 5, None),
-    # grid path: more heads than the gather's LDS table, or more keys per head
-    # than one workgroup takes
+    # grid path: thresholds, and per-head top-k above 16384 candidates per
+    # head; at most 16384, one workgroup per head selects in LDS
     ("many-heads-topk", 4097, 100, 64, 10, 30, None),
     ("many-heads-tau", 300, 700, 64, 16, None, float(np.exp(-6.0))),
     ("long-heads-topk", 2, 140000, 64, 128, 35000, None),
-    # per-head top-k is selected in one workgroup's LDS up to 16384 candidates
-    # per head, through the grid histograms above that
-    ("topk-lds-select-largest", 3, 16384 + 64, 128, 64, 4000, None),
-    ("topk-grid-select-smallest", 3, 16385 + 64, 64, 64, 4000, None),
-    ("topk-lds-select-top1", 2, 16384, 128, 0, 1, None),
-    # the LDS selection also counts each key block: window keys spanning
-    # whole blocks, and candidates ending on a block edge
-    ("topk-lds-select-wide-window", 2, 10000, 64, 9000, 300, None),
-    ("topk-lds-select-block-edge", 2, 4096 + 100, 128, 100, 1000, None),
+    ("topk-head-path-largest", 3, 16384 + 64, 128, 64, 4000, None),
+    ("topk-grid-path-smallest", 3, 16385 + 64, 64, 64, 4000, None),
+    ("topk-head-path-top1", 2, 16384, 128, 0, 1, None),
+    ("topk-head-path-k-cand-minus-1", 2, 16384, 64, 0, 16383, None),
+    ("keep-all-head-path", 3, 9000, 64, 16, 20000, None),
+    ("window-only-head-path", 3, 9000, 64, 16, 0, None),
+    # window keys spanning many wave segments, candidates ending on a segment
+    # edge (16 segments of 64 * ceil(n / 1024) positions), one candidate
+    ("topk-head-wide-window", 2, 10000, 64, 9000, 300, None),
+    ("topk-head-segment-edge", 2, 4096 + 100, 128, 100, 1000, None),
+    ("topk-head-one-candidate", 2, 129, 128, 128, 1, None),
     # small outputs: several key blocks per head with few kept rows, and
     # threshold mode on a short layer (its capacity is every token)
     ("topk-write-copies-rows", 4, 5000, 64, 8, 20, None),
     ("tau-write-copies-rows", 2, 100, 64, 4, None, float(np.exp(-6.0))),
     ("long-heads-tau", 2, 140000, 64, 128, None, float(np.exp(-6.0))),
 ]
+
+
+def _tie_heavy_scores(kind, Hkv, n, seed):
+    rng = np.random.default_rng(seed)
+    if kind == "constant":  # every candidate ties: lowest positions win
+        return np.full((Hkv, n), 0.25, dtype=np.float32)
+    if kind == "three-values":  # huge buckets at the k-th key
+        return rng.choice(np.array([0.1, 0.2, 0.3], dtype=np.float32), size=(Hkv, n))
+    if kind == "one-octave":  # every key shares the top 11 bits, many share 16
+        return (0.5 + 0.5 * rng.random((Hkv, n))).astype(np.float32)
+    if kind == "nan-heavy":  # half NaN, NaN ranks below every number
+        s = rng.random((Hkv, n)).astype(np.float32)
+        s[:, ::2] = np.nan
+        return s
+    if kind == "signed":  # negative and positive scores, -0 and +0
+        s = rng.standard_normal((Hkv, n)).astype(np.float32)
+        s[:, ::7] = -0.0
+        s[:, 3::7] = 0.0
+        return s
+    raise ValueError(kind)
+
+
+TIE_CASES = [
+    # kind, Hkv, n, D, window, k (tau for threshold mode)
+    ("constant", 2, 40000, 64, 64, 10000, None),
+    ("constant", 2, 3000, 64, 8, None, 0.25),
+    ("three-values", 3, 50000, 64, 100, 20000, None),
+    ("one-octave", 2, 120000, 64, 128, 30000, None),
+    ("one-octave", 2, 9000, 128, 16, 4000, None),
+    ("nan-heavy", 2, 20000, 64, 32, 15000, None),
+    ("nan-heavy", 2, 20000, 64, 32, None, 0.5),
+    ("signed", 2, 70000, 64, 0, 35000, None),
+    ("signed", 2, 70000, 64, 10, None, -0.0),
+]
+
+
+@pytest.mark.parametrize("kind,Hkv,n,D,window,k,tau", TIE_CASES,
+                         ids=[f"{c[0]}-{'topk' if c[5] is not None else 'tau'}-{c[2]}" for c in TIE_CASES])
+def test_evict_tie_heavy(kind, Hkv, n, D, window, k, tau):
+    """Scores whose k-th key shares its top bits with very many others (the
+    k-th key's 16-bit bucket overflows the LDS stash, or everything ties),
+    NaN-heavy and signed scores: exactly the oracle's selection."""
+    s = _tie_heavy_scores(kind, Hkv, n, 77)
+    K = synth.normal_bf16(78, 90, (Hkv, n, D))
+    V = synth.normal_bf16(78, 91, (Hkv, n, D))
+    say(f"[evict] tie-heavy {kind} Hkv={Hkv} n={n} k={k} tau={tau}")
+    kept, offs, Ko, Vo = kvs.evict(dev_f32(s), dev_bf16(K), dev_bf16(V), window=window, k=k, tau=tau)
+    torch.cuda.synchronize()
+    _check_evict_exact(kind, s, K, V, window, k, tau, kept, offs, Ko, Vo)
 
 
 def _evict_special_scores(s):

@@ -68,13 +68,13 @@ def test_noalloc_equals_evict_on_two_calls(name, first, second, sel):
 
 
 def test_noalloc_rejects_layers_past_its_scratch():
-    Hkv, n = 256, 1000
+    Hkv, n = 300, 1000  # threshold mode: the grid path, 24 KiB of histograms per head
     s = torch.zeros((Hkv, n), dtype=torch.float32, device="cuda")
     K = torch.zeros((Hkv, n, 64), dtype=torch.bfloat16, device="cuda")
-    e = kvs.evict_desc(s, K, window=8, k=10)
+    e = kvs.evict_desc(s, K, window=8, tau=0.5)
     assert kvs.evict_workspace_bytes(e) > kvs.EVICT_NOALLOC_MAX_WORKSPACE
     with pytest.raises(kvs.KvsError) as ei:
-        kvs.evict_noalloc(s, K, K, window=8, k=10, outputs=_outs(e))
+        kvs.evict_noalloc(s, K, K, window=8, tau=0.5, outputs=_outs(e))
     assert ei.value.status == kvs.KVS_EWORKSPACE
 
 
