@@ -258,7 +258,9 @@ int check_stream(const kvs_stream_desc* d) {
   if (d->head_dim != 64 && d->head_dim != 128)
     return fail(KVS_EUNSUPPORTED, "head_dim %d is not supported (64 or 128)", d->head_dim);
   if (d->n_seen < 0 || d->n_new < 0 || d->window < 0) return fail(KVS_EINVAL, "negative size");
-  if (d->n_seen + d->n_new > MAX_TOKENS) return fail(KVS_EUNSUPPORTED, "more than 2^30 tokens");
+  // (each bounded before the sum, which then cannot overflow)
+  if (d->n_seen > MAX_TOKENS || d->n_new > MAX_TOKENS || d->n_seen + d->n_new > MAX_TOKENS)
+    return fail(KVS_EUNSUPPORTED, "more than 2^30 tokens");
   if (d->window > MAX_TOKENS) return fail(KVS_EUNSUPPORTED, "window above 2^30");
   const int64_t need = d->window > d->n_seen + d->n_new ? d->window : d->n_seen + d->n_new;
   if (d->capacity < need)
