@@ -10,16 +10,20 @@ timed region.
 One step = kvscore_lse (all chunks in one call) + kvscore_max + kv_evict.
 value = context keys scored per second over whole steps (Hkv * n_ctx / step).
 
-Also reported: per-kernel times (HIP events on the launch stream), the score
-pass's TFLOP/s against the bf16 MFMA peak (roofline), the LSE pass's
-TFLOP/s, eviction GB/s against HBM peak, the CPU oracle timed on a
-bounded sample of the same workload, and (under "adjacent", timed after the
-step and not part of it) the attention forward that also returns O, the
-value-norm kernel that produces the vnorm input, decode attention of one
-new token per query head over the cache this step compacted, and eviction
-with one layer-wide top-k budget keeping as many rows as the step did.
+Also reported: per-kernel times (HIP events on the launch stream); the
+roofline of the step's dominant kernel, the LSE pass (TFLOP/s against the
+bf16 MFMA peak, and against a dense bf16 GEMM timed in the same run), with
+its exp2 rate; the score pass's TFLOP/s; eviction GB/s with cold caches
+against HBM peak and against a plain device copy of the same bytes timed in
+the same run; the CPU oracle timed on a bounded sample of the same workload
+and on whole small layers; and (under "adjacent", timed after the step and
+not part of it) the attention forward that also returns O, the value-norm
+kernel that produces the vnorm input, decode attention of one new token per
+query head over the cache this step compacted, and eviction with one
+layer-wide top-k budget keeping as many rows as the step did.
 
     python bench.py [--gpus 1] [--steps 10] [--warmup 3] [--no-cpu-baseline]
+    python bench.py --cpu-configs   # the oracle alone on whole layers (no GPU)
 """
 from __future__ import annotations
 
@@ -37,6 +41,9 @@ sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+# v_exp_f32 issues at half rate: a wave64 instruction takes 8 cycles of a
+# 16-lane SIMD, so 8 exp2 per cycle per SIMD; 256 CUs x 4 SIMDs at 2.4 GHz
+PEAK_EXP2_PER_S = 256 * 4 * 8 * 2.4e9
 METRIC = "keys scored/sec & score-pass TFLOP/s (MFMA util) at 32k ctx; evict GB/s"
 
 
@@ -49,10 +56,11 @@ def source_hash(path: str) -> str:
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
-def stored_traffic(kernel_src: str):
-    """HBM bytes per launch of the score pass from the counter runs kept in
-    profiles/, or None when the kernel source changed since they were taken."""
-    p = os.path.join(ROOT, "profiles", "score_max_qwen3-8b-32k_traffic.json")
+def stored_traffic(kernel_src: str, name: str):
+    """HBM bytes per launch of a kernel from the counter runs kept in
+    profiles/<name>, or None when the kernel source changed since they were
+    taken."""
+    p = os.path.join(ROOT, "profiles", name)
     if not os.path.exists(p):
         return None
     with open(p) as f:
@@ -62,19 +70,59 @@ def stored_traffic(kernel_src: str):
     return t.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(d, wl, n_heads_sample=1, n_chunks_sample=6):
-    """The oracle as it stands on a bounded sample: LSE + max score for one KV
-    head's query heads over `n_chunks_sample` repeat chunks against the whole
-    context, then selection + compaction of the full layer; scaled to the
-    whole workload."""
-    import oracle
-
+def host_cpu():
+    """Cores this process may run on, the BLAS threads numpy uses, and the CPU model."""
+    cores = len(os.sched_getaffinity(0))
     try:
         from threadpoolctl import threadpool_info
 
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        blas = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:  # pragma: no cover
-        threads = os.cpu_count() or 1
+        blas = None
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for ln in f:
+                if ln.startswith("model name"):
+                    model = ln.split(":", 1)[1].strip()
+                    break
+    except OSError:  # pragma: no cover
+        pass
+    return cores, blas, model
+
+
+def oracle_whole_layer(wl):
+    """Wall seconds of the oracle over a whole workload: LSE, the score pass,
+    then the selection and compaction of every keep fraction."""
+    import oracle
+    import synth
+
+    r = wl.recipe
+    d = synth.draw(r, wl.seed)
+    t0 = time.perf_counter()
+    if wl.score_mode == "sum":
+        L = oracle.lse(d["Q"], d["Kctx"], None, d["scale"], "causal", 0)
+        s = oracle.future_mass(d["Q"], d["Kctx"], L, d["scale"], wl.window, r.Hkv, vnorm=d.get("vnorm"),
+                               hnorm=d.get("hnorm"))
+    else:
+        L = oracle.lse(d["Q"], d["Kctx"], d["Kself"], d["scale"], "repeat", r.self_chunk)
+        s = oracle.max_scores(d["Q"], d["Kctx"], L, d["scale"], r.Hkv, vnorm=d.get("vnorm"), hnorm=d.get("hnorm"))
+    sels = [dict(tau=wl.tau)] if wl.tau >= 0 else [dict(k=k) for k in wl.ks()]
+    for sel in sels:
+        kept = oracle.select(s, wl.window, **sel)
+        oracle.compact(d["Kctx"], d["V"], kept)
+    return time.perf_counter() - t0
+
+
+def cpu_baseline(d, wl, n_heads_sample=1, n_chunks_sample=6, whole=()):
+    """The oracle as it stands on a bounded sample: LSE + max score for one KV
+    head's query heads over `n_chunks_sample` repeat chunks against the whole
+    context, then selection + compaction of the full layer; scaled to the
+    whole workload (an extrapolation, labelled as such). Also the oracle's
+    wall time on the whole small layers in `whole`."""
+    import oracle
+
+    cores, blas, model = host_cpu()
     r = wl.recipe
     G, C = r.group, r.chunk
     hs = slice(0, n_heads_sample)
@@ -94,16 +142,37 @@ def cpu_baseline(d, wl, n_heads_sample=1, n_chunks_sample=6):
     oracle.compact(d["Kctx"], d["V"], kept)
     t_evict = time.perf_counter() - t1
     t_full = t_score / frac + t_evict
-    return {
+    out = {
         "value": r.Hkv * r.n_ctx / t_full,
         "unit": "keys/s",
-        "cores": int(threads),
+        "cores": int(blas or cores),
         "kind": "oracle",
-        "sample": (f"{n_heads_sample} KV head ({n_heads_sample * G} query heads) x {n_chunks_sample} of "
-                   f"{r.n_q // C} repeat chunks against the full {r.n_ctx}-key context: LSE + max score "
-                   f"({t_score:.1f} s, scaled x{1 / frac:.0f}); threshold selection + compaction of a whole "
-                   f"layer's seeded scores ({t_evict:.2f} s)"),
+        "sample": (f"extrapolated: {n_heads_sample} KV head ({n_heads_sample * G} query heads) x {n_chunks_sample} "
+                   f"of {r.n_q // C} repeat chunks against the full {r.n_ctx}-key context, LSE + max score "
+                   f"({t_score:.1f} s, scaled x{1 / frac:.1f} = {t_score / frac:.0f} s for the layer); threshold "
+                   f"selection + compaction of a whole layer's seeded scores ({t_evict:.2f} s)"),
+        "host_cores": cores,
+        "blas_threads": blas,
+        "cpu_model": model,
+        "layer_s_extrapolated": t_full,
     }
+    if whole:
+        out["whole_layer_s"] = {w.name: round(oracle_whole_layer(w), 3) for w in whole}
+    return out
+
+
+def cpu_configs(names):
+    """--cpu-configs: the oracle alone on whole layers, one JSON line."""
+    from synth.workloads import BY_NAME
+
+    cores, blas, model = host_cpu()
+    res = {}
+    for n in names:
+        _log(f"[cpu] oracle on the whole {n}")
+        res[n] = round(oracle_whole_layer(BY_NAME[n]), 2)
+        _log(f"[cpu] {n}: {res[n]} s")
+    print(json.dumps({"kind": "oracle", "unit": "s per whole layer", "host_cores": cores, "blas_threads": blas,
+                      "cpu_model": model, "whole_layer_s": res}), flush=True)
 
 
 def main():
@@ -116,10 +185,16 @@ def main():
                     help="skip the kernels timed after the step (attention forward with output)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy (for scaling HBM byte counters)")
+    ap.add_argument("--cpu-configs", nargs="*", default=None,
+                    help="only time the CPU oracle on whole layers (default: the tiny, 2k and KVpop 16k layers)")
     ap.add_argument("--workload", default="qwen3-8b-layer-kvzip+-32k",
                     help="named synthetic layer (synth/workloads.py); the default is the 32k layer the "
                          "headline metric is quoted on")
     args = ap.parse_args()
+    if args.cpu_configs is not None:
+        cpu_configs(args.cpu_configs or ["tiny-kvzip-d64-256", "qwen2.5-1.5b-layer-kvzip+-2k",
+                                         "kvpop-future-mass-causal-16k"])
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the scoring path shards by KV head "
               "with no communication, and this benchmark measures one GPU.", file=sys.stderr)
@@ -226,7 +301,57 @@ def main():
         e1.record(stream)
         torch.cuda.synchronize()
         cold.append(e0.elapsed_time(e1))
-    del flush
+
+    # Measured ceilings in the same run (not part of the step), from the
+    # calibration kernels built beside the library:
+    # * a plain copy of the eviction's byte volume (half read, half written)
+    #   with 16-byte non-temporal accesses, the same cache flush before each
+    #   repetition;
+    # * MFMA chains alone at the LSE pass's occupancy (3 four-wave workgroups
+    #   per CU), and the shader clock under that load.
+    import ctypes
+
+    from kv_cache_eviction_lse_amd import build as kbuild
+
+    cal = ctypes.CDLL(kbuild.CALIB_LIB)
+    cal.kvs_calib_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+    cal.kvs_calib_mfma.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+    sptr = ctypes.c_void_p(stream.cuda_stream)
+    offs_now = outs[1].cpu().numpy()
+    ev_bytes_now = acc.evict_bytes(r.Hkv, r.n_ctx, int(offs_now[-1]), r.D)
+    half = max(ev_bytes_now // 2 // 16 * 16, 16)
+    csrc = torch.empty(half, dtype=torch.uint8, device="cuda").fill_(3)
+    cdst = torch.empty_like(csrc)
+    copy_ms = []
+    for i in range(10):
+        flush.fill_(i & 0xFF)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        assert cal.kvs_calib_copy(ctypes.c_void_p(csrc.data_ptr()), ctypes.c_void_p(cdst.data_ptr()), half, sptr) == 0
+        e1.record(stream)
+        torch.cuda.synchronize()
+        copy_ms.append(e0.elapsed_time(e1))
+    assert torch.equal(csrc[:4096], cdst[:4096])
+    del csrc, cdst, flush
+    n_cus = torch.cuda.get_device_properties(0).multi_processor_count
+    mf_blocks, mf_iters = 3 * n_cus, 2000
+    sink = torch.empty(mf_blocks * 256, dtype=torch.float32, device="cuda")
+    clocks = torch.zeros(2, dtype=torch.int64, device="cuda")
+    mf_ms = []
+    for i in range(6):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        assert cal.kvs_calib_mfma(mf_iters, mf_blocks, ctypes.c_void_p(sink.data_ptr()),
+                                  ctypes.c_void_p(clocks.data_ptr()), sptr) == 0
+        e1.record(stream)
+        torch.cuda.synchronize()
+        if i:  # (the first run warms the clock)
+            mf_ms.append(e0.elapsed_time(e1))
+    cyc, ticks = (int(x) for x in clocks.cpu().tolist())
+    clock_mhz = cyc * 100.0 / ticks if ticks > 0 else None  # real-time counter at 100 MHz
+    mfma_tflops = mf_blocks * 4 * 2 * 8 * mf_iters * 32768 / (float(np.median(mf_ms)) * 1e-3) / 1e12
+    copy_gbs = 2 * half / (float(np.median(copy_ms)) * 1e-3) / 1e9
+    del sink, clocks
 
     # Adjacent kernels, timed after the step (not part of it): the attention
     # forward that returns O with the same LSE.
@@ -340,8 +465,15 @@ def main():
     evict_gbs = ev_bytes / (t_evict * 1e-3) / 1e9
     keys_per_s = r.Hkv * r.n_ctx / (ms_per_step * 1e-3)
 
-    traffic = None if sum_mode or wl is not BY_NAME["qwen3-8b-layer-kvzip+-32k"] else \
-        stored_traffic(os.path.join(ROOT, "kv_cache_eviction_lse_amd", "csrc", "score.hip"))
+    csrc_dir = os.path.join(ROOT, "kv_cache_eviction_lse_amd", "csrc")
+    headline = wl is BY_NAME["qwen3-8b-layer-kvzip+-32k"]
+    lse_traffic = stored_traffic(os.path.join(csrc_dir, "lse.hip"), "lse_qwen3-8b-32k_traffic.json") \
+        if headline else None
+    score_traffic = stored_traffic(os.path.join(csrc_dir, "score.hip"), "score_max_qwen3-8b-32k_traffic.json") \
+        if headline else None
+    lse_pairs = lse_flops / (2 * r.D)
+    cold_ms = float(np.median(cold))
+    cold_gbs = ev_bytes / (cold_ms * 1e-3) / 1e9
     out = {
         "metric": METRIC,
         "value": keys_per_s,
@@ -359,15 +491,29 @@ def main():
                    "n_q": r.n_q, "chunk": r.self_chunk, "mask": r.mask,
                    "selection": ({"tau": wl.tau} if wl.tau >= 0 else {"k": wl.ks()[0]}),
                    "window": wl.window, "parallelism": "single GPU"},
-        "roofline": {"bound": "mfma", "achieved": score_tflops, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": score_tflops / PEAK_BF16_TFLOPS, "traffic": traffic,
-                     "kernel": "score pass (" + ("kvscore_futuremass" if sum_mode else "kvscore_max") + ")"},
+        # the step's dominant kernel: the LSE pass
+        "roofline": {"bound": "mfma", "achieved": lse_tflops, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": lse_tflops / PEAK_BF16_TFLOPS, "traffic": lse_traffic,
+                     "kernel": "LSE pass (kvscore_lse)",
+                     "measured_peak": mfma_tflops, "frac_of_measured": lse_tflops / mfma_tflops},
         "kernels_ms": {"lse": t_lse, "score": t_score, "evict": t_evict},
         "kernels_ms_median": {k: float(np.median(v)) for k, v in per_step.items()},
         "kernels_ms_min": {k: float(np.min(v)) for k, v in per_step.items()},
-        "lse_pass": {"tflops": lse_tflops, "frac_of_bf16_peak": lse_tflops / PEAK_BF16_TFLOPS},
-        "score_pass": {"tflops": score_tflops, "flops": score_flops},
-        "evict": {"gbs": evict_gbs, "frac_of_hbm_peak": evict_gbs / PEAK_HBM_GBS, "bytes": ev_bytes,
+        "lse_pass": {"tflops": lse_tflops, "frac_of_bf16_peak": lse_tflops / PEAK_BF16_TFLOPS, "flops": lse_flops,
+                     "exp2_per_s": lse_pairs / (t_lse * 1e-3),
+                     "exp2_frac_of_peak": lse_pairs / (t_lse * 1e-3) / PEAK_EXP2_PER_S},
+        "score_pass": {"tflops": score_tflops, "flops": score_flops, "frac_of_bf16_peak": score_tflops / PEAK_BF16_TFLOPS,
+                       "frac_of_measured": score_tflops / mfma_tflops, "traffic": score_traffic,
+                       "kernel": "kvscore_futuremass" if sum_mode else "kvscore_max"},
+        "ceilings": {"mfma_bf16_tflops": mfma_tflops, "clock_mhz_under_mfma": clock_mhz,
+                     "copy_gbs_cold": copy_gbs, "copy_bytes": 2 * half,
+                     "kernels": "kvs_calib_mfma (MFMA chains alone, 3 four-wave workgroups per CU), "
+                                "kvs_calib_copy (16-byte non-temporal copy, caches flushed first)"},
+        # HBM fraction from the cold-cache repetitions (scores, K and V pushed out
+        # of L2 and the Infinity Cache first); the in-step (warm) rate beside it
+        "evict": {"gbs": cold_gbs, "frac_of_hbm_peak": cold_gbs / PEAK_HBM_GBS,
+                  "frac_of_copy": cold_gbs / copy_gbs, "bytes": ev_bytes,
+                  "warm_gbs": evict_gbs, "warm_frac_of_hbm_peak": evict_gbs / PEAK_HBM_GBS,
                   "kept_per_head": kept.tolist(),
                   "compression_per_head": [round(acc.compression_ratio(int(x), r.n_ctx), 4) for x in kept],
                   "cold_caches": {"median_ms": float(np.median(cold)), "min_ms": float(np.min(cold)), "reps": len(cold),
@@ -375,7 +521,8 @@ def main():
     }
     if not args.no_cpu_baseline and not sum_mode:
         _log("[bench] timing the CPU oracle on a sample")
-        out["cpu_baseline"] = cpu_baseline(d, wl)
+        out["cpu_baseline"] = cpu_baseline(d, wl, whole=(BY_NAME["tiny-kvzip-d64-256"],
+                                                         BY_NAME["qwen2.5-1.5b-layer-kvzip+-2k"]))
     if not args.no_adjacent:
         attn_tflops = 2 * lse_flops / (t_attn * 1e-3) / 1e12
         adjacent["attention"] = {"entry": "kvscore_attention", "ms": t_attn, "flops": 2 * lse_flops,
