@@ -495,15 +495,36 @@ __device__ __forceinline__ int below(uint64_t m) {
   return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
 }
 
+// Inclusive prefix sum over the 64 lanes of a wave: four DPP row shifts
+// (1, 2, 4, 8 lanes) give the sums within each row of 16 lanes, then the
+// totals of the rows before a lane's row are added from three readlanes.
+__device__ __forceinline__ int wave_incl_scan(int x) {
+  constexpr int ROW_SHR1 = 0x111, ROW_SHR2 = 0x112, ROW_SHR4 = 0x114, ROW_SHR8 = 0x118;
+  x += __builtin_amdgcn_update_dpp(0, x, ROW_SHR1, 0xf, 0xf, false);
+  x += __builtin_amdgcn_update_dpp(0, x, ROW_SHR2, 0xf, 0xf, false);
+  x += __builtin_amdgcn_update_dpp(0, x, ROW_SHR4, 0xf, 0xf, false);
+  x += __builtin_amdgcn_update_dpp(0, x, ROW_SHR8, 0xf, 0xf, false);
+  const int r0 = __builtin_amdgcn_readlane(x, 15);
+  const int r1 = __builtin_amdgcn_readlane(x, 31);
+  const int r2 = __builtin_amdgcn_readlane(x, 47);
+  const int row = (threadIdx.x & 63) >> 4;
+  return x + (row >= 1 ? r0 : 0) + (row >= 2 ? r1 : 0) + (row >= 3 ? r2 : 0);
+}
+
 // The digit (of nbins, counts summed over the copies) holding the rank-th
-// largest key, and the number of keys in higher digits. Every thread sums
-// its nbins / HD_THREADS digits (top digits first in thread order); wave 0
-// scans the HD_THREADS sums and finds the digit. Block-wide; every thread
-// returns the same values, and every read of hist is done when it returns.
+// largest key, and the number of keys in higher digits (1 <= rank <= the
+// keys counted). Thread t holds digits (HD_THREADS - 1 - t) * per ..
+// + per - 1, so thread order is descending digit order; a wave scan plus the
+// 16 wave totals give each thread the keys above its digits, and the one
+// thread whose range holds the rank-th key names the digit. Block-wide;
+// every thread returns the same values, and every read of hist is done
+// before the first barrier inside.
 __device__ void hd_find_digit(const uint32_t* hist, int nbins, int rank, int& digit, int& above) {
-  __shared__ int s_part[HD_THREADS];
+  __shared__ __attribute__((aligned(16))) int s_wsum[HD_WAVES];
   __shared__ int s_digit, s_above;
   const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int per = nbins / HD_THREADS;  // 2 (2048 bins) or 1 (1024)
   auto count = [&](int b) {
     int c = 0;
@@ -511,47 +532,21 @@ __device__ void hd_find_digit(const uint32_t* hist, int nbins, int rank, int& di
     for (int k = 0; k < HD_COPIES; ++k) c += (int)hist[k * HD_CSTRIDE + b];
     return c;
   };
-  const int lo = (HD_THREADS - 1 - tid) * per;  // thread 0 holds the top digits
-  int mine = 0;
-  for (int k = 0; k < per; ++k) mine += count(lo + k);
-  s_part[tid] = mine;
+  const int lo = (HD_THREADS - 1 - tid) * per;
+  const int c_top = count(lo + per - 1);  // the thread's higher digit first
+  const int c_low = per == 2 ? count(lo) : 0;
+  const int mine = c_top + c_low;
+  const int x = wave_incl_scan(mine);
+  if (lane == WAVE - 1) s_wsum[wave] = x;
   __syncthreads();
-  if (tid < WAVE) {
-    // lane l owns the sums of threads 16l .. 16l + 15
-    constexpr int PER_LANE = HD_THREADS / WAVE;
-    int v[PER_LANE], run = 0;
+  int before = 0;
 #pragma unroll
-    for (int j = 0; j < PER_LANE; ++j) {
-      v[j] = s_part[tid * PER_LANE + j];
-      run += v[j];
-    }
-    int x = run;  // inclusive scan over lanes
-#pragma unroll
-    for (int o = 1; o < WAVE; o <<= 1) {
-      const int y = __shfl_up(x, o);
-      if (tid >= o) x += y;
-    }
-    int higher = x - run;  // sums of the lanes before this one
-    if (higher < rank && rank <= x) {
-#pragma unroll
-      for (int j = 0; j < PER_LANE; ++j) {
-        if (higher < rank && rank <= higher + v[j]) {
-          // thread t = 16 * lane + j holds digits lo(t) .. lo(t) + per - 1, top first
-          const int t = tid * PER_LANE + j;
-          int cum = higher;
-          for (int k = per - 1; k >= 0; --k) {
-            const int c = count((HD_THREADS - 1 - t) * per + k);
-            if (cum + c >= rank) {
-              s_digit = (HD_THREADS - 1 - t) * per + k;
-              s_above = cum;
-              break;
-            }
-            cum += c;
-          }
-        }
-        higher += v[j];
-      }
-    }
+  for (int w = 0; w < HD_WAVES; ++w) before += w < wave ? s_wsum[w] : 0;
+  const int incl = before + x, excl = incl - mine;
+  if (excl < rank && rank <= incl) {
+    const bool in_top = rank <= excl + c_top;
+    s_digit = in_top ? lo + per - 1 : lo;
+    s_above = in_top ? excl : excl + c_top;
   }
   __syncthreads();
   digit = s_digit;
