@@ -9,9 +9,9 @@
 //
 // Kernels:
 //   per-head top-k (or keep-all / window-only) with at most HD_MAX
-//   candidates per head: evict_head, one workgroup per head, selects in LDS
-//   and writes the head's kept indices and offsets itself; then
-//   evict_gather_head copies the rows. Two launches.
+//   candidates per head: evict_head, a few workgroups per head, each of
+//   which selects in LDS and then writes and copies its share of the head's
+//   kept rows. One launch.
 //   Otherwise (thresholds, layer budgets, longer heads), one grid of blocks
 //   of EPB keys per head, unless noted:
 //   top-k: evict_zero, then three radix-digit histogram passes over the
@@ -464,11 +464,14 @@ __global__ __launch_bounds__(EV_THREADS) void evict_gather(EvictParams p) {
 
 // ---------------------------------------------------------------- one workgroup per head
 // Per-head top-k (and keep-all / window-only) with at most HD_MAX candidates
-// per head: one workgroup of HD_THREADS per head keeps the head's order keys
-// in LDS, radix-selects the k-th key T and the tie quota there, and writes
-// the head's kept positions itself, so only the gather follows (two
-// launches in all). Per-head row counts are known on the host in these
-// modes, so head h's rows start at h * per_head.
+// per head: `reps` workgroups of HD_THREADS per head each keep the head's
+// order keys in LDS and radix-select the k-th key T and the tie quota there
+// (the same work in every one of them: the head's scores are at most 64 KB,
+// and the copies run side by side on different CUs). Per-head row counts
+// are known on the host in these modes, so head h's rows start at
+// h * per_head; workgroup r of a head owns output rows
+// [per_head * r / reps, per_head * (r + 1) / reps): it writes their kept
+// positions and copies their K and V rows, so no gather launch follows.
 //
 // Radix digits as in the grid path (bits 31..21, 20..10, 9..0). Scores that
 // cluster in a few bins would serialise the histogram's LDS atomics on a
@@ -482,13 +485,19 @@ __global__ __launch_bounds__(EV_THREADS) void evict_gather(EvictParams p) {
 // w owns the contiguous positions [w * seg, (w + 1) * seg) and walks them
 // 64 at a time, so a ballot is the keep mask of 64 consecutive positions; a
 // count walk and one pass over the 16 waves' totals give each wave its
-// first output row and first tie rank.
+// first output row and first tie rank. A workgroup keeps the positions of
+// its own candidate rows in LDS (in the histogram's space, free once T is
+// known) for the copy; its window rows follow from their row numbers.
 constexpr int HD_THREADS = 1024;
 constexpr int HD_WAVES = HD_THREADS / WAVE;
 constexpr int HD_MAX = 16384;
 constexpr int HD_COPIES = 8;
 constexpr int HD_UNROLL = 16;  // score loads in flight per thread
 constexpr int HD_CSTRIDE = NBINS + 1;  // words between histogram copies
+constexpr int HD_ROWS_PER_WG = 128;    // kept rows a workgroup of a head copies (sets the workgroups per head)
+constexpr int HD_MAX_REPS = 64;        // at most this many workgroups per head
+constexpr int HD_CP_PASSES = 4;        // copy passes with loads in flight
+static_assert(HD_CSTRIDE * HD_COPIES >= HD_MAX, "a workgroup's candidate positions live in the histogram's space");
 
 // Number of set bits of m below this lane.
 __device__ __forceinline__ int below(uint64_t m) {
@@ -553,11 +562,13 @@ __device__ void hd_find_digit(const uint32_t* hist, int nbins, int rank, int& di
   above = s_above;
 }
 
-__global__ __launch_bounds__(HD_THREADS) void evict_head(EvictParams p) {
+template <int D>
+__global__ __launch_bounds__(HD_THREADS) void evict_head(EvictParams p, int reps) {
   __shared__ uint32_t s_key[HD_MAX];
   __shared__ __attribute__((aligned(16))) uint32_t s_hist[HD_CSTRIDE * HD_COPIES];
   __shared__ int s_cnt[HD_WAVES][2];
-  const int h = blockIdx.x;
+  const int h = blockIdx.x / reps;
+  const int rep = blockIdx.x % reps;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -659,11 +670,17 @@ __global__ __launch_bounds__(HD_THREADS) void evict_head(EvictParams p) {
     total += kw + take;
     ties_seen += tw;
   }
-  // kept candidate positions, ascending; the window's rows follow them
-  // (writes are capped to the head's rows whatever the counts say)
-  int32_t* out = p.kept_idx + (int64_t)h * p.per_head;
+  // Kept candidate positions, ascending, then the window's rows; this
+  // workgroup writes the rows [o_lo, o_hi) of the head and records its
+  // candidate rows' positions in s_pos (writes are capped to the head's rows
+  // whatever the counts say).
+  const int per_head = (int)p.per_head;
+  int32_t* out = p.kept_idx + (int64_t)h * per_head;
   const int w_rows = (int)(p.n - p.n_cand);
-  const int cand_rows = (int)p.per_head - w_rows;
+  const int cand_rows = per_head - w_rows;
+  const int o_lo = (int)((int64_t)per_head * rep / reps);
+  const int o_hi = (int)((int64_t)per_head * (rep + 1) / reps);
+  uint32_t* s_pos = s_hist;  // the histogram's space, free after the selection (barriers since its last read)
   for (int i0 = seg_lo; i0 < seg_hi; i0 += WAVE * WU) {
     int c[WU];
 #pragma unroll
@@ -676,50 +693,53 @@ __global__ __launch_bounds__(HD_THREADS) void evict_head(EvictParams p) {
       if (tm) keep = keep || (c[k] == 2 && tie_run + below(tm) < quota);  // (steps with no tie skip this)
       const uint64_t km = __ballot(keep);
       const int o = out_run + below(km);
-      if (keep && o < cand_rows) out[o] = i;
+      if (keep && o < cand_rows && o >= o_lo && o < o_hi) {
+        out[o] = i;
+        s_pos[o - o_lo] = (uint32_t)i;
+      }
       out_run += __popcll(km);
       tie_run += __popcll(tm);
     }
   }
-  for (int i = tid; i < w_rows && total + i < (int)p.per_head; i += HD_THREADS) out[total + i] = n_cand + i;
-  if (tid == 0) {
-    p.head_offsets[h] = (int64_t)h * p.per_head;
-    if (h == 0) p.head_offsets[p.Hkv] = (int64_t)p.Hkv * p.per_head;
+  // window row j is row total + j
+  const int win_lo = max(o_lo, total), win_hi = min(o_hi, min(total + w_rows, per_head));
+  for (int o = win_lo + tid; o < win_hi; o += HD_THREADS) out[o] = n_cand + (o - total);
+  if (tid == 0 && rep == 0) {
+    p.head_offsets[h] = (int64_t)h * per_head;
+    if (h == 0) p.head_offsets[p.Hkv] = (int64_t)p.Hkv * per_head;
   }
-}
+  __syncthreads();  // s_pos complete
 
-// Copy of the kept rows after evict_head (a grid over output rows, GROWS rows
-// per block, as evict_gather): the head of row r is r / per_head, and its
-// position is the kept index evict_head wrote (clamped into the head, which
-// never moves a correct index).
-template <int D>
-__global__ __launch_bounds__(EV_THREADS) void evict_gather_head(EvictParams p, int64_t total) {
-  const int64_t r0 = (int64_t)blockIdx.x * GROWS;
-  if (r0 >= total) return;
+  // Copy of the rows [o_lo, o_hi): D / 8 lanes per row, 16-byte pieces,
+  // HD_CP_PASSES passes of loads issued before their stores, non-temporal.
   constexpr int LPR = D / 8;
-  constexpr int RPP = EV_THREADS / LPR;
-  constexpr int PASSES = GROWS / RPP;
-  const int part = threadIdx.x % LPR;
-  const int rr = threadIdx.x / LPR;
-  u32x4 kv[PASSES], vv[PASSES];
+  constexpr int RPP = HD_THREADS / LPR;
+  const int part = tid % LPR;
+  const int rr = tid / LPR;
+  const int cand_end = min(total, cand_rows);  // rows below this hold candidates
+  const int64_t out_row0 = (int64_t)h * per_head;
+  const int64_t head_base = (int64_t)h * p.kv_hs + part * 8;
+  for (int b = o_lo; b < o_hi; b += RPP * HD_CP_PASSES) {
+    u32x4 kv[HD_CP_PASSES], vv[HD_CP_PASSES];
 #pragma unroll
-  for (int i = 0; i < PASSES; ++i) {
-    const int64_t r = r0 + i * RPP + rr;
-    if (r < total) {
-      const int h = (int)(r / p.per_head);
-      int64_t pos = p.kept_idx[r];
-      pos = pos < 0 ? 0 : (pos >= p.n ? p.n - 1 : pos);
-      const int64_t src = (int64_t)h * p.kv_hs + pos * p.kv_ts + part * 8;
-      kv[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p.K + src));
-      vv[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p.V + src));
+    for (int q = 0; q < HD_CP_PASSES; ++q) {
+      const int o = b + q * RPP + rr;
+      if (o < o_hi) {
+        int64_t pos = o < cand_end ? (int64_t)s_pos[o - o_lo] : (int64_t)n_cand + (o - total);
+        pos = pos < 0 ? 0 : (pos >= p.n ? p.n - 1 : pos);
+        const int64_t src = head_base + pos * p.kv_ts;
+        kv[q] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p.K + src));
+        vv[q] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p.V + src));
+      }
     }
-  }
 #pragma unroll
-  for (int i = 0; i < PASSES; ++i) {
-    const int64_t r = r0 + i * RPP + rr;
-    if (r < total) {
-      __builtin_nontemporal_store(kv[i], reinterpret_cast<u32x4*>(p.K_out + r * D + part * 8));
-      __builtin_nontemporal_store(vv[i], reinterpret_cast<u32x4*>(p.V_out + r * D + part * 8));
+    for (int q = 0; q < HD_CP_PASSES; ++q) {
+      const int o = b + q * RPP + rr;
+      if (o < o_hi) {
+        const int64_t dst = (out_row0 + o) * D + part * 8;
+        __builtin_nontemporal_store(kv[q], reinterpret_cast<u32x4*>(p.K_out + dst));
+        __builtin_nontemporal_store(vv[q], reinterpret_cast<u32x4*>(p.V_out + dst));
+      }
     }
   }
 }
@@ -821,17 +841,18 @@ hipError_t launch_evict(const kvs_evict_desc& e, const float* scores, const uint
   if (use_head_path(e)) {
     const int64_t kc = p.mode == MODE_TOPK ? p.kprime : (p.mode == MODE_ALL ? p.n_cand : 0);
     p.per_head = kc + (p.n - p.n_cand);
-    hipLaunchKernelGGL(evict_head, dim3(p.Hkv), dim3(HD_THREADS), 0, s, p);
-    hipError_t err = hipGetLastError();
-    if (err != hipSuccess) return err;
-    const int64_t rows = (int64_t)p.Hkv * p.per_head;  // known here in these modes
-    if (rows > 0) {
-      const int64_t gblocks = (rows + GROWS - 1) / GROWS;
-      if (p.D == 128)
-        hipLaunchKernelGGL(evict_gather_head<128>, dim3((unsigned)gblocks), dim3(EV_THREADS), 0, s, p, rows);
-      else
-        hipLaunchKernelGGL(evict_gather_head<64>, dim3((unsigned)gblocks), dim3(EV_THREADS), 0, s, p, rows);
-    }
+    // workgroups per head: one per HD_ROWS_PER_WG kept rows, at most
+    // HD_MAX_REPS, and no more than fill 512 workgroups over the heads
+    int64_t reps = (p.per_head + HD_ROWS_PER_WG - 1) / HD_ROWS_PER_WG;
+    const int64_t fill = (512 + p.Hkv - 1) / p.Hkv;
+    reps = reps < fill ? reps : fill;
+    reps = reps < HD_MAX_REPS ? reps : HD_MAX_REPS;
+    reps = reps < 1 ? 1 : reps;
+    const int64_t blocks = (int64_t)p.Hkv * reps;  // Hkv * n < 2^31 and reps <= 64
+    if (p.D == 128)
+      hipLaunchKernelGGL(evict_head<128>, dim3((unsigned)blocks), dim3(HD_THREADS), 0, s, p, (int)reps);
+    else
+      hipLaunchKernelGGL(evict_head<64>, dim3((unsigned)blocks), dim3(HD_THREADS), 0, s, p, (int)reps);
     return hipGetLastError();
   }
 
