@@ -276,6 +276,14 @@ EVICT_CASES = [
     ("topk-head-wide-window", 2, 10000, 64, 9000, 300, None),
     ("topk-head-segment-edge", 2, 4096 + 100, 128, 100, 1000, None),
     ("topk-head-one-candidate", 2, 129, 128, 128, 1, None),
+    # the per-head path splits a head's output rows over one workgroup per
+    # 128 rows (at most 64, and at most about 512 workgroups in all): rows
+    # on an exact multiple of 128, one row past it, the cap for many heads
+    # (70 heads: 8 workgroups each), and window rows split over workgroups
+    ("topk-head-rows-256", 2, 1000, 128, 0, 256, None),
+    ("topk-head-rows-257", 2, 1000, 64, 0, 257, None),
+    ("topk-head-70-heads", 70, 3000, 64, 40, 2900, None),
+    ("topk-head-window-split", 1, 2000, 128, 300, 1, None),
     # small outputs: several key blocks per head with few kept rows, and
     # threshold mode on a short layer (its capacity is every token)
     ("topk-write-copies-rows", 4, 5000, 64, 8, 20, None),
@@ -308,6 +316,7 @@ TIE_CASES = [
     # kind, Hkv, n, D, window, k (tau for threshold mode)
     ("constant", 2, 40000, 64, 64, 10000, None),
     ("constant", 2, 3000, 64, 8, None, 0.25),
+    ("constant", 3, 1000, 128, 0, 200, None),  # ties across the 128-row split of the per-head path
     ("three-values", 3, 50000, 64, 100, 20000, None),
     ("one-octave", 2, 120000, 64, 128, 30000, None),
     ("one-octave", 2, 9000, 128, 16, 4000, None),
