@@ -8,9 +8,17 @@
 // the query's chunk up to its position) or CAUSAL.
 //
 // Layout of the work:
-//   * a workgroup has 8 waves, each owning one query subtile (32 positions of
-//     one query head); subtiles are ordered position-major, so the heads of a
-//     GQA group at the same positions share every key and value tile;
+//   * a workgroup has 12 waves (3 per SIMD, one workgroup per CU), each
+//     owning one query subtile (32 positions of one query head); subtiles are
+//     ordered position-major, so the heads of a GQA group at the same
+//     positions share every key and value tile (384 queries per tile);
+//   * key and value tiles of 32 rows go through a 2-stage LDS ring of 4
+//     tiles per stage: one barrier per 128 keys, the next stage's tiles
+//     loaded while this stage's are used. Each tile's loads are issued before
+//     the S of the tile in use and stored after it, so only one tile's loads
+//     sit in registers; the matrix work of one wave overlaps the other
+//     waves' exponentials (no second set of S accumulators, which would not
+//     fit 3 waves per SIMD);
 //   * key tiles of 32 rows go through LDS as the A operand of S = K Q^T (keys
 //     as rows, queries as columns), exactly as in the LSE pass; each lane's
 //     16 accumulators are 16 keys of one query;
@@ -52,8 +60,9 @@ struct AttnParams {
   float scale;
 };
 
-constexpr int AT_WAVES = 8;
-constexpr int NSTAGE = 3;  // LDS ring: tile t's values, tile t+1's keys, tile t+2 being stored
+constexpr int AT_WAVES = 12;
+constexpr int NSTAGE = 2;  // LDS ring stages: the one in use and the one being filled
+constexpr int TPS = 4;     // 32-key tiles per stage
 constexpr int AT_THREADS = AT_WAVES * WAVE;
 constexpr float AT_LAZY = 1048576.0f;  // 2^20: raise the offset when a lane's tile sum exceeds this
 
@@ -68,10 +77,10 @@ struct ATile {
   static constexpr int DB = D / 32;            // output row blocks of O^T
   static constexpr int CHUNKS = 32 * D / 8;    // 16-byte pieces per tile, per tensor
   static constexpr int CPR = D / 8;            // pieces per row
-  static constexpr int KPT = CHUNKS / (AT_THREADS / 2);  // K pieces per K-loading thread
+  static constexpr int KPT = (CHUNKS + AT_THREADS - 1) / AT_THREADS;  // K pieces per thread
   static constexpr int VUNITS = 16 * CPR;      // (key pair, piece) units of a V tile
-  static constexpr int VPT = (VUNITS + AT_THREADS / 2 - 1) / (AT_THREADS / 2);  // per V-loading thread
-  static constexpr int NPRE = KPT > 2 * VPT ? KPT : 2 * VPT;
+  static constexpr int VPT = (VUNITS + AT_THREADS - 1) / AT_THREADS;  // V units per thread
+  static constexpr int NPRE = KPT + 2 * VPT;
 };
 
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
@@ -86,8 +95,7 @@ __device__ __forceinline__ bf16x8 pack_bf16(const f32x16& x, int base) {
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(AT_THREADS, 1) void attn_kernel(AttnParams p) {
   using T = ATile<D>;
-  static_assert(T::CHUNKS % (AT_THREADS / 2) == 0, "K pieces must split evenly over half the workgroup");
-  __shared__ __attribute__((aligned(16))) char s_tile[NSTAGE][T::STAGE];
+  __shared__ __attribute__((aligned(16))) char s_tile[NSTAGE][TPS][T::STAGE];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -133,11 +141,9 @@ __global__ __launch_bounds__(AT_THREADS, 1) void attn_kernel(AttnParams p) {
   const int n_ctx_s = (int)p.n_ctx, pos_end_s = (int)pos_end, self_lo_s = (int)self_lo;
   const int k_ts_s = (int)p.k_ts, ks_ts_s = CAUSAL ? k_ts_s : (int)p.ks_ts;
   const int64_t kh = (int64_t)h * p.k_hs, ksh = CAUSAL ? kh : (int64_t)h * p.ks_hs;
-  // Waves 0..3 load K tiles (CHUNKS / 256 pieces each); waves 4..7 load V
-  // tiles as pairs of adjacent key rows (one 16-byte piece of keys 2m and
-  // 2m+1 per thread), which they store transposed as 32-bit key pairs.
-  const bool k_loader = wave < AT_WAVES / 2;
-  const int lt = tid & (AT_THREADS / 2 - 1);  // thread index within its half of the workgroup
+  // Every thread loads up to KPT 16-byte pieces of the K tile and up to VPT
+  // units of the V tile (one 16-byte piece of keys 2m and 2m+1), which it
+  // stores transposed as 32-bit key pairs.
   u32x4 pre[T::NPRE];
   auto load_tile = [&](int tt) {
     const bool ctx = tt < n_ctx_tiles;
@@ -146,52 +152,43 @@ __global__ __launch_bounds__(AT_THREADS, 1) void attn_kernel(AttnParams p) {
     const int ts = ctx ? k_ts_s : ks_ts_s;
     const int rows = min(kend - k0, 32);
     const int64_t off = (ctx ? kh : ksh) + (int64_t)k0 * ts;
-    if (k_loader) {
-      const __amdgpu_buffer_rsrc_t rk = tile_rsrc((ctx || CAUSAL ? p.K : p.Kself) + off, rows * ts * 2);
+    const __amdgpu_buffer_rsrc_t rk = tile_rsrc((ctx || CAUSAL ? p.K : p.Kself) + off, rows * ts * 2);
+    const __amdgpu_buffer_rsrc_t rv = tile_rsrc((ctx || CAUSAL ? p.V : p.Vself) + off, rows * ts * 2);
 #pragma unroll
-      for (int c = 0; c < T::KPT; ++c) {
-        const int idx = lt + c * (AT_THREADS / 2);
-        pre[c] = buf_ld16(rk, (idx / T::CPR) * ts * 2 + (idx % T::CPR) * 16);
-      }
-    } else {
-      const __amdgpu_buffer_rsrc_t rv = tile_rsrc((ctx || CAUSAL ? p.V : p.Vself) + off, rows * ts * 2);
+    for (int c = 0; c < T::KPT; ++c) {
+      const int idx = tid + c * AT_THREADS;
+      if (idx < T::CHUNKS) pre[c] = buf_ld16(rk, (idx / T::CPR) * ts * 2 + (idx % T::CPR) * 16);
+    }
 #pragma unroll
-      for (int u = 0; u < T::VPT; ++u) {
-        const int unit = lt + u * (AT_THREADS / 2);
-        if (unit < T::VUNITS) {
-          const int m = unit & 15, part = unit >> 4;
-          pre[2 * u] = buf_ld16(rv, (2 * m) * ts * 2 + part * 16);
-          pre[2 * u + 1] = buf_ld16(rv, (2 * m + 1) * ts * 2 + part * 16);
-        }
+    for (int u = 0; u < T::VPT; ++u) {
+      const int unit = tid + u * AT_THREADS;
+      if (unit < T::VUNITS) {
+        const int m = unit & 15, part = unit >> 4;
+        pre[T::KPT + 2 * u] = buf_ld16(rv, (2 * m) * ts * 2 + part * 16);
+        pre[T::KPT + 2 * u + 1] = buf_ld16(rv, (2 * m + 1) * ts * 2 + part * 16);
       }
     }
   };
   // K rows as they are (padded). V transposed: elements (2m, d) and (2m+1, d)
   // form one 32-bit word of value row d at column pair m; a half-wave's
   // stores hit 32 distinct banks with the 72-byte row stride.
-  auto store_tile = [&](int buf) {
-    char* st = s_tile[buf];
-    if (k_loader) {
+  auto store_tile = [&](char* st) {
 #pragma unroll
-      for (int c = 0; c < T::KPT; ++c) {
-        const int idx = lt + c * (AT_THREADS / 2);
-        *reinterpret_cast<u32x4*>(st + (idx / T::CPR) * T::K_STRIDE + (idx % T::CPR) * 16) = pre[c];
-      }
-    } else {
+    for (int c = 0; c < T::KPT; ++c) {
+      const int idx = tid + c * AT_THREADS;
+      if (idx < T::CHUNKS) *reinterpret_cast<u32x4*>(st + (idx / T::CPR) * T::K_STRIDE + (idx % T::CPR) * 16) = pre[c];
+    }
 #pragma unroll
-      for (int u = 0; u < T::VPT; ++u) {
-        const int unit = lt + u * (AT_THREADS / 2);
-        if (unit < T::VUNITS) {
-          const int m = unit & 15, part = unit >> 4;
-          char* vt = st + T::K_BYTES + (8 * part) * T::VT_STRIDE + 4 * m;
+    for (int u = 0; u < T::VPT; ++u) {
+      const int unit = tid + u * AT_THREADS;
+      if (unit < T::VUNITS) {
+        const int m = unit & 15, part = unit >> 4;
+        char* vt = st + T::K_BYTES + (8 * part) * T::VT_STRIDE + 4 * m;
+        const u32x4 a0 = pre[T::KPT + 2 * u], a1 = pre[T::KPT + 2 * u + 1];
 #pragma unroll
-          for (int w = 0; w < 4; ++w) {
-            // low halves (element 2w) and high halves (element 2w+1) of keys 2m, 2m+1
-            *reinterpret_cast<uint32_t*>(vt + (2 * w) * T::VT_STRIDE) =
-                __builtin_amdgcn_perm(pre[2 * u + 1][w], pre[2 * u][w], 0x05040100u);
-            *reinterpret_cast<uint32_t*>(vt + (2 * w + 1) * T::VT_STRIDE) =
-                __builtin_amdgcn_perm(pre[2 * u + 1][w], pre[2 * u][w], 0x07060302u);
-          }
+        for (int w = 0; w < 4; ++w) {
+          *reinterpret_cast<uint32_t*>(vt + (2 * w) * T::VT_STRIDE) = __builtin_amdgcn_perm(a1[w], a0[w], 0x05040100u);
+          *reinterpret_cast<uint32_t*>(vt + (2 * w + 1) * T::VT_STRIDE) = __builtin_amdgcn_perm(a1[w], a0[w], 0x07060302u);
         }
       }
     }
@@ -221,8 +218,8 @@ __global__ __launch_bounds__(AT_THREADS, 1) void attn_kernel(AttnParams p) {
   };
 
   // S = K Q^T of one tile (keys from LDS stage buf), raw dot products.
-  auto qk = [&](int buf) {
-    const char* krow = s_tile[buf] + col * T::K_STRIDE + half * D;
+  auto qk = [&](const char* st) {
+    const char* krow = st + col * T::K_STRIDE + half * D;
     bf16x8 a[T::STEPS];
 #pragma unroll
     for (int s = 0; s < T::STEPS; ++s) a[s] = as_bf16x8(*reinterpret_cast<const u32x4*>(krow + 16 * s));
@@ -234,8 +231,7 @@ __global__ __launch_bounds__(AT_THREADS, 1) void attn_kernel(AttnParams p) {
 
   // Mask, exponentiate against the lazy offset, and O^T += V^T P^T for one
   // tile whose S is x (values from LDS stage buf).
-  auto softmax_pv = [&](f32x16 x, int buf, bool masked, int k0, int kend, bool is_ctx) {
-    const char* st = s_tile[buf];
+  auto softmax_pv = [&](f32x16 x, const char* st, bool masked, int k0, int kend, bool is_ctx) {
     if (masked) {
       const int kb = k0 + 4 * half;
 #pragma unroll
@@ -309,33 +305,30 @@ __global__ __launch_bounds__(AT_THREADS, 1) void attn_kernel(AttnParams p) {
     return ti;
   };
 
-  // Software pipeline: while the softmax and PV of tile tt run on the VALU
-  // and the matrix core, S of tile tt+1 is already in flight, so a wave's
-  // matrix work overlaps its own exponentials even though the tile barrier
-  // keeps the waves in step. Tile tt lives in stage tt % NSTAGE from its
-  // store (two iterations ahead) until the barrier after its PV.
-  for (int t = 0; t < 2 && t < n_tiles; ++t) {
+  // Tiles TPS*i .. TPS*i + TPS-1 live in stage i % NSTAGE, stored NSTAGE-1
+  // iterations ahead; one barrier per stage.
+  constexpr int AHEAD = NSTAGE - 1;
+  const int n_iters = (n_tiles + TPS - 1) / TPS;
+  for (int t = 0; t < AHEAD * TPS && t < n_tiles; ++t) {
     load_tile(t);
-    store_tile(t);
+    store_tile(s_tile[(t / TPS) % NSTAGE][t % TPS]);
   }
   __syncthreads();
-  f32x16 x_cur = f32x16{};
-  {
-    const TileInfo ti = tile_info(0);
-    if (n_tiles > 0 && ti.run) x_cur = qk(0);
-  }
-  for (int tt = 0; tt < n_tiles; ++tt) {
-    if (tt + 2 < n_tiles) load_tile(tt + 2);
-    const TileInfo cur = tile_info(tt);
-    f32x16 x_next = f32x16{};
-    if (tt + 1 < n_tiles) {
-      const TileInfo nxt = tile_info(tt + 1);
-      if (nxt.run) x_next = qk((tt + 1) % NSTAGE);
+  for (int it = 0; it < n_iters; ++it) {
+#pragma unroll 1
+    for (int sub = 0; sub < TPS; ++sub) {
+      const int tt = TPS * it + sub;
+      const int tl = TPS * (it + AHEAD) + sub;  // loaded now, into the stage of iteration it - 1
+      if (tl < n_tiles) load_tile(tl);
+      const TileInfo cur = tile_info(tt);
+      const bool run = tt < n_tiles && cur.run;
+      const char* st = s_tile[it % NSTAGE][sub];
+      f32x16 x = f32x16{};
+      if (run) x = qk(st);
+      if (tl < n_tiles) store_tile(s_tile[(it + AHEAD) % NSTAGE][sub]);
+      if (run) softmax_pv(x, st, cur.masked, cur.k0, cur.kend, cur.is_ctx);
     }
-    if (cur.run) softmax_pv(x_cur, tt % NSTAGE, cur.masked, cur.k0, cur.kend, cur.is_ctx);
-    if (tt + 2 < n_tiles) store_tile((tt + 2) % NSTAGE);
     __syncthreads();
-    x_cur = x_next;
   }
 
   // ---- finish: merge the halves' partial sums, write LSE and O = O^T / l
