@@ -25,8 +25,10 @@
 //   * the exponentials P (against a per-query offset) are packed to bf16 and
 //     are, without any data movement, the B operand of O^T += V^T P^T: the
 //     16 keys a lane holds are the 2 x 8 contraction elements it supplies;
-//   * value tiles are stored transposed in LDS (rows = head dimension), so
-//     the A operand V^T is two 8-byte reads per 16 keys;
+//   * value tiles are stored transposed in LDS (rows = head dimension, 80-byte
+//     rows), with the keys of each row in the order the P operand takes them
+//     (key groups of 4 in the order 0 2 1 3 4 6 5 7), so the A operand V^T of
+//     one MFMA is one 16-byte read;
 //   * O^T accumulates in registers: a lane holds one query and D/2 of its
 //     output elements; it never leaves the chip until the final scaling by
 //     1 / sum P, which is per lane.
@@ -71,7 +73,7 @@ struct ATile {
   static constexpr int STEPS = D / 16;         // k-steps of the QK^T chain
   static constexpr int K_STRIDE = D * 2 + 16;  // padded key rows, bytes
   static constexpr int K_BYTES = 32 * K_STRIDE;
-  static constexpr int VT_STRIDE = 72;         // transposed value rows: 32 keys * 2 B + 8 B pad
+  static constexpr int VT_STRIDE = 80;         // transposed value rows: 32 keys * 2 B + 16 B pad
   static constexpr int V_BYTES = D * VT_STRIDE;
   static constexpr int STAGE = K_BYTES + V_BYTES;
   static constexpr int DB = D / 32;            // output row blocks of O^T
@@ -170,8 +172,9 @@ __global__ __launch_bounds__(AT_THREADS, 1) void attn_kernel(AttnParams p) {
     }
   };
   // K rows as they are (padded). V transposed: elements (2m, d) and (2m+1, d)
-  // form one 32-bit word of value row d at column pair m; a half-wave's
-  // stores hit 32 distinct banks with the 72-byte row stride.
+  // form one 32-bit word of value row d at its pair slot; a half-wave's
+  // stores (16 pair slots of two rows 8 apart) hit 32 distinct banks with the
+  // 80-byte row stride, as do a 16-lane group's 16-byte reads.
   auto store_tile = [&](char* st) {
 #pragma unroll
     for (int c = 0; c < T::KPT; ++c) {
@@ -183,7 +186,11 @@ __global__ __launch_bounds__(AT_THREADS, 1) void attn_kernel(AttnParams p) {
       const int unit = tid + u * AT_THREADS;
       if (unit < T::VUNITS) {
         const int m = unit & 15, part = unit >> 4;
-        char* vt = st + T::K_BYTES + (8 * part) * T::VT_STRIDE + 4 * m;
+        // key pair m sits at pair slot 2 * grp(m / 2) + m % 2, grp swapping
+        // key groups 1, 2 and 5, 6 (of 4 keys), so the 8 keys a lane feeds one
+        // MFMA are 16 contiguous bytes
+        const int g4 = m >> 1, sg = (g4 == 1 || g4 == 5) ? g4 + 1 : ((g4 == 2 || g4 == 6) ? g4 - 1 : g4);
+        char* vt = st + T::K_BYTES + (8 * part) * T::VT_STRIDE + 4 * (2 * sg + (m & 1));
         const u32x4 a0 = pre[T::KPT + 2 * u], a1 = pre[T::KPT + 2 * u + 1];
 #pragma unroll
         for (int w = 0; w < 4; ++w) {
@@ -261,21 +268,12 @@ __global__ __launch_bounds__(AT_THREADS, 1) void attn_kernel(AttnParams p) {
     }
     l_run += sum;
     const bf16x8 pb0 = pack_bf16(e, 0), pb1 = pack_bf16(e, 8);
-    const char* vrow = st + T::K_BYTES + col * T::VT_STRIDE + half * 8;
+    const char* vrow = st + T::K_BYTES + col * T::VT_STRIDE + half * 16;
 #pragma unroll
     for (int db = 0; db < T::DB; ++db) {
       const char* vr = vrow + 32 * db * T::VT_STRIDE;
-      bf16x8 v0, v1;
-      {
-        const bf16x4 lo = *reinterpret_cast<const bf16x4*>(vr);
-        const bf16x4 hi = *reinterpret_cast<const bf16x4*>(vr + 16);
-        v0 = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-      }
-      {
-        const bf16x4 lo = *reinterpret_cast<const bf16x4*>(vr + 32);
-        const bf16x4 hi = *reinterpret_cast<const bf16x4*>(vr + 48);
-        v1 = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-      }
+      const bf16x8 v0 = as_bf16x8(*reinterpret_cast<const u32x4*>(vr));
+      const bf16x8 v1 = as_bf16x8(*reinterpret_cast<const u32x4*>(vr + 32));
       oacc[db] = mfma32(v0, pb0, oacc[db]);
       oacc[db] = mfma32(v1, pb1, oacc[db]);
     }
