@@ -172,9 +172,9 @@ __global__ __launch_bounds__(AT_THREADS, 1) void attn_kernel(AttnParams p) {
     }
   };
   // K rows as they are (padded). V transposed: elements (2m, d) and (2m+1, d)
-  // form one 32-bit word of value row d at its pair slot; a half-wave's
-  // stores (16 pair slots of two rows 8 apart) hit 32 distinct banks with the
-  // 80-byte row stride, as do a 16-lane group's 16-byte reads.
+  // form one 32-bit word of value row d at its pair slot (80-byte rows, so an
+  // MFMA operand is one aligned 16-byte read); a half-wave's stores cover 16
+  // pair slots in two row groups, walked so that they hit distinct banks.
   auto store_tile = [&](char* st) {
 #pragma unroll
     for (int c = 0; c < T::KPT; ++c) {
@@ -191,11 +191,20 @@ __global__ __launch_bounds__(AT_THREADS, 1) void attn_kernel(AttnParams p) {
         // MFMA are 16 contiguous bytes
         const int g4 = m >> 1, sg = (g4 == 1 || g4 == 5) ? g4 + 1 : ((g4 == 2 || g4 == 6) ? g4 - 1 : g4);
         char* vt = st + T::K_BYTES + (8 * part) * T::VT_STRIDE + 4 * (2 * sg + (m & 1));
-        const u32x4 a0 = pre[T::KPT + 2 * u], a1 = pre[T::KPT + 2 * u + 1];
+        // odd pieces walk their rows from row 4 on (data word e goes to rows 2e,
+        // 2e+1 either way), so the two pieces of a half-wave store rows 4 or 12
+        // apart: 16 banks apart on 32 banks, 16 or 48 on 64
+        const bool odd = part & 1;
+        u32x4 a0 = pre[T::KPT + 2 * u], a1 = pre[T::KPT + 2 * u + 1];
+        if (odd) {
+          a0 = u32x4{a0[2], a0[3], a0[0], a0[1]};
+          a1 = u32x4{a1[2], a1[3], a1[0], a1[1]};
+        }
 #pragma unroll
         for (int w = 0; w < 4; ++w) {
-          *reinterpret_cast<uint32_t*>(vt + (2 * w) * T::VT_STRIDE) = __builtin_amdgcn_perm(a1[w], a0[w], 0x05040100u);
-          *reinterpret_cast<uint32_t*>(vt + (2 * w + 1) * T::VT_STRIDE) = __builtin_amdgcn_perm(a1[w], a0[w], 0x07060302u);
+          char* vr = vt + (((2 * w) + (odd ? 4 : 0)) & 7) * T::VT_STRIDE;
+          *reinterpret_cast<uint32_t*>(vr) = __builtin_amdgcn_perm(a1[w], a0[w], 0x05040100u);
+          *reinterpret_cast<uint32_t*>(vr + T::VT_STRIDE) = __builtin_amdgcn_perm(a1[w], a0[w], 0x07060302u);
         }
       }
     }
