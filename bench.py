@@ -525,8 +525,11 @@ def main():
                                                          BY_NAME["qwen2.5-1.5b-layer-kvzip+-2k"]))
     if not args.no_adjacent:
         attn_tflops = 2 * lse_flops / (t_attn * 1e-3) / 1e12
+        attn_traffic = stored_traffic(os.path.join(csrc_dir, "attn.hip"), "attn_qwen3-8b-32k_traffic.json") \
+            if wl.name == "qwen3-8b-layer-kvzip+-32k" else None
         adjacent["attention"] = {"entry": "kvscore_attention", "ms": t_attn, "flops": 2 * lse_flops,
-                                 "tflops": attn_tflops, "frac_of_bf16_peak": attn_tflops / PEAK_BF16_TFLOPS}
+                                 "tflops": attn_tflops, "frac_of_bf16_peak": attn_tflops / PEAK_BF16_TFLOPS,
+                                 "traffic": attn_traffic}
         dec_bytes = kept_total * 2 * r.D * 2 + r.Hq * r.D * 2 * 2  # kept K and V rows, plus Q and O
         adjacent["decode"] = {"entry": "kvscore_decode", "ms": t_dec, "queries_per_head": 1, "rows": kept_total,
                               "bytes": dec_bytes, "gbs": dec_bytes / (t_dec * 1e-3) / 1e9,
