@@ -45,6 +45,12 @@ CASES = [
     ("causal-g6-ragged", dict(Hq=6, Hkv=1, D=128, n_ctx=777, n_q=777, mask="causal"), "causal", 0),
     ("causal-g4-sinks-d64", dict(Hq=8, Hkv=2, D=64, n_ctx=1000, n_q=1000, mask="causal", sinks=4), "causal", 0),
     ("causal-tiny", dict(Hq=2, Hkv=1, D=128, n_ctx=3, n_q=3, mask="causal"), "causal", 0),
+    # key tiles go through LDS 4 to a stage; workgroups hold 12 query
+    # subtiles: one whole stage of context tiles, a stage plus one tile, and a
+    # last workgroup with 3 of its 12 subtiles filled
+    ("repeat-one-stage", dict(Hq=4, Hkv=1, D=128, n_ctx=128, n_q=70), "repeat", 64),
+    ("repeat-stage-plus-one-g3", dict(Hq=3, Hkv=1, D=64, n_ctx=160, n_q=132), "repeat", 40),
+    ("causal-five-tiles-g5", dict(Hq=5, Hkv=1, D=128, n_ctx=129, n_q=129, mask="causal"), "causal", 0),
 ]
 
 
