@@ -494,6 +494,8 @@ constexpr int HD_MAX = 16384;
 constexpr int HD_COPIES = 8;
 constexpr int HD_UNROLL = 16;  // score loads in flight per thread
 constexpr int HD_CSTRIDE = NBINS + 1;  // words between histogram copies
+constexpr int HD_STEPS = HD_MAX / (HD_WAVES * WAVE);  // 64-position steps of a wave's segment
+static_assert(2 * HD_STEPS <= 32, "a segment's classes fit one 32-bit word per lane");
 constexpr int HD_ROWS_PER_WG = 128;    // kept rows a workgroup of a head copies (sets the workgroups per head)
 constexpr int HD_MAX_REPS = 64;        // at most this many workgroups per head
 constexpr int HD_CP_PASSES = 4;        // copy passes with loads in flight
@@ -643,13 +645,17 @@ __global__ __launch_bounds__(HD_THREADS) void evict_head(EvictParams p, int reps
     return u > T ? 1 : (u == T ? 2 : 0);
   };
   constexpr int WU = 2;  // 64-position steps of a walk whose reads are issued together
+  // the walk's classes, 2 bits per step (a segment has at most HD_STEPS steps),
+  // kept for the write walk
+  uint32_t cls_bits = 0u;
   int n_keep = 0, n_tie = 0;
-  for (int i0 = seg_lo; i0 < seg_hi; i0 += WAVE * WU) {
+  for (int i0 = seg_lo, st = 0; i0 < seg_hi; i0 += WAVE * WU, st += WU) {
     int c[WU];
 #pragma unroll
     for (int k = 0; k < WU; ++k) c[k] = cls_of(i0 + k * WAVE + lane);
 #pragma unroll
     for (int k = 0; k < WU; ++k) {
+      cls_bits |= (uint32_t)c[k] << (2 * (st + k));
       n_keep += __popcll(__ballot(c[k] == 1));
       n_tie += __popcll(__ballot(c[k] == 2));
     }
@@ -681,10 +687,10 @@ __global__ __launch_bounds__(HD_THREADS) void evict_head(EvictParams p, int reps
   const int o_lo = (int)((int64_t)per_head * rep / reps);
   const int o_hi = (int)((int64_t)per_head * (rep + 1) / reps);
   uint32_t* s_pos = s_hist;  // the histogram's space, free after the selection (barriers since its last read)
-  for (int i0 = seg_lo; i0 < seg_hi; i0 += WAVE * WU) {
+  for (int i0 = seg_lo, st = 0; i0 < seg_hi; i0 += WAVE * WU, st += WU) {
     int c[WU];
 #pragma unroll
-    for (int k = 0; k < WU; ++k) c[k] = cls_of(i0 + k * WAVE + lane);
+    for (int k = 0; k < WU; ++k) c[k] = (int)((cls_bits >> (2 * (st + k))) & 3u);
 #pragma unroll
     for (int k = 0; k < WU; ++k) {
       const int i = i0 + k * WAVE + lane;
