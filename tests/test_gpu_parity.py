@@ -403,6 +403,58 @@ def test_evict_reuses_one_workspace():
         _check_evict_exact(name, s, K, V, window, k, tau, kept, offs, Ko, Vo)
 
 
+def _sweep_case(i):
+    """Seeded random eviction case i: shape, window, mode (per-head top-k,
+    threshold or one layer budget) and score law (log-normal with ties and
+    zeros, one octave, three values)."""
+    rng = np.random.default_rng(5150 + i)
+    Hkv = int(rng.integers(1, 13))
+    n = int(np.exp(rng.uniform(0.0, np.log(20000.0))))
+    n = min(n, 120000 // Hkv)
+    D = int(rng.choice([64, 128]))
+    window = int(rng.integers(0, n + 11)) if rng.random() < 0.3 else int(rng.integers(0, min(n, 512) + 1))
+    mode = str(rng.choice(["topk", "topk", "tau", "layer"]))
+    law = str(rng.choice(["lognormal", "lognormal", "octave", "three"]))
+    if law == "lognormal":
+        sc = synth.evict_scores(6000 + i, Hkv, n, tie_frac=float(rng.uniform(0, 0.3)), zero_frac=0.02)
+    elif law == "octave":
+        sc = (0.5 + 0.5 * rng.random((Hkv, n))).astype(np.float32)
+    else:
+        sc = rng.choice(np.array([0.1, 0.2, 0.3], dtype=np.float32), size=(Hkv, n))
+    cand = max(n - window, 0)
+    k = tau = None
+    if mode == "tau":
+        tau = float(np.quantile(sc, rng.uniform(0, 1))) if sc.size else 0.5
+    elif mode == "layer":
+        k = int(rng.integers(0, Hkv * cand + 2))
+    else:
+        k = int(rng.integers(0, cand + 2))
+    return Hkv, n, D, window, mode, law, sc, k, tau
+
+
+@pytest.mark.parametrize("i", range(40))
+def test_evict_random_sweep(i):
+    """Forty seeded random layers through both eviction paths and all modes:
+    exactly the oracle's selection and compaction."""
+    Hkv, n, D, window, mode, law, sc, k, tau = _sweep_case(i)
+    K = synth.normal_bf16(7000 + i, 90, (Hkv, n, D))
+    V = synth.normal_bf16(7000 + i, 91, (Hkv, n, D))
+    name = f"sweep-{i} Hkv={Hkv} n={n} D={D} w={window} {mode} {law} k={k} tau={tau}"
+    say(f"[evict] {name}")
+    scope = "layer" if mode == "layer" else "head"
+    kept, offs, Ko, Vo = kvs.evict(dev_f32(sc), dev_bf16(K), dev_bf16(V), window=window, k=k, tau=tau, scope=scope)
+    torch.cuda.synchronize()
+    offs = host(offs)
+    ref = oracle.select(sc, window, k=k, tau=tau, scope=scope)
+    gk = kept_from_gpu(host(kept), offs)
+    for h in range(Hkv):
+        assert np.array_equal(gk[h], ref[h]), f"{name}: head {h} differs"
+    Kr, Vr, offr = oracle.compact(K, V, ref)
+    assert np.array_equal(offs, offr), f"{name}: offsets differ"
+    total = int(offs[-1])
+    assert np.array_equal(host_bits(Ko)[:total], Kr) and np.array_equal(host_bits(Vo)[:total], Vr), name
+
+
 LAYER_CASES = [
     # name, Hkv, n, D, window, k (one budget for the layer), identical heads
     ("layer-multiblock", 4, 5000, 128, 128, 3000, False),
