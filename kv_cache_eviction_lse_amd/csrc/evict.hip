@@ -530,6 +530,7 @@ __device__ __forceinline__ int wave_incl_scan(int x) {
 // thread whose range holds the rank-th key names the digit. Block-wide;
 // every thread returns the same values, and every read of hist is done
 // before the first barrier inside.
+template <int COPIES>
 __device__ void hd_find_digit(const uint32_t* hist, int nbins, int rank, int& digit, int& above) {
   __shared__ __attribute__((aligned(16))) int s_wsum[HD_WAVES];
   __shared__ int s_digit, s_above;
@@ -540,7 +541,7 @@ __device__ void hd_find_digit(const uint32_t* hist, int nbins, int rank, int& di
   auto count = [&](int b) {
     int c = 0;
 #pragma unroll
-    for (int k = 0; k < HD_COPIES; ++k) c += (int)hist[k * HD_CSTRIDE + b];
+    for (int k = 0; k < COPIES; ++k) c += (int)hist[k * HD_CSTRIDE + b];
     return c;
   };
   const int lo = (HD_THREADS - 1 - tid) * per;
@@ -568,6 +569,7 @@ template <int D>
 __global__ __launch_bounds__(HD_THREADS) void evict_head(EvictParams p, int reps) {
   __shared__ uint32_t s_key[HD_MAX];
   __shared__ __attribute__((aligned(16))) uint32_t s_hist[HD_CSTRIDE * HD_COPIES];
+  __shared__ uint32_t s_hist12[NBINS + NBINS / 2];  // passes 2 and 3: one copy each (few keys reach them)
   __shared__ int s_cnt[HD_WAVES][2];
   const int h = blockIdx.x / reps;
   const int rep = blockIdx.x % reps;
@@ -601,11 +603,16 @@ __global__ __launch_bounds__(HD_THREADS) void evict_head(EvictParams p, int reps
 #pragma unroll 1
     for (int pass = 0; pass < 3; ++pass) {
       const int nbins = pass == 2 ? 1024 : 2048;
-      for (int i = tid; i < HD_CSTRIDE * HD_COPIES; i += HD_THREADS) s_hist[i] = 0u;
-      __syncthreads();  // (pass 0: also the key stores)
+      if (pass == 0) {
+        for (int i = tid; i < HD_CSTRIDE * HD_COPIES; i += HD_THREADS) s_hist[i] = 0u;
+        for (int i = tid; i < NBINS + NBINS / 2; i += HD_THREADS) s_hist12[i] = 0u;
+      }
+      __syncthreads();  // (pass 0: also the key stores and the clears)
+      uint32_t* hist = pass == 0 ? s_hist : s_hist12 + (pass == 2 ? NBINS : 0);
       const int hs = pass > 0 ? digit_shift(pass - 1) : 32;
       const int ds = digit_shift(pass);
       const uint32_t dm = digit_mask(pass);
+      const int cofs = pass == 0 ? copy * HD_CSTRIDE : 0;
       constexpr int RU = 4;  // LDS reads of a batch issued before its atomics
       for (int i0 = tid; i0 < n_cand; i0 += HD_THREADS * RU) {
         uint32_t u[RU];
@@ -618,12 +625,15 @@ __global__ __launch_bounds__(HD_THREADS) void evict_head(EvictParams p, int reps
         for (int k = 0; k < RU; ++k) {
           const int i = i0 + k * HD_THREADS;
           if (i < n_cand && (pass == 0 || (u[k] >> hs) == (prefix >> hs)))
-            atomicAdd(&s_hist[copy * HD_CSTRIDE + ((u[k] >> ds) & dm)], 1u);
+            atomicAdd(&hist[cofs + ((u[k] >> ds) & dm)], 1u);
         }
       }
       __syncthreads();
       int digit, above;
-      hd_find_digit(s_hist, nbins, rank, digit, above);
+      if (pass == 0)
+        hd_find_digit<HD_COPIES>(hist, nbins, rank, digit, above);
+      else
+        hd_find_digit<1>(hist, nbins, rank, digit, above);
       prefix |= (uint32_t)digit << ds;
       rank -= above;
     }
