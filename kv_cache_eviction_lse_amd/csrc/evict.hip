@@ -569,7 +569,7 @@ template <int D>
 __global__ __launch_bounds__(HD_THREADS) void evict_head(EvictParams p, int reps) {
   __shared__ uint32_t s_key[HD_MAX];
   __shared__ __attribute__((aligned(16))) uint32_t s_hist[HD_CSTRIDE * HD_COPIES];
-  __shared__ uint32_t s_hist12[NBINS + NBINS / 2];  // passes 2 and 3: one copy each (few keys reach them)
+  __shared__ __attribute__((aligned(16))) uint32_t s_hist12[NBINS + NBINS / 2];  // passes 2 and 3: one copy each (few keys reach them)
   __shared__ int s_cnt[HD_WAVES][2];
   const int h = blockIdx.x / reps;
   const int rep = blockIdx.x % reps;
@@ -584,29 +584,32 @@ __global__ __launch_bounds__(HD_THREADS) void evict_head(EvictParams p, int reps
   int quota = 0;
   const bool topk = p.mode == MODE_TOPK;
   if (topk) {
-    // order keys of the candidates into LDS (HD_UNROLL loads in flight)
-    for (int i0 = tid; i0 < n_cand; i0 += HD_THREADS * HD_UNROLL) {
-      float v[HD_UNROLL];
+    // order keys of the candidates into LDS: a thread's HD_UNROLL score
+    // loads (all its candidates) go out first, and the histograms are cleared
+    // while they are in flight
+    static_assert(HD_THREADS * HD_UNROLL == HD_MAX, "one round of loads covers every candidate");
+    float v[HD_UNROLL];
 #pragma unroll
-      for (int u = 0; u < HD_UNROLL; ++u) {
-        const int i = i0 + u * HD_THREADS;
-        v[u] = i < n_cand ? sc[i] : 0.f;
-      }
+    for (int u = 0; u < HD_UNROLL; ++u) {
+      const int i = tid + u * HD_THREADS;
+      v[u] = i < n_cand ? sc[i] : 0.f;
+    }
+    {
+      u32x4* h4 = reinterpret_cast<u32x4*>(s_hist);
+      for (int i = tid; i < HD_CSTRIDE * HD_COPIES / 4; i += HD_THREADS) h4[i] = u32x4{0u, 0u, 0u, 0u};
+      u32x4* g4 = reinterpret_cast<u32x4*>(s_hist12);
+      for (int i = tid; i < (NBINS + NBINS / 2) / 4; i += HD_THREADS) g4[i] = u32x4{0u, 0u, 0u, 0u};
+    }
 #pragma unroll
-      for (int u = 0; u < HD_UNROLL; ++u) {
-        const int i = i0 + u * HD_THREADS;
-        if (i < n_cand) s_key[i] = order_key(v[u]);
-      }
+    for (int u = 0; u < HD_UNROLL; ++u) {
+      const int i = tid + u * HD_THREADS;
+      if (i < n_cand) s_key[i] = order_key(v[u]);
     }
     uint32_t prefix = 0;
     int rank = (int)p.kprime;
 #pragma unroll 1
     for (int pass = 0; pass < 3; ++pass) {
       const int nbins = pass == 2 ? 1024 : 2048;
-      if (pass == 0) {
-        for (int i = tid; i < HD_CSTRIDE * HD_COPIES; i += HD_THREADS) s_hist[i] = 0u;
-        for (int i = tid; i < NBINS + NBINS / 2; i += HD_THREADS) s_hist12[i] = 0u;
-      }
       __syncthreads();  // (pass 0: also the key stores and the clears)
       uint32_t* hist = pass == 0 ? s_hist : s_hist12 + (pass == 2 ? NBINS : 0);
       const int hs = pass > 0 ? digit_shift(pass - 1) : 32;
