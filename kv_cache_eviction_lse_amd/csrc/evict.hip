@@ -64,6 +64,7 @@ struct EvictParams {
   int layer;  // top-k over all heads' candidates together (one histogram, one quota)
   float tau;
   int64_t per_head;  // one-workgroup-per-head path: rows per head (known on the host there)
+  int32_t rows_q, rows_r;  // per-head path: workgroup r of a head owns rows_q + (r < rows_r) rows
 };
 
 // Order-preserving key: a > b as floats <=> key(a) > key(b); -0 and +0 share
@@ -678,7 +679,7 @@ __global__ __launch_bounds__(HD_THREADS) void evict_head(EvictParams p, int reps
     s_cnt[wave][1] = n_tie;
   }
   __syncthreads();
-  int out_run = 0, tie_run = 0, total = 0, ties_seen = 0;
+  int out_run = 0, tie_run = 0, total = 0, ties_seen = 0, my_rows = 0;
   for (int w = 0; w < HD_WAVES; ++w) {
     const int kw = s_cnt[w][0], tw = s_cnt[w][1];
     const int take = min(max(quota - ties_seen, 0), tw);
@@ -686,6 +687,7 @@ __global__ __launch_bounds__(HD_THREADS) void evict_head(EvictParams p, int reps
       out_run += kw + take;
       tie_run += tw;
     }
+    if (w == wave) my_rows = kw + take;
     total += kw + take;
     ties_seen += tw;
   }
@@ -697,10 +699,12 @@ __global__ __launch_bounds__(HD_THREADS) void evict_head(EvictParams p, int reps
   int32_t* out = p.kept_idx + (int64_t)h * per_head;
   const int w_rows = (int)(p.n - p.n_cand);
   const int cand_rows = per_head - w_rows;
-  const int o_lo = (int)((int64_t)per_head * rep / reps);
-  const int o_hi = (int)((int64_t)per_head * (rep + 1) / reps);
+  const int o_lo = rep * p.rows_q + min(rep, p.rows_r);
+  const int o_hi = o_lo + p.rows_q + (rep < p.rows_r ? 1 : 0);
   uint32_t* s_pos = s_hist;  // the histogram's space, free after the selection (barriers since its last read)
-  for (int i0 = seg_lo, st = 0; i0 < seg_hi; i0 += WAVE * WU, st += WU) {
+  // only waves whose output rows meet this workgroup's candidate rows walk
+  const bool my_part = out_run < min(o_hi, cand_rows) && out_run + my_rows > o_lo;  // wave-uniform
+  for (int i0 = seg_lo, st = 0; my_part && i0 < seg_hi; i0 += WAVE * WU, st += WU) {
     int c[WU];
 #pragma unroll
     for (int k = 0; k < WU; ++k) c[k] = (int)((cls_bits >> (2 * (st + k))) & 3u);
@@ -868,6 +872,8 @@ hipError_t launch_evict(const kvs_evict_desc& e, const float* scores, const uint
     reps = reps < HD_MAX_REPS ? reps : HD_MAX_REPS;
     reps = reps < 1 ? 1 : reps;
     const int64_t blocks = (int64_t)p.Hkv * reps;  // Hkv * n < 2^31 and reps <= 64
+    p.rows_q = (int32_t)(p.per_head / reps);
+    p.rows_r = (int32_t)(p.per_head % reps);
     if (p.D == 128)
       hipLaunchKernelGGL(evict_head<128>, dim3((unsigned)blocks), dim3(HD_THREADS), 0, s, p, (int)reps);
     else
