@@ -64,7 +64,11 @@ struct EvictParams {
   int layer;  // top-k over all heads' candidates together (one histogram, one quota)
   float tau;
   int64_t per_head;  // one-workgroup-per-head path: rows per head (known on the host there)
-  int32_t rows_q, rows_r;  // per-head path: workgroup r of a head owns rows_q + (r < rows_r) rows
+  int32_t rows_q, rows_r;  // per-head paths: workgroup r of a head owns rows_q + (r < rows_r) rows
+  int32_t vec4;            // long-head path: scores 16-byte aligned with a head stride divisible by 4
+  uint32_t* seg_above;     // long-head path: [Hkv][n_seg] keys above the first digit's bin per segment
+  int32_t* lh_state;       // long-head path: [Hkv][4] first digit, rank inside its bin, keys in the bin
+  uint2* lh_list;          // long-head path: [Hkv][LH_CAP] (key, position) of the bin's keys
 };
 
 // Order-preserving key: a > b as floats <=> key(a) > key(b); -0 and +0 share
@@ -523,31 +527,22 @@ __device__ __forceinline__ int wave_incl_scan(int x) {
   return x + (row >= 1 ? r0 : 0) + (row >= 2 ? r1 : 0) + (row >= 3 ? r2 : 0);
 }
 
-// The digit (of nbins, counts summed over the copies) holding the rank-th
-// largest key, and the number of keys in higher digits (1 <= rank <= the
-// keys counted). Thread t holds digits (HD_THREADS - 1 - t) * per ..
-// + per - 1, so thread order is descending digit order; a wave scan plus the
-// 16 wave totals give each thread the keys above its digits, and the one
-// thread whose range holds the rank-th key names the digit. Block-wide;
-// every thread returns the same values, and every read of hist is done
-// before the first barrier inside.
-template <int COPIES>
-__device__ void hd_find_digit(const uint32_t* hist, int nbins, int rank, int& digit, int& above) {
+// The digit holding the rank-th largest key, from per-thread digit counts:
+// thread t holds the counts of digits lo + per - 1 (c_top) and lo (c_low,
+// per == 2 only), lo = (HD_THREADS - 1 - t) * per, so thread order is
+// descending digit order. A wave scan plus the 16 wave totals give each
+// thread the keys above its digits, and the one thread whose range holds the
+// rank-th key names the digit, the keys in higher digits and the digit's own
+// count (1 <= rank <= the keys counted). Block-wide; every thread returns the
+// same values.
+__device__ __forceinline__ void hd_find_core(int c_top, int c_low, int per, int rank, int& digit, int& above,
+                                             int& count) {
   __shared__ __attribute__((aligned(16))) int s_wsum[HD_WAVES];
-  __shared__ int s_digit, s_above;
+  __shared__ int s_digit, s_above, s_count;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int per = nbins / HD_THREADS;  // 2 (2048 bins) or 1 (1024)
-  auto count = [&](int b) {
-    int c = 0;
-#pragma unroll
-    for (int k = 0; k < COPIES; ++k) c += (int)hist[k * HD_CSTRIDE + b];
-    return c;
-  };
   const int lo = (HD_THREADS - 1 - tid) * per;
-  const int c_top = count(lo + per - 1);  // the thread's higher digit first
-  const int c_low = per == 2 ? count(lo) : 0;
   const int mine = c_top + c_low;
   const int x = wave_incl_scan(mine);
   if (lane == WAVE - 1) s_wsum[wave] = x;
@@ -560,10 +555,71 @@ __device__ void hd_find_digit(const uint32_t* hist, int nbins, int rank, int& di
     const bool in_top = rank <= excl + c_top;
     s_digit = in_top ? lo + per - 1 : lo;
     s_above = in_top ? excl : excl + c_top;
+    s_count = in_top ? c_top : c_low;
   }
   __syncthreads();
   digit = s_digit;
   above = s_above;
+  count = s_count;
+}
+
+// hd_find_core over an LDS histogram of nbins (2048 or 1024) digits whose
+// counts are summed over COPIES copies; every read of hist is done before
+// the first barrier inside.
+template <int COPIES>
+__device__ void hd_find_digit(const uint32_t* hist, int nbins, int rank, int& digit, int& above) {
+  const int per = nbins / HD_THREADS;  // 2 (2048 bins) or 1 (1024)
+  auto count = [&](int b) {
+    int c = 0;
+#pragma unroll
+    for (int k = 0; k < COPIES; ++k) c += (int)hist[k * HD_CSTRIDE + b];
+    return c;
+  };
+  const int lo = (HD_THREADS - 1 - (int)threadIdx.x) * per;
+  const int c_top = count(lo + per - 1);  // the thread's higher digit first
+  const int c_low = per == 2 ? count(lo) : 0;
+  int in_digit;
+  hd_find_core(c_top, c_low, per, rank, digit, above, in_digit);
+}
+
+// Copy of a head's output rows [o_lo, o_hi): D / 8 lanes per row, 16-byte
+// pieces, HD_CP_PASSES passes of loads issued before their stores,
+// non-temporal. Rows below cand_end take their positions from s_pos (row o
+// at s_pos[o - o_lo]); row o >= total is window row o - total.
+template <int D>
+__device__ __forceinline__ void hd_copy_rows(const EvictParams& p, int h, int o_lo, int o_hi, int cand_end,
+                                             int total, const uint32_t* s_pos) {
+  constexpr int LPR = D / 8;
+  constexpr int RPP = HD_THREADS / LPR;
+  const int tid = threadIdx.x;
+  const int part = tid % LPR;
+  const int rr = tid / LPR;
+  const int n_cand = (int)p.n_cand;
+  const int64_t out_row0 = (int64_t)h * p.per_head;
+  const int64_t head_base = (int64_t)h * p.kv_hs + part * 8;
+  for (int b = o_lo; b < o_hi; b += RPP * HD_CP_PASSES) {
+    u32x4 kv[HD_CP_PASSES], vv[HD_CP_PASSES];
+#pragma unroll
+    for (int q = 0; q < HD_CP_PASSES; ++q) {
+      const int o = b + q * RPP + rr;
+      if (o < o_hi) {
+        int64_t pos = o < cand_end ? (int64_t)s_pos[o - o_lo] : (int64_t)n_cand + (o - total);
+        pos = pos < 0 ? 0 : (pos >= p.n ? p.n - 1 : pos);
+        const int64_t src = head_base + pos * p.kv_ts;
+        kv[q] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p.K + src));
+        vv[q] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p.V + src));
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < HD_CP_PASSES; ++q) {
+      const int o = b + q * RPP + rr;
+      if (o < o_hi) {
+        const int64_t dst = (out_row0 + o) * D + part * 8;
+        __builtin_nontemporal_store(kv[q], reinterpret_cast<u32x4*>(p.K_out + dst));
+        __builtin_nontemporal_store(vv[q], reinterpret_cast<u32x4*>(p.V_out + dst));
+      }
+    }
+  }
 }
 
 template <int D>
@@ -733,38 +789,474 @@ __global__ __launch_bounds__(HD_THREADS) void evict_head(EvictParams p, int reps
   }
   __syncthreads();  // s_pos complete
 
-  // Copy of the rows [o_lo, o_hi): D / 8 lanes per row, 16-byte pieces,
-  // HD_CP_PASSES passes of loads issued before their stores, non-temporal.
-  constexpr int LPR = D / 8;
-  constexpr int RPP = HD_THREADS / LPR;
-  const int part = tid % LPR;
-  const int rr = tid / LPR;
-  const int cand_end = min(total, cand_rows);  // rows below this hold candidates
-  const int64_t out_row0 = (int64_t)h * per_head;
-  const int64_t head_base = (int64_t)h * p.kv_hs + part * 8;
-  for (int b = o_lo; b < o_hi; b += RPP * HD_CP_PASSES) {
-    u32x4 kv[HD_CP_PASSES], vv[HD_CP_PASSES];
+  hd_copy_rows<D>(p, h, o_lo, o_hi, min(total, cand_rows), total, s_pos);
+}
+
+// ---------------------------------------------------------------- long heads
+// Per-head top-k with more than HD_MAX candidates per head (up to LH_MAX),
+// three launches:
+// evict_lh_hist: blocks of LH_CHUNK positions of a head each store the
+//   histogram of their keys' first radix digit (bits 31..21) with plain
+//   stores, so no workspace needs clearing.
+// evict_lh_bin: the same blocks each sum their head's block histograms and
+//   find the first digit of the k-th key; then, for their own positions,
+//   they store per segment of LH_SEG positions the count of keys above that
+//   digit's bin, and the (key, position) pairs of the keys inside it into
+//   the head's list. A block's first list entry is the bin count of the
+//   blocks before it, read from their histograms, so the list holds exactly
+//   the bin's keys in position order of blocks, with the keys of a segment
+//   adjacent. (A bin of more than LH_CAP keys is not listed.)
+// evict_long_head: `reps` workgroups per head, each of which finishes the
+//   selection from the list in LDS: second and third digits, then the kept
+//   and tied counts per segment. (For a bin too large for the list, it reads
+//   the scores for these steps instead.) A scan of the segment counts gives
+//   every segment its first output row and the ties before it; the
+//   workgroup walks only the segments that meet its rows [o_lo, o_hi),
+//   writes their kept positions and copies the rows as evict_head does.
+//   Workgroup b serves head b % Hkv: with a multiple of 8 heads the
+//   workgroups of one head share an XCD and its L2.
+constexpr int LH_SEG = 4 * WAVE;                // positions per segment: a 16-byte load per lane of a wave
+constexpr int LH_MAX_SEGS = 2 * HD_THREADS;     // two segments per thread in the scans
+constexpr int LH_MAX = LH_SEG * LH_MAX_SEGS;    // 524,288 candidates per head
+constexpr int LH_CAP = 16384;                   // keys of the first digit's bin kept in LDS
+constexpr int LH_CHUNK = 8 * HD_THREADS;        // positions per first-digit histogram block
+constexpr int LH_SPW = LH_CHUNK / LH_SEG / HD_WAVES;  // segments per wave in evict_lh_bin
+constexpr int LH_UNROLL = 4;                    // segments per wave with loads in flight (score passes)
+constexpr int LH_ROWS_PER_WG = 128;             // kept rows per workgroup, before the fill cap
+
+// Scores i .. i + 3 of a head through a buffer resource over its candidates
+// (a load past them reads 0; callers mask those entries). `wide` (uniform
+// over the wave: an aligned head and a segment that is not the ragged last
+// one) takes one 16-byte load, else four 4-byte loads, each checked on its
+// own against the resource's end. No per-lane branch: a load is never
+// ordered behind another path's loads into the same registers.
+__device__ __forceinline__ void lh_load(__amdgpu_buffer_rsrc_t r, int i, bool wide, float (&v)[4]) {
+  if (wide) {
+    const u32x4 x = buf_ld16(r, 4 * i);
 #pragma unroll
-    for (int q = 0; q < HD_CP_PASSES; ++q) {
-      const int o = b + q * RPP + rr;
-      if (o < o_hi) {
-        int64_t pos = o < cand_end ? (int64_t)s_pos[o - o_lo] : (int64_t)n_cand + (o - total);
-        pos = pos < 0 ? 0 : (pos >= p.n ? p.n - 1 : pos);
-        const int64_t src = head_base + pos * p.kv_ts;
-        kv[q] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p.K + src));
-        vv[q] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p.V + src));
+    for (int e = 0; e < 4; ++e) v[e] = __uint_as_float(x[e]);
+  } else {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) v[e] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, 4 * (i + e), 0, 0));
+  }
+}
+
+// grid: nch blocks per head, head-major (block h * nch + c)
+__global__ __launch_bounds__(HD_THREADS) void evict_lh_hist(EvictParams p, int nch) {
+  __shared__ __attribute__((aligned(16))) uint32_t s_h[HD_CSTRIDE * HD_COPIES];
+  const int h = blockIdx.x / nch, c = blockIdx.x % nch;
+  const int tid = threadIdx.x;
+  const int copy = (tid & 63) % HD_COPIES;
+  const int n_cand = (int)p.n_cand;
+  const float* sc = p.scores + (int64_t)h * p.s_hs;
+  constexpr int PER = LH_CHUNK / HD_THREADS;
+  float v[PER];
+#pragma unroll
+  for (int u = 0; u < PER; ++u) {
+    const int i = c * LH_CHUNK + u * HD_THREADS + tid;
+    v[u] = i < n_cand ? sc[i] : 0.f;
+  }
+  u32x4* h4 = reinterpret_cast<u32x4*>(s_h);
+  for (int i = tid; i < HD_CSTRIDE * HD_COPIES / 4; i += HD_THREADS) h4[i] = u32x4{0u, 0u, 0u, 0u};
+  __syncthreads();
+#pragma unroll
+  for (int u = 0; u < PER; ++u) {
+    const int i = c * LH_CHUNK + u * HD_THREADS + tid;
+    if (i < n_cand) atomicAdd(&s_h[copy * HD_CSTRIDE + (order_key(v[u]) >> 21)], 1u);
+  }
+  __syncthreads();
+  const int b = 2 * tid;
+  uint32_t c0 = 0, c1 = 0;
+#pragma unroll
+  for (int k = 0; k < HD_COPIES; ++k) {
+    c0 += s_h[k * HD_CSTRIDE + b];
+    c1 += s_h[k * HD_CSTRIDE + b + 1];
+  }
+  *reinterpret_cast<uint2*>(p.hist + ((int64_t)h * nch + c) * NBINS + b) = make_uint2(c0, c1);
+}
+
+// grid: nch blocks per head, head-major (block h * nch + c)
+__global__ __launch_bounds__(HD_THREADS) void evict_lh_bin(EvictParams p, int nch) {
+  __shared__ int s_wn[HD_WAVES];
+  __shared__ int s_cbase;
+  const int h = blockIdx.x / nch, c = blockIdx.x % nch;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int n_cand = (int)p.n_cand;
+  const int n_seg = (n_cand + LH_SEG - 1) / LH_SEG;
+  const __amdgpu_buffer_rsrc_t rs = tile_rsrc(p.scores + (int64_t)h * p.s_hs, 4 * n_cand);
+  const int n_wide = p.vec4 ? (n_cand % LH_SEG == 0 ? n_seg : n_seg - 1) : 0;
+  const int sg0 = c * (LH_CHUNK / LH_SEG) + wave * LH_SPW;  // this wave's first segment
+  float v[LH_SPW][4];
+#pragma unroll
+  for (int u = 0; u < LH_SPW; ++u) {
+    const int sg = sg0 + u;
+    if (sg < n_seg) lh_load(rs, sg * LH_SEG + 4 * lane, sg < n_wide, v[u]);
+  }
+  // first digit: thread t sums digits 2 * (HD_THREADS - 1 - t) and + 1 over
+  // the head's block histograms (descending digit order over the threads)
+  int c_low = 0, c_top = 0;
+  {
+    const uint32_t* g = p.hist + (int64_t)h * nch * NBINS + 2 * (HD_THREADS - 1 - tid);
+#pragma unroll 8
+    for (int cc = 0; cc < nch; ++cc) {
+      const uint2 x = *reinterpret_cast<const uint2*>(g + (int64_t)cc * NBINS);
+      c_low += (int)x.x;
+      c_top += (int)x.y;
+    }
+  }
+  int d0, above, n_bin;
+  hd_find_core(c_top, c_low, 2, (int)p.kprime, d0, above, n_bin);
+  if (c == 0 && tid == 0) {
+    p.lh_state[4 * h + 0] = d0;
+    p.lh_state[4 * h + 1] = (int)p.kprime - above;  // rank of the k-th key inside the bin
+    p.lh_state[4 * h + 2] = n_bin;
+  }
+  const uint32_t d0u = (uint32_t)d0;
+  uint32_t k[LH_SPW][4];
+  uint64_t m[LH_SPW][4];
+  int w_n = 0;  // this wave's bin keys (wave-uniform)
+#pragma unroll
+  for (int u = 0; u < LH_SPW; ++u) {
+    const int sg = sg0 + u;
+    const int i = sg * LH_SEG + 4 * lane;
+    int n_above = 0;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      k[u][e] = order_key(v[u][e]);
+      const bool ok = i + e < n_cand;  // (false past the last segment)
+      n_above += __popcll(__ballot(ok && (k[u][e] >> 21) > d0u));
+      m[u][e] = __ballot(ok && (k[u][e] >> 21) == d0u);
+      w_n += __popcll(m[u][e]);
+    }
+    if (sg < n_seg && lane == 0) p.seg_above[(int64_t)h * n_seg + sg] = (uint32_t)n_above;
+  }
+  if (n_bin > LH_CAP) return;  // (block-uniform) the long-head kernel reads the scores instead
+  if (lane == 0) s_wn[wave] = w_n;
+  if (wave == 0) {  // the bin's keys in the blocks before this one
+    int x = 0;
+    for (int cc = lane; cc < c; cc += WAVE) x += (int)p.hist[((int64_t)h * nch + cc) * NBINS + (d0 & (NBINS - 1))];
+    x = wave_incl_scan(x);
+    if (lane == WAVE - 1) s_cbase = x;
+  }
+  __syncthreads();
+  int base = s_cbase;
+#pragma unroll
+  for (int w = 0; w < HD_WAVES; ++w) base += w < wave ? s_wn[w] : 0;
+  uint2* out = p.lh_list + (int64_t)h * LH_CAP;
+#pragma unroll
+  for (int u = 0; u < LH_SPW; ++u) {
+    const int i = (sg0 + u) * LH_SEG + 4 * lane;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int j = base + below(m[u][e]);
+      if (((m[u][e] >> lane) & 1u) && j < LH_CAP) out[j] = make_uint2(k[u][e], (uint32_t)(i + e));
+      base += __popcll(m[u][e]);
+    }
+  }
+}
+
+template <int D>
+__global__ __launch_bounds__(HD_THREADS) void evict_long_head(EvictParams p, int reps) {
+  // the head's bin list ((key, position) pairs); after the counts, the
+  // positions of this workgroup's candidate rows
+  __shared__ __attribute__((aligned(16))) uint32_t s_list[2 * LH_CAP];
+  __shared__ __attribute__((aligned(16))) uint32_t s_h1[NBINS + 4];  // second digit; then segment first rows [n_seg + 1]
+  __shared__ __attribute__((aligned(16))) uint32_t s_h2[NBINS / 2];  // third digit
+  __shared__ __attribute__((aligned(16))) uint32_t s_kt[LH_MAX_SEGS];  // per segment: kept above T | tied << 16; then ties before
+  __shared__ uint16_t s_above[LH_MAX_SEGS];  // per segment: keys above the first digit's bin
+  __shared__ int s_wsum[HD_WAVES], s_wsum2[HD_WAVES];
+  __shared__ int s_first, s_last, s_namb;
+  static_assert(LH_SEG <= 0xffff, "segment counts fit 16 bits");
+  constexpr int AMB_CAP = NBINS / 2;  // keys sharing T's bits 31..10, kept in s_h1's space
+  const int h = blockIdx.x % p.Hkv;
+  const int rep = blockIdx.x / p.Hkv;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int n_cand = (int)p.n_cand;
+  const int n_seg = (n_cand + LH_SEG - 1) / LH_SEG;
+  const float* sc = p.scores + (int64_t)h * p.s_hs;
+  const __amdgpu_buffer_rsrc_t rs = tile_rsrc(sc, 4 * n_cand);
+  // 16-byte loads: an aligned head, every segment but a ragged last one
+  const int n_wide = p.vec4 ? (n_cand % LH_SEG == 0 ? n_seg : n_seg - 1) : 0;
+  const uint32_t d0u = (uint32_t)p.lh_state[4 * h + 0];
+  int rank = p.lh_state[4 * h + 1];
+  const int n_bin = p.lh_state[4 * h + 2];
+  const bool use_list = n_bin <= LH_CAP;  // (else the score passes below)
+
+  // Passes over the scores (a bin too large for the list) visit the
+  // segments from a per-workgroup offset on, wrapping round, so that the
+  // workgroups of a head do not all read the same lines at once; wave w
+  // takes the w-th of every HD_WAVES segments in that order.
+  const int s_off = n_seg * rep / reps;  // n_seg <= 2048 and reps < 2^17
+  auto seg_at = [&](int j) { return j + s_off < n_seg ? j + s_off : j + s_off - n_seg; };
+
+  // the segment counts' loads go out first, then the list's (one round:
+  // LH_CAP = 16 * HD_THREADS) once its length is known; the clears run
+  // while they are in flight
+  static_assert(LH_MAX_SEGS == 2 * HD_THREADS, "two segment counts per thread");
+  uint32_t ab[2];
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    const int sg = tid + q * HD_THREADS;
+    ab[q] = sg < n_seg ? p.seg_above[(int64_t)h * n_seg + sg] : 0u;
+  }
+  constexpr int LU = LH_CAP / HD_THREADS;
+  uint2 le[LU];
+  if (use_list) {
+    const uint2* lst = p.lh_list + (int64_t)h * LH_CAP;
+#pragma unroll
+    for (int u = 0; u < LU; ++u) {
+      const int j = tid + u * HD_THREADS;
+      le[u] = j < n_bin ? lst[j] : make_uint2(0u, 0u);
+    }
+  }
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    const int sg = tid + q * HD_THREADS;
+    if (sg < n_seg) s_above[sg] = (uint16_t)ab[q];
+  }
+  for (int i = tid; i < NBINS / 4; i += HD_THREADS) reinterpret_cast<u32x4*>(s_h1)[i] = u32x4{0u, 0u, 0u, 0u};
+  for (int i = tid; i < NBINS / 8; i += HD_THREADS) reinterpret_cast<u32x4*>(s_h2)[i] = u32x4{0u, 0u, 0u, 0u};
+  for (int i = tid; i < LH_MAX_SEGS / 4; i += HD_THREADS) reinterpret_cast<u32x4*>(s_kt)[i] = u32x4{0u, 0u, 0u, 0u};
+  if (tid == 0) {
+    s_first = n_seg;  // (an empty walk unless set below)
+    s_last = -1;
+    s_namb = 0;
+  }
+  __syncthreads();
+
+  // second digit over the bin's keys; the list into LDS
+  if (use_list) {
+#pragma unroll
+    for (int u = 0; u < LU; ++u) {
+      const int j = tid + u * HD_THREADS;
+      if (j < n_bin) {
+        *reinterpret_cast<uint2*>(&s_list[2 * j]) = le[u];
+        atomicAdd(&s_h1[(le[u].x >> 10) & 2047u], 1u);
       }
     }
+  } else {
+    for (int j = wave; j < n_seg; j += HD_WAVES) {
+      float v[4];
+      const int s = seg_at(j);
+      const int i = s * LH_SEG + 4 * lane;
+      lh_load(rs, i, s < n_wide, v);
 #pragma unroll
-    for (int q = 0; q < HD_CP_PASSES; ++q) {
-      const int o = b + q * RPP + rr;
-      if (o < o_hi) {
-        const int64_t dst = (out_row0 + o) * D + part * 8;
-        __builtin_nontemporal_store(kv[q], reinterpret_cast<u32x4*>(p.K_out + dst));
-        __builtin_nontemporal_store(vv[q], reinterpret_cast<u32x4*>(p.V_out + dst));
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t kk = order_key(v[e]);
+        if (i + e < n_cand && (kk >> 21) == d0u) atomicAdd(&s_h1[(kk >> 10) & 2047u], 1u);
       }
     }
   }
+  __syncthreads();
+  int d1, above;
+  hd_find_digit<1>(s_h1, NBINS, rank, d1, above);
+  rank -= above;
+  const uint32_t pre = (d0u << 21) | ((uint32_t)d1 << 10);  // the k-th key's bits 31..10
+
+  // Third digit over the keys with those bits, and the per-segment counts
+  // of kept keys (besides those above the bin) and of ties at T. From the
+  // list: one pass over each thread's run of entries (a segment's keys are
+  // adjacent in the list, so a thread adds once per segment it meets) counts
+  // the keys above T's bits 31..10 and histograms and sets aside the keys
+  // sharing them (few unless very many keys tie); those are sorted out once
+  // T is known. Without the list: two passes over the scores.
+  uint32_t T;
+  int quota;
+  const uint32_t pre10 = pre >> 10;
+  if (use_list) {
+    const int per = (n_bin + HD_THREADS - 1) / HD_THREADS;  // <= LU
+    const int j0 = tid * per, j1 = min(j0 + per, n_bin);
+    uint2* s_amb = reinterpret_cast<uint2*>(s_h1);  // free since the second digit was found
+    int cur = -1;
+    uint32_t acc = 0u;
+#pragma unroll
+    for (int q = 0; q < LU; ++q) {
+      if (j0 + q < j1) {
+        const uint2 e = *reinterpret_cast<const uint2*>(&s_list[2 * (j0 + q)]);
+        const int sg = (int)(e.y / LH_SEG);
+        if (sg != cur) {
+          if (acc) atomicAdd(&s_kt[cur], acc);
+          cur = sg;
+          acc = 0u;
+        }
+        const uint32_t t10 = e.x >> 10;
+        if (t10 > pre10) {
+          ++acc;
+        } else if (t10 == pre10) {
+          atomicAdd(&s_h2[e.x & 1023u], 1u);
+          const int a = atomicAdd(&s_namb, 1);
+          if (a < AMB_CAP) s_amb[a] = e;
+        }
+      }
+    }
+    if (acc) atomicAdd(&s_kt[cur], acc);
+    __syncthreads();
+    int d2;
+    hd_find_digit<1>(s_h2, NBINS / 2, rank, d2, above);
+    T = pre | (uint32_t)d2;
+    quota = rank - above;
+    const int n_amb = s_namb;
+    if (n_amb <= AMB_CAP) {
+      for (int j = tid; j < n_amb; j += HD_THREADS) {
+        const uint2 e = s_amb[j];
+        if (e.x >= T) atomicAdd(&s_kt[e.y / LH_SEG], e.x > T ? 1u : 0x10000u);
+      }
+    } else {
+      for (int j = j0; j < j1; ++j) {
+        const uint2 e = *reinterpret_cast<const uint2*>(&s_list[2 * j]);
+        if ((e.x >> 10) == pre10 && e.x >= T) atomicAdd(&s_kt[e.y / LH_SEG], e.x > T ? 1u : 0x10000u);
+      }
+    }
+  } else {
+    for (int j = wave; j < n_seg; j += HD_WAVES) {
+      float v[4];
+      const int s = seg_at(j);
+      const int i = s * LH_SEG + 4 * lane;
+      lh_load(rs, i, s < n_wide, v);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t kk = order_key(v[e]);
+        if (i + e < n_cand && (kk >> 10) == pre10) atomicAdd(&s_h2[kk & 1023u], 1u);
+      }
+    }
+    __syncthreads();
+    int d2;
+    hd_find_digit<1>(s_h2, NBINS / 2, rank, d2, above);
+    T = pre | (uint32_t)d2;
+    quota = rank - above;
+    for (int j = wave; j < n_seg; j += HD_WAVES) {
+      const int s = seg_at(j);
+      float v[4];
+      const int i = s * LH_SEG + 4 * lane;
+      lh_load(rs, i, s < n_wide, v);
+      int sure = 0, tied = 0;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t kk = order_key(v[e]);
+        const bool ok = i + e < n_cand;
+        sure += __popcll(__ballot(ok && kk > T));
+        tied += __popcll(__ballot(ok && kk == T));
+      }
+      if (lane == 0) {
+        s_kt[s] = (uint32_t)sure | ((uint32_t)tied << 16);
+        s_above[s] = 0;
+      }
+    }
+  }
+  quota = max(quota, 0);  // keys equal to T that are kept, lowest positions first
+  __syncthreads();
+
+  // thread t: segments 2t and 2t + 1. Ties are kept lowest position first,
+  // so the rows before a segment are its sure rows before plus
+  // min(ties before it, quota): one scan of both counts.
+  int sure[2], tied[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int s = 2 * tid + j;
+    const uint32_t kt = s < n_seg ? s_kt[s] : 0u;
+    sure[j] = (s < n_seg ? (int)s_above[s] : 0) + (int)(kt & 0xffffu);
+    tied[j] = (int)(kt >> 16);
+  }
+  const int ss = sure[0] + sure[1], tt = tied[0] + tied[1];
+  const int xs = wave_incl_scan(ss), xt = wave_incl_scan(tt);
+  if (lane == WAVE - 1) {
+    s_wsum[wave] = xs;
+    s_wsum2[wave] = xt;
+  }
+  __syncthreads();
+  int sb = xs - ss, tb = xt - tt;
+#pragma unroll
+  for (int w = 0; w < HD_WAVES; ++w) {
+    sb += w < wave ? s_wsum[w] : 0;
+    tb += w < wave ? s_wsum2[w] : 0;
+  }
+  uint32_t* s_start = s_h1;  // free once the set-aside keys are sorted out
+  uint32_t* s_tb = s_kt;     // each thread overwrites only the entries it read
+  if (2 * tid < n_seg) {
+    s_start[2 * tid] = (uint32_t)(sb + min(tb, quota));
+    s_tb[2 * tid] = (uint32_t)tb;
+  }
+  if (2 * tid + 1 < n_seg) {
+    s_start[2 * tid + 1] = (uint32_t)(sb + sure[0] + min(tb + tied[0], quota));
+    s_tb[2 * tid + 1] = (uint32_t)(tb + tied[0]);
+  }
+  if (2 * tid < n_seg && 2 * tid + 2 >= n_seg) s_start[n_seg] = (uint32_t)(sb + ss + min(tb + tt, quota));
+  __syncthreads();
+
+  // this workgroup's rows: kept candidates in ascending position, then the window
+  const int per_head = (int)p.per_head;
+  const int w_rows = (int)(p.n - p.n_cand);
+  const int cand_rows = per_head - w_rows;
+  const int total = (int)s_start[n_seg];
+  const int o_lo = rep * p.rows_q + min(rep, p.rows_r);
+  const int o_hi = o_lo + p.rows_q + (rep < p.rows_r ? 1 : 0);
+  const int c_hi = min(o_hi, min(total, cand_rows));
+  const bool walk = o_lo < c_hi;
+  // the segments holding rows o_lo and c_hi - 1 (non-empty, so unique)
+  if (walk) {
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int s = 2 * tid + j;
+      if (s < n_seg) {
+        const int st = (int)s_start[s], en = (int)s_start[s + 1];
+        if (st <= o_lo && o_lo < en) s_first = s;
+        if (st < c_hi && c_hi <= en) s_last = s;
+      }
+    }
+  }
+  __syncthreads();
+  int32_t* out = p.kept_idx + (int64_t)h * per_head;
+  uint32_t* s_pos = s_list;  // the list is no longer read
+  if (walk) {
+    const int sf = max(s_first, 0), sl = min(s_last, n_seg - 1);
+    for (int s = sf + wave; s <= sl; s += HD_WAVES) {
+      float v[4];
+      const int i = s * LH_SEG + 4 * lane;
+      lh_load(rs, i, s < n_wide, v);
+      bool gt[4], eq[4], keep[4];
+      int tc = 0;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t kk = order_key(v[e]);
+        const bool ok = i + e < n_cand;
+        gt[e] = ok && kk > T;
+        eq[e] = ok && kk == T;
+        tc += eq[e];
+      }
+      int tr = (int)s_tb[s] + wave_incl_scan(tc) - tc;  // tie rank of the lane's first tie
+      int kc = 0;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        keep[e] = gt[e] || (eq[e] && tr < quota);
+        tr += eq[e];
+        kc += keep[e];
+      }
+      int o = (int)s_start[s] + wave_incl_scan(kc) - kc;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        if (keep[e]) {
+          if (o >= o_lo && o < c_hi) {
+            out[o] = i + e;
+            s_pos[o - o_lo] = (uint32_t)(i + e);
+          }
+          ++o;
+        }
+      }
+    }
+  }
+  // window row j is row total + j
+  const int win_lo = max(o_lo, total), win_hi = min(o_hi, min(total + w_rows, per_head));
+  for (int o = win_lo + tid; o < win_hi; o += HD_THREADS) out[o] = n_cand + (o - total);
+  if (tid == 0 && rep == 0) {
+    p.head_offsets[h] = (int64_t)h * per_head;
+    if (h == 0) p.head_offsets[p.Hkv] = (int64_t)p.Hkv * per_head;
+  }
+  __syncthreads();  // s_pos complete
+  hd_copy_rows<D>(p, h, o_lo, o_hi, min(total, cand_rows), total, s_pos);
 }
 
 // The one-workgroup-per-head path serves per-head top-k budgets (and their
@@ -777,8 +1269,17 @@ bool use_head_path(const kvs_evict_desc& e) {
          (int64_t)e.n_kvheads * e.n_tok < ((int64_t)1 << 31);
 }
 
+// Per-head top-k with HD_MAX < candidates <= LH_MAX per head (and the same
+// row-count limit) takes the long-head path.
+bool use_long_path(const kvs_evict_desc& e) {
+  const int64_t w = e.window < e.n_tok ? e.window : e.n_tok;
+  const int64_t n_cand = e.n_tok - w;
+  return e.k > 0 && e.k < n_cand && e.scope == KVS_SCOPE_HEAD && n_cand > HD_MAX && n_cand <= LH_MAX &&
+         (int64_t)e.n_kvheads * e.n_tok < ((int64_t)1 << 31);
+}
+
 struct WsLayout {
-  size_t hist, blk, state, total;
+  size_t hist, blk, state, list, total;
 };
 
 // Grid path: histograms, block counts, per-head state. The head path uses no
@@ -789,6 +1290,17 @@ WsLayout ws_layout(const kvs_evict_desc& e) {
   const int Hkv = e.n_kvheads;
   if (use_head_path(e)) {
     L.total = 256;
+    return L;
+  }
+  if (use_long_path(e)) {  // block histograms, segment counts, head state, bin lists
+    const int64_t w = e.window < e.n_tok ? e.window : e.n_tok;
+    const int64_t nch = (e.n_tok - w + LH_CHUNK - 1) / LH_CHUNK;
+    const int64_t n_seg = (e.n_tok - w + LH_SEG - 1) / LH_SEG;
+    L.hist = 0;
+    L.blk = al((size_t)Hkv * nch * NBINS * 4);                 // segment counts
+    L.state = L.blk + al((size_t)Hkv * n_seg * 4);             // head state
+    L.list = L.state + al((size_t)Hkv * 16);                   // bin lists
+    L.total = L.list + al((size_t)Hkv * LH_CAP * 8);
     return L;
   }
   const int64_t nb = (e.n_tok + EPB - 1) / EPB;
@@ -878,6 +1390,36 @@ hipError_t launch_evict(const kvs_evict_desc& e, const float* scores, const uint
       hipLaunchKernelGGL(evict_head<128>, dim3((unsigned)blocks), dim3(HD_THREADS), 0, s, p, (int)reps);
     else
       hipLaunchKernelGGL(evict_head<64>, dim3((unsigned)blocks), dim3(HD_THREADS), 0, s, p, (int)reps);
+    return hipGetLastError();
+  }
+
+  if (use_long_path(e)) {
+    p.hist = reinterpret_cast<uint32_t*>(ws + L.hist);
+    p.seg_above = reinterpret_cast<uint32_t*>(ws + L.blk);
+    p.lh_state = reinterpret_cast<int32_t*>(ws + L.state);
+    p.lh_list = reinterpret_cast<uint2*>(ws + L.list);
+    const int nch = (int)((p.n_cand + LH_CHUNK - 1) / LH_CHUNK);
+    p.per_head = p.kprime + (p.n - p.n_cand);
+    p.vec4 = (reinterpret_cast<uintptr_t>(scores) & 15u) == 0 && (p.s_hs & 3) == 0;
+    // workgroups per head: one per LH_ROWS_PER_WG kept rows, at most
+    // HD_MAX_REPS, no more than fill one workgroup per CU over the heads,
+    // and enough that a workgroup's candidate rows fit its position list
+    int64_t reps = (p.per_head + LH_ROWS_PER_WG - 1) / LH_ROWS_PER_WG;
+    const int64_t fill = (256 + p.Hkv - 1) / p.Hkv;
+    reps = reps < fill ? reps : fill;
+    reps = reps < HD_MAX_REPS ? reps : HD_MAX_REPS;
+    const int64_t need = (p.per_head + 2 * LH_CAP - 1) / (2 * LH_CAP);
+    reps = reps > need ? reps : need;
+    reps = reps < 1 ? 1 : reps;
+    p.rows_q = (int32_t)(p.per_head / reps);
+    p.rows_r = (int32_t)(p.per_head % reps);
+    hipLaunchKernelGGL(evict_lh_hist, dim3((unsigned)(p.Hkv * nch)), dim3(HD_THREADS), 0, s, p, nch);
+    hipLaunchKernelGGL(evict_lh_bin, dim3((unsigned)(p.Hkv * nch)), dim3(HD_THREADS), 0, s, p, nch);
+    const unsigned blocks = (unsigned)(p.Hkv * reps);  // Hkv * n < 2^31, so Hkv * reps < 2^17
+    if (p.D == 128)
+      hipLaunchKernelGGL(evict_long_head<128>, dim3(blocks), dim3(HD_THREADS), 0, s, p, (int)reps);
+    else
+      hipLaunchKernelGGL(evict_long_head<64>, dim3(blocks), dim3(HD_THREADS), 0, s, p, (int)reps);
     return hipGetLastError();
   }
 

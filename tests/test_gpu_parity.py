@@ -260,8 +260,9 @@ EVICT_CASES = [
     ("tau-zero", 2, 3000, 64, 8, None, 0.0),
     ("tau-inf", 2, 3000, 128, 8, None, float("inf")),
     ("empty", 2, 0, 128, 8, 5, None),
-    # grid path: thresholds, and per-head top-k above 16384 candidates per
-    # head; at most 16384, one workgroup per head selects in LDS
+    # grid path: thresholds, layer budgets and heads past the long-head
+    # path; per-head top-k with at most 16384 candidates per head: one
+    # workgroup per head selects in LDS; above that, the long-head path
     ("many-heads-topk", 4097, 100, 64, 10, 30, None),
     ("many-heads-tau", 300, 700, 64, 16, None, float(np.exp(-6.0))),
     ("long-heads-topk", 2, 140000, 64, 128, 35000, None),
@@ -289,6 +290,17 @@ EVICT_CASES = [
     ("topk-write-copies-rows", 4, 5000, 64, 8, 20, None),
     ("tau-write-copies-rows", 2, 100, 64, 4, None, float(np.exp(-6.0))),
     ("long-heads-tau", 2, 140000, 64, 128, None, float(np.exp(-6.0))),
+    # long-head path (per-head top-k, 16384 < candidates <= 524288): candidates
+    # ending off a 4-key boundary, a wide window, top-1 and k = candidates - 1,
+    # a head count that is not a multiple of 8, the largest such head and
+    # one past it (grid path)
+    ("long-topk-ragged-tail", 3, 70001, 128, 0, 20000, None),
+    ("long-topk-wide-window", 2, 40000, 64, 20000, 10000, None),
+    ("long-topk-top1", 2, 30000, 64, 5, 1, None),
+    ("long-topk-cand-minus-1", 2, 30000, 64, 5, 29994, None),
+    ("long-topk-12-heads", 12, 20000, 128, 64, 5000, None),
+    ("long-topk-largest", 1, 524288 + 128, 64, 128, 100000, None),
+    ("long-topk-past-largest", 1, 524289 + 128, 64, 128, 100000, None),
 ]
 
 
@@ -373,6 +385,23 @@ def test_evict_parity(name, Hkv, n, D, window, k, tau):
     _check_evict_exact(name, s, K, V, window, k, tau, kept, offs, Ko, Vo)
 
 
+def test_evict_long_head_strided_scores():
+    """Long-head top-k reading its scores through a head stride that is not a
+    multiple of 4 from a base that is not 16-byte aligned (element loads
+    instead of 16-byte loads): exactly the oracle's selection."""
+    Hkv, n, D, window, k = 3, 30001, 64, 17, 9000
+    s, K, V = _evict_case(831, Hkv, n, D)
+    _evict_special_scores(s)
+    wide = np.zeros((Hkv, n + 2), dtype=np.float32)
+    wide[:, 1:n + 1] = s
+    sd = dev_f32(wide)[:, 1:n + 1]
+    assert sd.stride(0) % 4 != 0 and sd.data_ptr() % 16 != 0
+    say("[evict] long-head strided scores")
+    kept, offs, Ko, Vo = kvs.evict(sd, dev_bf16(K), dev_bf16(V), window=window, k=k)
+    torch.cuda.synchronize()
+    _check_evict_exact("long-head-strided", s, K, V, window, k, None, kept, offs, Ko, Vo)
+
+
 def test_evict_reuses_one_workspace():
     """One workspace (left uninitialised) through a sequence of calls of
     every mode and of different shapes (more blocks, then fewer): each call
@@ -385,6 +414,8 @@ def test_evict_reuses_one_workspace():
         ("window-only", 2, 3000, 128, 16, 0, None),
         ("tau-fewer-blocks", 2, 700, 128, 16, None, float(np.exp(-6.0))),
         ("keep-all", 3, 2000, 128, 16, 10 ** 6, None),
+        ("long-topk", 2, 40000, 64, 64, 9000, None),
+        ("long-topk-shorter", 2, 20000, 128, 64, 3000, None),
         ("tau-last", 4, 9000, 128, 128, None, float(np.exp(-7.0))),
     ]
     cases = []
