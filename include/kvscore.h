@@ -230,8 +230,11 @@ int kv_evict(const kvs_evict_desc* e, const float* scores, const kvs_bf16* K,
  * inputs, outputs, checks and results as kv_evict (it runs the same
  * kernels); the workspace kv_evict would take is instead a fixed device
  * array inside the library, KVS_EVICT_NOALLOC_MAX_WORKSPACE bytes, one copy
- * per GPU, held until the process ends. A layer whose
- * kv_evict_workspace_bytes(e) exceeds that returns KVS_EWORKSPACE (nothing
+ * per GPU, held until the process ends. Per-head top-k over more than 16,384
+ * candidates per head, whose fastest kernels need more workspace
+ * (kv_evict_workspace_bytes(e)) than that array holds, takes the smaller
+ * histogram-pass selection here instead (the same results). A layer whose
+ * smallest workspace still exceeds the array returns KVS_EWORKSPACE (nothing
  * is launched). The first call on a device looks up that device's copy
  * (no allocation); no call allocates, frees or synchronises.
  * Every call on one GPU shares that GPU's array: calls ordered on one

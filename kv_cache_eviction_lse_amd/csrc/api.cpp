@@ -395,7 +395,7 @@ KVS_API int kv_evict(const kvs_evict_desc* e, const float* scores, const kvs_bf1
   int cus;
   if ((st = check_device(&cus))) return st;
   return hip_status(kvs::launch_evict(*e, scores, K, V, kept_idx, head_offsets, K_out, V_out, workspace,
-                                      static_cast<hipStream_t>(stream)),
+                                      workspace_bytes, static_cast<hipStream_t>(stream)),
                     "kv_evict");
 }
 
@@ -404,7 +404,7 @@ KVS_API int kv_evict_noalloc(const kvs_evict_desc* e, const float* scores, const
                              void* stream) {
   int st = check_evict_call(e, scores, K, V, kept_idx, head_offsets, K_out, V_out);
   if (st) return st;
-  const size_t ws = kvs::evict_workspace_bytes(*e);
+  const size_t ws = kvs::evict_workspace_bytes(*e, kvs::EVICT_SCRATCH_BYTES);
   static_assert(kvs::EVICT_SCRATCH_BYTES == KVS_EVICT_NOALLOC_MAX_WORKSPACE, "header and library disagree");
   if (ws > kvs::EVICT_SCRATCH_BYTES)
     return fail(KVS_EWORKSPACE, "this layer needs %zu bytes of workspace, above the %zu-byte built-in scratch of "
@@ -415,6 +415,6 @@ KVS_API int kv_evict_noalloc(const kvs_evict_desc* e, const float* scores, const
   st = hip_status(kvs::evict_scratch(dev, &ws_dev), "kv_evict_noalloc: scratch lookup");
   if (st) return st;
   return hip_status(kvs::launch_evict(*e, scores, K, V, kept_idx, head_offsets, K_out, V_out, ws_dev,
-                                      static_cast<hipStream_t>(stream)),
+                                      kvs::EVICT_SCRATCH_BYTES, static_cast<hipStream_t>(stream)),
                     "kv_evict_noalloc");
 }

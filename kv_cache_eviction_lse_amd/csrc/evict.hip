@@ -1280,11 +1280,15 @@ bool use_long_path(const kvs_evict_desc& e) {
 
 struct WsLayout {
   size_t hist, blk, state, list, total;
+  bool long_head;  // the long-head path's layout
 };
 
 // Grid path: histograms, block counts, per-head state. The head path uses no
 // workspace (its state lives in LDS; it writes the kept indices directly).
-WsLayout ws_layout(const kvs_evict_desc& e) {
+// The long-head path's workspace (block histograms, segment counts, bin
+// lists) is larger than the grid path's: it is taken when it fits `budget`
+// bytes, else the grid path serves those heads too (the same selection).
+WsLayout ws_layout(const kvs_evict_desc& e, size_t budget) {
   auto al = [](size_t x) { return (x + 255) & ~(size_t)255; };
   WsLayout L{};
   const int Hkv = e.n_kvheads;
@@ -1301,7 +1305,9 @@ WsLayout ws_layout(const kvs_evict_desc& e) {
     L.state = L.blk + al((size_t)Hkv * n_seg * 4);             // head state
     L.list = L.state + al((size_t)Hkv * 16);                   // bin lists
     L.total = L.list + al((size_t)Hkv * LH_CAP * 8);
-    return L;
+    L.long_head = true;
+    if (L.total <= budget) return L;
+    L = WsLayout{};
   }
   const int64_t nb = (e.n_tok + EPB - 1) / EPB;
   L.hist = 0;
@@ -1339,11 +1345,11 @@ hipError_t evict_scratch(int dev, void** ptr) {
   return hipSuccess;
 }
 
-size_t evict_workspace_bytes(const kvs_evict_desc& e) { return ws_layout(e).total; }
+size_t evict_workspace_bytes(const kvs_evict_desc& e, size_t budget) { return ws_layout(e, budget).total; }
 
 hipError_t launch_evict(const kvs_evict_desc& e, const float* scores, const uint16_t* K, const uint16_t* V,
                         int32_t* kept_idx, int64_t* head_offsets, uint16_t* K_out, uint16_t* V_out,
-                        void* workspace, hipStream_t s) {
+                        void* workspace, size_t workspace_bytes, hipStream_t s) {
   EvictParams p{};
   p.scores = scores;
   p.s_hs = e.score_head_stride;
@@ -1370,7 +1376,7 @@ hipError_t launch_evict(const kvs_evict_desc& e, const float* scores, const uint
     p.kprime = e.k < cand ? e.k : cand;
     p.mode = p.kprime == 0 ? MODE_WINDOW : (p.kprime == cand ? MODE_ALL : MODE_TOPK);
   }
-  const WsLayout L = ws_layout(e);
+  const WsLayout L = ws_layout(e, workspace_bytes);
   char* ws = static_cast<char*>(workspace);
 
   if (use_head_path(e)) {
@@ -1393,7 +1399,7 @@ hipError_t launch_evict(const kvs_evict_desc& e, const float* scores, const uint
     return hipGetLastError();
   }
 
-  if (use_long_path(e)) {
+  if (L.long_head) {
     p.hist = reinterpret_cast<uint32_t*>(ws + L.hist);
     p.seg_above = reinterpret_cast<uint32_t*>(ws + L.blk);
     p.lh_state = reinterpret_cast<int32_t*>(ws + L.state);

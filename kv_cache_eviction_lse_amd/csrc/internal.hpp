@@ -34,7 +34,11 @@ hipError_t launch_stream_append(const kvs_stream_desc& d, const float* new_score
                                 const uint16_t* V_new, uint16_t* K_cache, uint16_t* V_cache, int32_t* pos_cache,
                                 float* win_scores, int64_t* head_len, hipStream_t s);
 
-size_t evict_workspace_bytes(const kvs_evict_desc& e);
+// Workspace of the eviction path the layer takes when `budget` bytes are
+// available (long heads take the grid path when the long-head path's larger
+// workspace does not fit); launch_evict chooses the same way from its
+// workspace_bytes.
+size_t evict_workspace_bytes(const kvs_evict_desc& e, size_t budget = ~(size_t)0);
 
 // kv_evict_noalloc's workspace: a device array of EVICT_SCRATCH_BYTES per
 // GPU. evict_scratch() returns its device address on device `dev`, which
@@ -45,6 +49,6 @@ hipError_t evict_scratch(int dev, void** ptr);
 
 hipError_t launch_evict(const kvs_evict_desc& e, const float* scores, const uint16_t* K, const uint16_t* V,
                         int32_t* kept_idx, int64_t* head_offsets, uint16_t* K_out, uint16_t* V_out,
-                        void* workspace, hipStream_t s);
+                        void* workspace, size_t workspace_bytes, hipStream_t s);
 
 }  // namespace kvs

@@ -67,6 +67,28 @@ def test_noalloc_equals_evict_on_two_calls(name, first, second, sel):
         assert tot > 0
 
 
+def test_noalloc_long_heads_past_its_scratch_take_the_grid_selection():
+    """Per-head top-k on 20 KV heads of 120,000 tokens: kv_evict's long-head
+    kernels need more workspace than the scratch holds, so kv_evict_noalloc
+    selects with the grid's histogram passes instead. Both are exact: the
+    outputs must still be identical, on two calls in a row (the second on a
+    smaller layer that takes the long-head kernels inside the scratch)."""
+    for i, (Hkv, n) in enumerate(((20, 120000), (4, 30000))):
+        say(f"[noalloc] long heads call {i}: Hkv={Hkv} n={n}")
+        g = torch.Generator(device="cuda")
+        g.manual_seed(500 + i)
+        s = torch.rand((Hkv, n), device="cuda", generator=g)
+        K = torch.randn((Hkv, n, 64), device="cuda", generator=g).to(torch.bfloat16)
+        V = torch.randn((Hkv, n, 64), device="cuda", generator=g).to(torch.bfloat16)
+        e = kvs.evict_desc(s, K, window=128, k=n // 4)
+        assert (kvs.evict_workspace_bytes(e) > kvs.EVICT_NOALLOC_MAX_WORKSPACE) == (i == 0)
+        ref = kvs.evict(s, K, V, window=128, k=n // 4, outputs=_outs(e))
+        got = kvs.evict_noalloc(s, K, V, window=128, k=n // 4, outputs=_outs(e))
+        torch.cuda.synchronize()
+        assert _same(got, ref, f"long heads call {i}") == Hkv * (n // 4 + 128)
+        del s, K, V, ref, got
+
+
 def test_noalloc_rejects_layers_past_its_scratch():
     Hkv, n = 300, 1000  # threshold mode: the grid path, 24 KiB of histograms per head
     s = torch.zeros((Hkv, n), dtype=torch.float32, device="cuda")
