@@ -486,6 +486,48 @@ def test_evict_random_sweep(i):
     assert np.array_equal(host_bits(Ko)[:total], Kr) and np.array_equal(host_bits(Vo)[:total], Vr), name
 
 
+def _long_sweep_case(i):
+    """Seeded random per-head top-k layer i with 16,385-200,000 candidates per
+    head (the long-head path): 1-12 heads, D = 64/128, windows up to 2048,
+    k from 1 to all but one candidate, and log-normal (with ties and zeros),
+    one-octave, three-valued or rounded-normal scores (the latter two give
+    first-digit bins too large for the key list)."""
+    rng = np.random.default_rng(9150 + i)
+    Hkv = int(rng.integers(1, 13))
+    n = int(np.exp(rng.uniform(np.log(16500.0), np.log(200000.0))))
+    n = min(n, 600000 // Hkv)
+    D = int(rng.choice([64, 128]))
+    window = int(rng.integers(0, 2049))
+    cand = n - window
+    if cand <= 16384:
+        window, cand = 0, n
+    k = int(rng.integers(1, cand))
+    law = str(rng.choice(["lognormal", "lognormal", "octave", "three", "rounded"]))
+    if law == "lognormal":
+        sc = synth.evict_scores(9600 + i, Hkv, n, tie_frac=float(rng.uniform(0, 0.3)), zero_frac=0.02)
+    elif law == "octave":
+        sc = (0.5 + 0.5 * rng.random((Hkv, n))).astype(np.float32)
+    elif law == "three":
+        sc = rng.choice(np.array([0.1, 0.2, 0.3], dtype=np.float32), size=(Hkv, n))
+    else:
+        sc = np.round(rng.standard_normal((Hkv, n)), 2).astype(np.float32)
+    return Hkv, n, D, window, law, sc, k
+
+
+@pytest.mark.parametrize("i", range(16))
+def test_evict_long_head_sweep(i):
+    """Sixteen seeded random layers through the long-head top-k path: exactly
+    the oracle's selection and compaction."""
+    Hkv, n, D, window, law, sc, k = _long_sweep_case(i)
+    K = synth.normal_bf16(9700 + i, 90, (Hkv, n, D))
+    V = synth.normal_bf16(9700 + i, 91, (Hkv, n, D))
+    name = f"long-sweep-{i} Hkv={Hkv} n={n} D={D} w={window} {law} k={k}"
+    say(f"[evict] {name}")
+    kept, offs, Ko, Vo = kvs.evict(dev_f32(sc), dev_bf16(K), dev_bf16(V), window=window, k=k)
+    torch.cuda.synchronize()
+    _check_evict_exact(name, sc, K, V, window, k, None, kept, offs, Ko, Vo)
+
+
 LAYER_CASES = [
     # name, Hkv, n, D, window, k (one budget for the layer), identical heads
     ("layer-multiblock", 4, 5000, 128, 128, 3000, False),
