@@ -415,22 +415,24 @@ __global__ __launch_bounds__(EV_THREADS) void evict_write_fused(EvictParams p) {
   write_block(p, h, b, (uint32_t)p.state[h * 4 + 0], s_quota, s_start + t_sb + min(t_tb, s_quota), t_tb);
 }
 
-// Coalesced copy of the kept K and V rows: GROWS output rows per block, D/8
-// lanes per row with 16 bytes each; all loads of a block's rows are issued
-// before the stores. Rows past the total (known only on the device in
-// threshold mode) are skipped.
-constexpr int GROWS = 32;
+// Coalesced copy of the kept K and V rows: GROWS output rows per block of
+// GT threads, D/8 lanes per row with 16 bytes each; all loads of a block's
+// rows are issued before the stores. Rows past the total (known only on the
+// device in threshold mode) are skipped. Small blocks (many resident per CU)
+// measured fastest: 128 threads and 16 rows against 256 and 32, 64 or more.
+constexpr int GROWS = 16;
+constexpr int GT = 128;
 constexpr int MAX_LDS_HEADS = 256;
 
 template <int D>
-__global__ __launch_bounds__(EV_THREADS) void evict_gather(EvictParams p) {
+__global__ __launch_bounds__(GT) void evict_gather(EvictParams p) {
   __shared__ int64_t s_off[MAX_LDS_HEADS + 1];
   const int64_t total = p.head_offsets[p.Hkv];
   const int64_t r0 = (int64_t)blockIdx.x * GROWS;
   if (r0 >= total) return;
   const bool lds_heads = p.Hkv <= MAX_LDS_HEADS;
   if (lds_heads)
-    for (int k = threadIdx.x; k <= p.Hkv; k += EV_THREADS) s_off[k] = p.head_offsets[k];
+    for (int k = threadIdx.x; k <= p.Hkv; k += GT) s_off[k] = p.head_offsets[k];
   __syncthreads();
   auto head_of = [&](int64_t r) {  // last h with offset[h] <= r
     int lo = 0, hi = p.Hkv - 1;
@@ -442,8 +444,9 @@ __global__ __launch_bounds__(EV_THREADS) void evict_gather(EvictParams p) {
     return lo;
   };
   constexpr int LPR = D / 8;
-  constexpr int RPP = EV_THREADS / LPR;  // rows per pass
+  constexpr int RPP = GT / LPR;  // rows per pass
   constexpr int PASSES = GROWS / RPP;
+  static_assert(PASSES >= 1 && PASSES * RPP == GROWS, "a block's rows are whole passes");
   const int part = threadIdx.x % LPR;
   const int rr = threadIdx.x / LPR;
   u32x4 kv[PASSES], vv[PASSES];
@@ -1455,9 +1458,9 @@ hipError_t launch_evict(const kvs_evict_desc& e, const float* scores, const uint
   if (cap_rows > 0 && p.nb > 0) {
     const int64_t gblocks = (cap_rows + GROWS - 1) / GROWS;
     if (p.D == 128)
-      hipLaunchKernelGGL(evict_gather<128>, dim3((unsigned)gblocks), dim3(EV_THREADS), 0, s, p);
+      hipLaunchKernelGGL(evict_gather<128>, dim3((unsigned)gblocks), dim3(GT), 0, s, p);
     else
-      hipLaunchKernelGGL(evict_gather<64>, dim3((unsigned)gblocks), dim3(EV_THREADS), 0, s, p);
+      hipLaunchKernelGGL(evict_gather<64>, dim3((unsigned)gblocks), dim3(GT), 0, s, p);
   }
   return hipGetLastError();
 }
