@@ -40,7 +40,7 @@ namespace kvs {
 namespace {
 
 constexpr int EV_THREADS = 256;
-constexpr int EV_PER_THREAD = 8;
+constexpr int EV_PER_THREAD = 4;  // 1024-key blocks: twice the blocks of 2048 measured faster on the count and write passes
 constexpr int EPB = EV_THREADS * EV_PER_THREAD;  // keys per block
 constexpr int NBINS = 2048;
 
