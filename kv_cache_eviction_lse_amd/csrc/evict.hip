@@ -12,6 +12,12 @@
 //   candidates per head: evict_head, a few workgroups per head, each of
 //   which selects in LDS and then writes and copies its share of the head's
 //   kept rows. One launch.
+//   per-head top-k with HD_MAX < candidates <= LH_MAX per head, when its
+//   workspace fits: evict_lh_hist (first-digit histograms per chunk),
+//   evict_lh_bin (the k-th key's first digit, per-segment counts and the
+//   digit's keys listed per head), evict_long_head (workgroups per head that
+//   finish the selection from the list, write and copy their rows). Three
+//   launches; see the long-heads section.
 //   Otherwise (thresholds, layer budgets, longer heads), one grid of blocks
 //   of EPB keys per head, unless noted:
 //   top-k: evict_zero, then three radix-digit histogram passes over the
