@@ -905,7 +905,7 @@ __global__ __launch_bounds__(HD_THREADS) void evict_lh_bin(EvictParams p, int nc
   }
   // first digit: thread t sums digits 2 * (HD_THREADS - 1 - t) and + 1 over
   // the head's block histograms (descending digit order over the threads)
-  int c_low = 0, c_top = 0;
+  int c_low = 0, c_top = 0, b_low = 0, b_top = 0;  // (b_*: the chunks before this one)
   {
     const uint32_t* g = p.hist + (int64_t)h * nch * NBINS + 2 * (HD_THREADS - 1 - tid);
 #pragma unroll 8
@@ -913,10 +913,13 @@ __global__ __launch_bounds__(HD_THREADS) void evict_lh_bin(EvictParams p, int nc
       const uint2 x = *reinterpret_cast<const uint2*>(g + (int64_t)cc * NBINS);
       c_low += (int)x.x;
       c_top += (int)x.y;
+      b_low += cc < c ? (int)x.x : 0;
+      b_top += cc < c ? (int)x.y : 0;
     }
   }
+  if (tid == 0) s_cbase = 0;  // (set below by the thread that summed the k-th key's digit)
   int d0, above, n_bin;
-  hd_find_core(c_top, c_low, 2, (int)p.kprime, d0, above, n_bin);
+  hd_find_core(c_top, c_low, 2, (int)p.kprime, d0, above, n_bin);  // (its barriers order the store above)
   if (c == 0 && tid == 0) {
     p.lh_state[4 * h + 0] = d0;
     p.lh_state[4 * h + 1] = (int)p.kprime - above;  // rank of the k-th key inside the bin
@@ -943,12 +946,10 @@ __global__ __launch_bounds__(HD_THREADS) void evict_lh_bin(EvictParams p, int nc
   }
   if (n_bin > LH_CAP) return;  // (block-uniform) the long-head kernel reads the scores instead
   if (lane == 0) s_wn[wave] = w_n;
-  if (wave == 0) {  // the bin's keys in the blocks before this one
-    int x = 0;
-    for (int cc = lane; cc < c; cc += WAVE) x += (int)p.hist[((int64_t)h * nch + cc) * NBINS + (d0 & (NBINS - 1))];
-    x = wave_incl_scan(x);
-    if (lane == WAVE - 1) s_cbase = x;
-  }
+  // the bin's keys in the chunks before this one: from the thread that summed d0
+  const int lo = 2 * (HD_THREADS - 1 - tid);
+  if (d0 == lo) s_cbase = b_low;
+  if (d0 == lo + 1) s_cbase = b_top;
   __syncthreads();
   int base = s_cbase;
 #pragma unroll
@@ -960,7 +961,7 @@ __global__ __launch_bounds__(HD_THREADS) void evict_lh_bin(EvictParams p, int nc
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int j = base + below(m[u][e]);
-      if (((m[u][e] >> lane) & 1u) && j < LH_CAP) out[j] = make_uint2(k[u][e], (uint32_t)(i + e));
+      if (((m[u][e] >> lane) & 1u) && j >= 0 && j < LH_CAP) out[j] = make_uint2(k[u][e], (uint32_t)(i + e));
       base += __popcll(m[u][e]);
     }
   }
