@@ -19,7 +19,7 @@
 //   finish the selection from the list, write and copy their rows). Three
 //   launches; see the long-heads section.
 //   Otherwise (thresholds, layer budgets, longer heads), one grid of blocks
-//   of EPB keys per head, unless noted:
+//   of 1024 or 2048 keys per head (GRID_SMALL), unless noted:
 //   top-k: evict_zero, then three radix-digit histogram passes over the
 //     order-preserving 32-bit keys of the candidate scores (bits 31..21,
 //     20..10, 9..0). Each pass re-derives, from the previous passes'
@@ -46,8 +46,14 @@ namespace kvs {
 namespace {
 
 constexpr int EV_THREADS = 256;
-constexpr int EV_PER_THREAD = 4;  // 1024-key blocks: twice the blocks of 2048 measured faster on the count and write passes
-constexpr int EPB = EV_THREADS * EV_PER_THREAD;  // keys per block
+// Keys per thread (PER) and per block (EV_THREADS * PER) of the grid kernels:
+// 8 (2048-key blocks), or 4 (1024-key blocks) for layers that would have at
+// most GRID_SMALL blocks of 2048 keys, where twice the blocks measured faster
+// (32k threshold layer 58.0-58.6 -> 56.3-56.5 us); on larger layers the
+// write pass's reduction of every (head, block) count grows with the square
+// of the blocks (120k layer budget 87 -> 103 us with 1024-key blocks).
+constexpr int GRID_SMALL = 256;
+__host__ __device__ constexpr int epb_of(int per) { return EV_THREADS * per; }
 constexpr int NBINS = 2048;
 
 enum Mode : int { MODE_TOPK = 0, MODE_TAU = 1, MODE_ALL = 2, MODE_WINDOW = 3 };
@@ -168,7 +174,7 @@ __global__ void evict_zero(uint32_t* p, int64_t n) {
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride) p[i] = 0u;
 }
 
-template <int PASS>
+template <int PASS, int PER>
 __global__ __launch_bounds__(EV_THREADS) void evict_hist(EvictParams p) {
   __shared__ uint32_t s_hist[NBINS];
   const int h = blockIdx.y, b = blockIdx.x;
@@ -179,10 +185,10 @@ __global__ __launch_bounds__(EV_THREADS) void evict_hist(EvictParams p) {
   if (PASS > 0) radix_state(p, hh, PASS, prefix, above, rank);
   __syncthreads();
   const int hs = PASS > 0 ? digit_shift(PASS - 1) : 32;
-  const int64_t i0 = (int64_t)b * EPB + threadIdx.x * EV_PER_THREAD;
+  const int64_t i0 = (int64_t)b * epb_of(PER) + threadIdx.x * PER;
   const float* sc = p.scores + (int64_t)h * p.s_hs;
 #pragma unroll
-  for (int e = 0; e < EV_PER_THREAD; ++e) {
+  for (int e = 0; e < PER; ++e) {
     const int64_t i = i0 + e;
     if (i < p.n_cand) {
       const uint32_t u = order_key(sc[i]);
@@ -210,6 +216,7 @@ __device__ __forceinline__ int keep_class(const EvictParams& p, int64_t i, float
   }
 }
 
+template <int PER>
 __global__ __launch_bounds__(EV_THREADS) void evict_count(EvictParams p) {
   const int h = blockIdx.y, b = blockIdx.x;
   uint32_t T = 0;
@@ -225,11 +232,11 @@ __global__ __launch_bounds__(EV_THREADS) void evict_count(EvictParams p) {
     p.state[h * 4 + 0] = (int32_t)T;
     p.state[h * 4 + 1] = quota;
   }
-  const int64_t i0 = (int64_t)b * EPB + threadIdx.x * EV_PER_THREAD;
+  const int64_t i0 = (int64_t)b * epb_of(PER) + threadIdx.x * PER;
   const float* sc = p.scores + (int64_t)h * p.s_hs;
   int sure = 0, tied = 0;
 #pragma unroll
-  for (int e = 0; e < EV_PER_THREAD; ++e) {
+  for (int e = 0; e < PER; ++e) {
     const int64_t i = i0 + e;
     if (i < p.n) {
       const int c = keep_class(p, i, i < p.n_cand ? sc[i] : 0.f, T);
@@ -296,14 +303,15 @@ __device__ __forceinline__ int64_t head_start(const EvictParams& p, int h) {
 
 // Predicate, tie ranks, positions and the kept indices of one block of keys,
 // given the block's first output row and the head's ties before the block.
+template <int PER>
 __device__ void write_block(const EvictParams& p, int h, int b, uint32_t T, int quota, int64_t out0,
                             int ties_before) {
-  const int64_t i0 = (int64_t)b * EPB + threadIdx.x * EV_PER_THREAD;
+  const int64_t i0 = (int64_t)b * epb_of(PER) + threadIdx.x * PER;
   const float* sc = p.scores + (int64_t)h * p.s_hs;
-  int cls[EV_PER_THREAD];
+  int cls[PER];
   int tied = 0;
 #pragma unroll
-  for (int k = 0; k < EV_PER_THREAD; ++k) {
+  for (int k = 0; k < PER; ++k) {
     const int64_t i = i0 + k;
     cls[k] = i < p.n ? keep_class(p, i, i < p.n_cand ? sc[i] : 0.f, T) : 0;
     tied += cls[k] == 1;
@@ -312,7 +320,7 @@ __device__ void write_block(const EvictParams& p, int h, int b, uint32_t T, int 
   int tie_rank = ties_before + block_exclusive_scan(tied, &tot);
   int keep = 0;
 #pragma unroll
-  for (int k = 0; k < EV_PER_THREAD; ++k) {
+  for (int k = 0; k < PER; ++k) {
     if (cls[k] == 1) {
       cls[k] = tie_rank < quota ? 2 : 0;
       ++tie_rank;
@@ -322,13 +330,14 @@ __device__ void write_block(const EvictParams& p, int h, int b, uint32_t T, int 
   int n_keep;
   int pos = block_exclusive_scan(keep, &n_keep);
 #pragma unroll
-  for (int k = 0; k < EV_PER_THREAD; ++k) {
+  for (int k = 0; k < PER; ++k) {
     if (cls[k] == 2) p.kept_idx[out0 + pos++] = (int32_t)(i0 + k);
   }
 }
 
 // After evict_scan: block offsets and head totals are in the workspace.
 // Block (0, 0) also writes the per-head offsets.
+template <int PER>
 __global__ __launch_bounds__(EV_THREADS) void evict_write(EvictParams p) {
   const int h = blockIdx.y, b = blockIdx.x;
   if (b == 0 && h == 0) {
@@ -336,7 +345,7 @@ __global__ __launch_bounds__(EV_THREADS) void evict_write(EvictParams p) {
   }
   if (p.nb == 0) return;  // no keys: only the (zero) offsets
   const int32_t* e = p.blk + ((int64_t)h * p.nb + b) * 4;
-  write_block(p, h, b, (uint32_t)p.state[h * 4 + 0], p.state[h * 4 + 1], head_start(p, h) + e[2], e[3]);
+  write_block<PER>(p, h, b, (uint32_t)p.state[h * 4 + 0], p.state[h * 4 + 1], head_start(p, h) + e[2], e[3]);
 }
 
 // Scan and write in one launch, for layers with at most FUSED_HEADS heads and
@@ -348,6 +357,7 @@ constexpr int FUSED_HEADS = 1024;
 constexpr int FUSED_ENTRIES = 8192;
 constexpr int HPT = FUSED_HEADS / EV_THREADS;  // heads per thread in the head scans
 
+template <int PER>
 __global__ __launch_bounds__(EV_THREADS) void evict_write_fused(EvictParams p) {
   __shared__ int s_sure[FUSED_HEADS], s_tied[FUSED_HEADS];
   __shared__ int64_t s_start;
@@ -418,7 +428,7 @@ __global__ __launch_bounds__(EV_THREADS) void evict_write_fused(EvictParams p) {
   if (b == 0 && h == 0 && tid == 0) p.head_offsets[p.Hkv] = tot_rows;
   __syncthreads();
   if (p.nb == 0) return;
-  write_block(p, h, b, (uint32_t)p.state[h * 4 + 0], s_quota, s_start + t_sb + min(t_tb, s_quota), t_tb);
+  write_block<PER>(p, h, b, (uint32_t)p.state[h * 4 + 0], s_quota, s_start + t_sb + min(t_tb, s_quota), t_tb);
 }
 
 // Coalesced copy of the kept K and V rows: GROWS output rows per block of
@@ -1288,6 +1298,12 @@ bool use_long_path(const kvs_evict_desc& e) {
          (int64_t)e.n_kvheads * e.n_tok < ((int64_t)1 << 31);
 }
 
+// Keys per thread of the grid kernels for this layer (see GRID_SMALL).
+int grid_per(const kvs_evict_desc& e) {
+  const int64_t nb2 = (e.n_tok + epb_of(8) - 1) / epb_of(8);
+  return (int64_t)e.n_kvheads * nb2 <= GRID_SMALL ? 4 : 8;
+}
+
 struct WsLayout {
   size_t hist, blk, state, list, total;
   bool long_head;  // the long-head path's layout
@@ -1319,7 +1335,7 @@ WsLayout ws_layout(const kvs_evict_desc& e, size_t budget) {
     if (L.total <= budget) return L;
     L = WsLayout{};
   }
-  const int64_t nb = (e.n_tok + EPB - 1) / EPB;
+  const int64_t nb = (e.n_tok + epb_of(grid_per(e)) - 1) / epb_of(grid_per(e));
   L.hist = 0;
   L.blk = al((size_t)3 * Hkv * NBINS * 4);
   L.state = L.blk + al((size_t)Hkv * (nb > 0 ? nb : 1) * 16);
@@ -1376,7 +1392,8 @@ hipError_t launch_evict(const kvs_evict_desc& e, const float* scores, const uint
   p.n = e.n_tok;
   const int64_t w = e.window < e.n_tok ? e.window : e.n_tok;
   p.n_cand = e.n_tok - w;
-  p.nb = (int)((e.n_tok + EPB - 1) / EPB);
+  const int per = grid_per(e);
+  p.nb = (int)((e.n_tok + epb_of(per) - 1) / epb_of(per));
   p.tau = e.tau;
   p.layer = e.scope == KVS_SCOPE_LAYER && e.k >= 0;
   if (e.k < 0) {
@@ -1447,19 +1464,36 @@ hipError_t launch_evict(const kvs_evict_desc& e, const float* scores, const uint
   hipError_t err;
   if (p.mode == MODE_TOPK) {
     hipLaunchKernelGGL(evict_zero, dim3(64), dim3(256), 0, s, p.hist, (int64_t)3 * p.Hkv * NBINS);
-    hipLaunchKernelGGL(evict_hist<0>, grid, dim3(EV_THREADS), 0, s, p);
-    hipLaunchKernelGGL(evict_hist<1>, grid, dim3(EV_THREADS), 0, s, p);
-    hipLaunchKernelGGL(evict_hist<2>, grid, dim3(EV_THREADS), 0, s, p);
+    if (per == 4) {
+      hipLaunchKernelGGL((evict_hist<0, 4>), grid, dim3(EV_THREADS), 0, s, p);
+      hipLaunchKernelGGL((evict_hist<1, 4>), grid, dim3(EV_THREADS), 0, s, p);
+      hipLaunchKernelGGL((evict_hist<2, 4>), grid, dim3(EV_THREADS), 0, s, p);
+    } else {
+      hipLaunchKernelGGL((evict_hist<0, 8>), grid, dim3(EV_THREADS), 0, s, p);
+      hipLaunchKernelGGL((evict_hist<1, 8>), grid, dim3(EV_THREADS), 0, s, p);
+      hipLaunchKernelGGL((evict_hist<2, 8>), grid, dim3(EV_THREADS), 0, s, p);
+    }
   }
-  if (p.nb > 0) hipLaunchKernelGGL(evict_count, grid, dim3(EV_THREADS), 0, s, p);
+  if (p.nb > 0) {
+    if (per == 4)
+      hipLaunchKernelGGL(evict_count<4>, grid, dim3(EV_THREADS), 0, s, p);
+    else
+      hipLaunchKernelGGL(evict_count<8>, grid, dim3(EV_THREADS), 0, s, p);
+  }
   if ((err = hipGetLastError()) != hipSuccess) return err;
   const bool fused = p.Hkv <= FUSED_HEADS && (int64_t)p.Hkv * p.nb <= FUSED_ENTRIES;
   const dim3 wgrid = p.nb > 0 ? grid : dim3(1, 1);  // no keys: one block writes the (zero) offsets
   if (fused) {
-    hipLaunchKernelGGL(evict_write_fused, wgrid, dim3(EV_THREADS), 0, s, p);
+    if (per == 4)
+      hipLaunchKernelGGL(evict_write_fused<4>, wgrid, dim3(EV_THREADS), 0, s, p);
+    else
+      hipLaunchKernelGGL(evict_write_fused<8>, wgrid, dim3(EV_THREADS), 0, s, p);
   } else {
     hipLaunchKernelGGL(evict_scan, dim3(p.Hkv), dim3(EV_THREADS), 0, s, p);
-    hipLaunchKernelGGL(evict_write, wgrid, dim3(EV_THREADS), 0, s, p);
+    if (per == 4)
+      hipLaunchKernelGGL(evict_write<4>, wgrid, dim3(EV_THREADS), 0, s, p);
+    else
+      hipLaunchKernelGGL(evict_write<8>, wgrid, dim3(EV_THREADS), 0, s, p);
   }
   const int64_t cap_rows = e.capacity;
   if (cap_rows > 0 && p.nb > 0) {
