@@ -15,10 +15,11 @@
 //   * key and value tiles of 32 rows go through a 2-stage LDS ring of 4
 //     tiles per stage: one barrier per 128 keys, the next stage's tiles
 //     loaded while this stage's are used. Each tile's loads are issued before
-//     the S of the tile in use and stored after it, so only one tile's loads
-//     sit in registers; the matrix work of one wave overlaps the other
-//     waves' exponentials (no second set of S accumulators, which would not
-//     fit 3 waves per SIMD);
+//     the S of the tile in use and stored after its PV product, so only one
+//     tile's loads sit in registers and the whole tile's work covers their
+//     latency; the matrix work of one wave overlaps the other waves'
+//     exponentials (no second set of S accumulators, which would not fit 3
+//     waves per SIMD);
 //   * key tiles of 32 rows go through LDS as the A operand of S = K Q^T (keys
 //     as rows, queries as columns), exactly as in the LSE pass; each lane's
 //     16 accumulators are 16 keys of one query;
@@ -332,8 +333,8 @@ __global__ __launch_bounds__(AT_THREADS, 1) void attn_kernel(AttnParams p) {
       const char* st = s_tile[it % NSTAGE][sub];
       f32x16 x = f32x16{};
       if (run) x = qk(st);
-      if (tl < n_tiles) store_tile(s_tile[(it + AHEAD) % NSTAGE][sub]);
       if (run) softmax_pv(x, st, cur.masked, cur.k0, cur.kend, cur.is_ctx);
+      if (tl < n_tiles) store_tile(s_tile[(it + AHEAD) % NSTAGE][sub]);
     }
     __syncthreads();
   }
