@@ -124,25 +124,22 @@ __global__ __launch_bounds__(LSE_WAVES * WAVE, 3) void lse_kernel(LseParams p) {
   // Key tiles come in through buffer loads. A tile's resource starts at its
   // first row and covers only the rows its segment has, so rows past the end
   // read as zero; every such row is masked (ctx: key >= n_ctx; self/causal:
-  // key > j), so its value never counts. A thread's byte offsets within a
-  // tile are fixed, so a tile costs no per-thread address arithmetic. Token
-  // strides are at most 2^22 elements, so 32 rows span at most 2^28 bytes.
-  int voff_ctx[CPT], voff_self[CPT];
-#pragma unroll
-  for (int c = 0; c < CPT; ++c) {
-    const int idx = tid + c * NTHREADS;
-    const int rr = idx / CHUNKS_PER_ROW, part = idx % CHUNKS_PER_ROW;
-    voff_ctx[c] = (int)(rr * p.k_ts * 2 + part * 16);
-    voff_self[c] = (int)(rr * (CAUSAL ? p.k_ts : p.ks_ts) * 2 + part * 16);
-  }
-  u32x4 pre[CPT];
+  // key > j), so its value never counts. A thread loads the pieces of rows
+  // rr0, rr0 + RSTEP, ...: one per-thread offset per tile, the rest in the
+  // scalar offset. Token strides are at most 2^22 elements, so 32 rows span
+  // at most 2^28 bytes.
+  const int rr0 = tid / CHUNKS_PER_ROW, p16 = (tid % CHUNKS_PER_ROW) * 16;
+  constexpr int RSTEP = NTHREADS / CHUNKS_PER_ROW;
+  // two register sets: tile t is loaded into set t % 2 two iterations before
+  // its use (see the loop below)
+  u32x4 preA[CPT], preB[CPT];
   // (32-bit positions and scalar compares: every position is below 2^30)
   const int n_ctx_tiles_s = (int)n_ctx_tiles, n_ctx_s = (int)p.n_ctx, pos_end_s = (int)pos_end;
   const int self_lo_s = (int)self_lo, k_ts_s = (int)p.k_ts;
   const int ks_ts_s = CAUSAL ? k_ts_s : (int)p.ks_ts;
   const uint16_t* const ctx_base = p.K + (int64_t)h * p.k_hs;
   const uint16_t* const self_base = CAUSAL ? ctx_base : p.Kself + (int64_t)h * p.ks_hs;
-  auto load_tile = [&](int tt) {
+  auto load_tile = [&](int tt, u32x4 (&pre)[CPT]) {
     const bool ctx = tt < n_ctx_tiles_s;
     const int k0 = ctx ? tt * 32 : self_lo_s + (tt - n_ctx_tiles_s) * 32;
     const int kend = ctx ? n_ctx_s : pos_end_s;
@@ -150,9 +147,10 @@ __global__ __launch_bounds__(LSE_WAVES * WAVE, 3) void lse_kernel(LseParams p) {
     const int rows = min(kend - k0, 32);
     const __amdgpu_buffer_rsrc_t r = tile_rsrc((ctx ? ctx_base : self_base) + (int64_t)k0 * ts, rows * ts * 2);
 #pragma unroll
-    for (int c = 0; c < CPT; ++c) pre[c] = buf_ld16(r, ctx ? voff_ctx[c] : voff_self[c]);
+    for (int c = 0; c < CPT; ++c)
+      pre[c] = __builtin_amdgcn_raw_buffer_load_b128(r, rr0 * ts * 2 + p16, c * RSTEP * ts * 2, 0);
   };
-  auto store_tile = [&](int buf) {
+  auto store_tile = [&](int buf, const u32x4 (&pre)[CPT]) {
 #pragma unroll
     for (int c = 0; c < CPT; ++c) {
       const int idx = tid + c * NTHREADS;
@@ -259,15 +257,23 @@ __global__ __launch_bounds__(LSE_WAVES * WAVE, 3) void lse_kernel(LseParams p) {
     }
   };
 
+  // Tile t goes through register set t % 2 and LDS buffer t % 2: its loads
+  // are issued at the start of iteration t - 2 and stored at the end of
+  // iteration t - 1, into the buffer that held tile t - 2, which every wave
+  // finished before the barrier ending iteration t - 2. So two iterations of
+  // matrix and exponential work cover a tile's load latency.
   if (n_tiles_i > 0) {
-    load_tile(0);
-    store_tile(0);
+    load_tile(0, preA);
+    store_tile(0, preA);
   }
+  if (n_tiles_i > 1) load_tile(1, preB);
   __syncthreads();
 
-  for (int tt = 0; tt < n_tiles_i; ++tt) {
+  // one iteration: tile tt from LDS; the loads of tile tt + 2 into pl (the
+  // set that held tile tt); tile tt + 1 from ps into the other buffer
+  auto step = [&](int tt, u32x4 (&pl)[CPT], const u32x4 (&ps)[CPT]) {
     const int cur = tt & 1;
-    if (tt + 1 < n_tiles_i) load_tile(tt + 1);
+    if (tt + 2 < n_tiles_i) load_tile(tt + 2, pl);
 
     bf16x8 a[T::STEPS];
     const char* krow = &s_k[cur][col * T::LDS_STRIDE + half * (D / 2) * 2];
@@ -295,8 +301,13 @@ __global__ __launch_bounds__(LSE_WAVES * WAVE, 3) void lse_kernel(LseParams p) {
       tile_general(tt, a);
     }
 
-    if (tt + 1 < n_tiles_i) store_tile(cur ^ 1);
+    if (tt + 1 < n_tiles_i) store_tile(cur ^ 1, ps);
     __syncthreads();
+  };
+  // (unrolled by two so that each register set stays a fixed set of registers)
+  for (int tt = 0; tt < n_tiles_i; tt += 2) {
+    step(tt, preA, preB);
+    if (tt + 1 < n_tiles_i) step(tt + 1, preB, preA);
   }
 
   // ---- merge half-waves, write natural-log LSE
