@@ -49,6 +49,13 @@ LSE_CASES = [
     ("repeat-lds-form-ragged", dict(Hq=32, Hkv=8, D=128, n_ctx=700, n_q=2048, lowrank_rank=8,
                                     lowrank_scale=2.0), "repeat", 1000),
     ("causal-lds-form", dict(Hq=32, Hkv=8, D=128, n_ctx=2048, n_q=2048, mask="causal", sinks=4), "causal", 0),
+    # LDS form with every tile count from 1 up (8 query heads per KV head: a
+    # workgroup serves one 32-position block, so block b sees b + 1 key
+    # tiles), for both head dims; and three tiles per workgroup with a
+    # partial context tile (20 context keys, chunks of 32)
+    ("causal-lds-form-g8", dict(Hq=64, Hkv=8, D=128, n_ctx=1024, n_q=1024, mask="causal"), "causal", 0),
+    ("causal-lds-form-g8-d64", dict(Hq=64, Hkv=8, D=64, n_ctx=1024, n_q=1024, mask="causal"), "causal", 0),
+    ("repeat-lds-form-short-context", dict(Hq=32, Hkv=8, D=128, n_ctx=20, n_q=2048), "repeat", 32),
 ]
 
 
