@@ -279,6 +279,10 @@ __global__ __launch_bounds__(AT_THREADS, 1) void attn_kernel(AttnParams p) {
     l_run += sum;
     const bf16x8 pb0 = pack_bf16(e, 0), pb1 = pack_bf16(e, 8);
     const char* vrow = st + T::K_BYTES + col * T::VT_STRIDE + half * 16;
+    // the PV MFMAs at raised wave priority: a wave whose exponentials are
+    // done hands its matrix work to the core ahead of the SIMD's other waves,
+    // which keep the VALU busy meanwhile
+    __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int db = 0; db < T::DB; ++db) {
       const char* vr = vrow + 32 * db * T::VT_STRIDE;
@@ -287,6 +291,7 @@ __global__ __launch_bounds__(AT_THREADS, 1) void attn_kernel(AttnParams p) {
       oacc[db] = mfma32(v0, pb0, oacc[db]);
       oacc[db] = mfma32(v1, pb1, oacc[db]);
     }
+    __builtin_amdgcn_s_setprio(0);
   };
 
   // What this wave does with tile tt: skip it, or run it masked or not.
