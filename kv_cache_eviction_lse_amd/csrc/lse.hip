@@ -283,20 +283,20 @@ __global__ __launch_bounds__(LSE_WAVES * WAVE, 3) void lse_kernel(LseParams p) {
     if (tt < n_ctx_full_tiles && all_sub_ok) {
       // Fast path (all full context tiles): every key visible to every query
       // of both subtiles; straight-line code, no masks.
-      // The MFMA block runs at raised wave priority: among the waves of a
-      // SIMD, the one ready to issue matrix work goes first, the others fill
-      // the VALU with their exponentials meanwhile.
+      // The exponentials run at raised wave priority: a wave whose logits
+      // are ready finishes its VALU work ahead of the SIMD's other waves and
+      // returns to the matrix core sooner, while their MFMAs keep it busy.
       f32x16 acc[LSE_NQ];
-      __builtin_amdgcn_s_setprio(1);
 #pragma unroll
       for (int q = 0; q < LSE_NQ; ++q) {
         acc[q] = mfma32(a[0], qreg[q][0], f32x16{});
 #pragma unroll
         for (int s = 1; s < T::STEPS; ++s) acc[q] = mfma32(a[s], qreg[q][s], acc[q]);
       }
-      __builtin_amdgcn_s_setprio(0);
+      __builtin_amdgcn_s_setprio(1);
 #pragma unroll
       for (int q = 0; q < LSE_NQ; ++q) softmax_update(q, acc[q]);
+      __builtin_amdgcn_s_setprio(0);
     } else {
       tile_general(tt, a);
     }
@@ -310,7 +310,11 @@ __global__ __launch_bounds__(LSE_WAVES * WAVE, 3) void lse_kernel(LseParams p) {
     if (tt + 1 < n_tiles_i) step(tt + 1, preB, preA);
   }
 
-  // ---- merge half-waves, write natural-log LSE
+  // ---- merge half-waves, write natural-log LSE. The lane index is taken
+  // afresh here, so the half and column computed before the loop need not
+  // stay in registers across it.
+  const int lane_e = (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+  const int half_e = lane_e >> 5, col_e = lane_e & 31;
 #pragma unroll
   for (int q = 0; q < LSE_NQ; ++q) {
     const float o_o = __shfl_xor(o_run[q], 32);
@@ -318,8 +322,8 @@ __global__ __launch_bounds__(LSE_WAVES * WAVE, 3) void lse_kernel(LseParams p) {
     const float Mc = fmaxf(o_run[q], o_o);
     const float L = (l_run[q] > 0.f ? l_run[q] * fast_exp2(o_run[q] - Mc) : 0.f) +
                     (l_o > 0.f ? l_o * fast_exp2(o_o - Mc) : 0.f);
-    const int64_t j = sub_pos[q] + col;
-    if (half == 0 && sub_ok[q] && j < p.n_q) p.lse[(int64_t)sub_g[q] * p.n_q + j] = (Mc + __log2f(L)) * LN2;
+    const int64_t j = sub_pos[q] + col_e;
+    if (half_e == 0 && sub_ok[q] && j < p.n_q) p.lse[(int64_t)sub_g[q] * p.n_q + j] = (Mc + __log2f(L)) * LN2;
   }
 }
 

@@ -246,6 +246,8 @@ __global__ __launch_bounds__(NW * WAVE) void score_kernel(ScoreParams p) {
             f32x16 acc = bias;
 #pragma unroll
             for (int s = 0; s < T::STEPS; ++s) acc = mfma32(a[s], kreg[st][s], acc);
+            // the exponentials at raised wave priority (as in the LSE pass)
+            __builtin_amdgcn_s_setprio(1);
             float sum = 0.f;
             if (jt0 >= ib + 31 + p.window) {
 #pragma unroll
@@ -260,6 +262,7 @@ __global__ __launch_bounds__(NW * WAVE) void score_kernel(ScoreParams p) {
               }
             }
             red[st] += sum;
+            __builtin_amdgcn_s_setprio(0);
           }
         } else {
 #pragma unroll
