@@ -676,24 +676,30 @@ __global__ __launch_bounds__(HD_THREADS) void evict_head(EvictParams p, int reps
       u32x4* g4 = reinterpret_cast<u32x4*>(s_hist12);
       for (int i = tid; i < (NBINS + NBINS / 2) / 4; i += HD_THREADS) g4[i] = u32x4{0u, 0u, 0u, 0u};
     }
+    __syncthreads();  // the clears (the score loads may still be in flight)
+    // first digit straight from the registers as each load arrives
 #pragma unroll
     for (int u = 0; u < HD_UNROLL; ++u) {
       const int i = tid + u * HD_THREADS;
-      if (i < n_cand) s_key[i] = order_key(v[u]);
+      if (i < n_cand) {
+        const uint32_t k = order_key(v[u]);
+        s_key[i] = k;
+        atomicAdd(&s_hist[copy * HD_CSTRIDE + (k >> 21)], 1u);
+      }
     }
     uint32_t prefix = 0;
     int rank = (int)p.kprime;
 #pragma unroll 1
     for (int pass = 0; pass < 3; ++pass) {
       const int nbins = pass == 2 ? 1024 : 2048;
-      __syncthreads();  // (pass 0: also the key stores and the clears)
+      __syncthreads();  // (pass 0: the key stores and the first digit's atomics)
       uint32_t* hist = pass == 0 ? s_hist : s_hist12 + (pass == 2 ? NBINS : 0);
-      const int hs = pass > 0 ? digit_shift(pass - 1) : 32;
+      const int hs = digit_shift(pass > 0 ? pass - 1 : 0);  // (pass 0 accumulates nothing here)
       const int ds = digit_shift(pass);
       const uint32_t dm = digit_mask(pass);
-      const int cofs = pass == 0 ? copy * HD_CSTRIDE : 0;
       constexpr int RU = 4;  // LDS reads of a batch issued before its atomics
-      for (int i0 = tid; i0 < n_cand; i0 += HD_THREADS * RU) {
+      // passes 1 and 2: the keys that share the digits found so far
+      for (int i0 = tid; pass > 0 && i0 < n_cand; i0 += HD_THREADS * RU) {
         uint32_t u[RU];
 #pragma unroll
         for (int k = 0; k < RU; ++k) {
@@ -703,8 +709,7 @@ __global__ __launch_bounds__(HD_THREADS) void evict_head(EvictParams p, int reps
 #pragma unroll
         for (int k = 0; k < RU; ++k) {
           const int i = i0 + k * HD_THREADS;
-          if (i < n_cand && (pass == 0 || (u[k] >> hs) == (prefix >> hs)))
-            atomicAdd(&hist[cofs + ((u[k] >> ds) & dm)], 1u);
+          if (i < n_cand && (u[k] >> hs) == (prefix >> hs)) atomicAdd(&hist[(u[k] >> ds) & dm], 1u);
         }
       }
       __syncthreads();
