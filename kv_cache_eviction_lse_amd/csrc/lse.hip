@@ -125,9 +125,10 @@ __global__ __launch_bounds__(LSE_WAVES * WAVE, 3) void lse_kernel(LseParams p) {
   // first row and covers only the rows its segment has, so rows past the end
   // read as zero; every such row is masked (ctx: key >= n_ctx; self/causal:
   // key > j), so its value never counts. A thread loads the pieces of rows
-  // rr0, rr0 + RSTEP, ...: one per-thread offset per tile, the rest in the
-  // scalar offset. Token strides are at most 2^22 elements, so 32 rows span
-  // at most 2^28 bytes.
+  // rr0, rr0 + RSTEP, ...; each load's whole byte offset is in its per-lane
+  // offset, because the range check does not include the scalar offset.
+  // Token strides are at most 2^22 elements, so 32 rows span at most 2^28
+  // bytes.
   const int rr0 = tid / CHUNKS_PER_ROW, p16 = (tid % CHUNKS_PER_ROW) * 16;
   constexpr int RSTEP = NTHREADS / CHUNKS_PER_ROW;
   // two register sets: tile t is loaded into set t % 2 two iterations before
@@ -148,7 +149,7 @@ __global__ __launch_bounds__(LSE_WAVES * WAVE, 3) void lse_kernel(LseParams p) {
     const __amdgpu_buffer_rsrc_t r = tile_rsrc((ctx ? ctx_base : self_base) + (int64_t)k0 * ts, rows * ts * 2);
 #pragma unroll
     for (int c = 0; c < CPT; ++c)
-      pre[c] = __builtin_amdgcn_raw_buffer_load_b128(r, rr0 * ts * 2 + p16, c * RSTEP * ts * 2, 0);
+      pre[c] = buf_ld16(r, (rr0 + c * RSTEP) * ts * 2 + p16);
   };
   auto store_tile = [&](int buf, const u32x4 (&pre)[CPT]) {
 #pragma unroll
